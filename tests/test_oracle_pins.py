@@ -1,0 +1,281 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself.
+
+Each check ties one step of the oracle to something fixed independently:
+hand-packed bytes derived from the pages' packing rule, a bit-by-bit brute
+force, exact rational arithmetic (``fractions.Fraction``) on tiny inputs,
+integer arithmetic on inputs where every sum is exact, closed forms, and
+one-hot activations.  ``test_mutants_are_caught`` builds deliberately broken
+copies of the oracle and checks that these pins reject every one of them.
+"""
+
+import json
+import os
+import subprocess
+import sys
+import tempfile
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from bit_affine_quantized_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = os.path.join(ROOT, "tests", "golden", "handpacked.json")
+
+
+def brute_codes(words: np.ndarray, bits: int, k: int) -> np.ndarray:
+    """Bit-by-bit unpack: bit j of code i is bit (i*bits + j) of the row's
+    bytes, bit 0 being the low bit of byte 0."""
+    words = np.asarray(words, dtype=np.uint32)
+    n = words.shape[0]
+    raw = np.ascontiguousarray(words).view(np.uint8).reshape(n, -1)
+    out = np.zeros((n, k), dtype=np.int64)
+    for r in range(n):
+        row = [int(v) for v in raw[r]]
+        for i in range(k):
+            c = 0
+            for j in range(bits):
+                p = i * bits + j
+                c |= ((row[p // 8] >> (p % 8)) & 1) << j
+            out[r, i] = c
+    return out
+
+
+def bf16_fraction(h: int) -> Fraction:
+    """Exact value of a bf16 bit pattern (finite, normal or zero)."""
+    h = int(h)
+    sign = -1 if h & 0x8000 else 1
+    e = (h >> 7) & 0xFF
+    f = h & 0x7F
+    if e == 0:
+        return sign * Fraction(f, 1 << 7) * Fraction(1, 1 << 126)
+    assert e != 0xFF
+    val = Fraction(128 + f, 128)
+    return sign * (val * (Fraction(2) ** (e - 127)))
+
+
+# --------------------------------------------------------------------------
+# unpack
+# --------------------------------------------------------------------------
+
+def test_handpacked_vectors():
+    d = json.load(open(GOLDEN))
+    assert len(d["vectors"]) >= 9
+    for v in d["vectors"]:
+        bits, codes = v["bits"], np.array(v["codes"], dtype=np.uint8)
+        raw = bytes.fromhex(v["bytes"])
+        words = np.frombuffer(raw, dtype="<u4").astype(np.uint32)[None, :]
+        k = len(codes)
+        got = oracle.unpack(words, bits, 1, k)[0]
+        assert got.tolist() == codes.tolist(), v["derivation"]
+        # the format encoder used for structured inputs writes the same bytes
+        enc = synth.pack_codes(codes[None, :], bits)
+        assert enc.tobytes() == raw, v["derivation"]
+
+
+@pytest.mark.parametrize("bits", synth.BITS)
+def test_unpack_matches_brute_force(bits):
+    rng = np.random.default_rng(100 + bits)
+    for k in (32, 96, 160, 256):
+        if (k * bits) % 32:
+            continue
+        words = synth.draw_words(rng, (3,), k, bits)
+        got = oracle.unpack(words, bits, 3, k).astype(np.int64)
+        assert np.array_equal(got, brute_codes(words, bits, k))
+
+
+@pytest.mark.parametrize("bits", synth.BITS)
+def test_unpack_roundtrip_every_offset(bits):
+    # every code value at every bit offset within a 32-bit word
+    k = 32 * (1 << bits)
+    codes = synth.sweep_codes(2, k, bits)
+    words = synth.pack_codes(codes, bits)
+    assert np.array_equal(oracle.unpack(words, bits, 2, k), codes)
+
+
+def test_shape_rules():
+    ok = oracle.check_shape
+    assert ok(4, 64, 1, 2048) == 0
+    assert ok(7, 64, 1, 2048) != 0      # width
+    assert ok(4, 16, 1, 2048) != 0      # group
+    assert ok(4, 64, 1, 2080) != 0      # group does not divide K
+    assert ok(4, 64, 0, 2048) != 0      # empty matrix
+    for b in synth.BITS:
+        for g in synth.GROUPS:
+            assert ok(b, g, 5, g) == 0
+
+
+# --------------------------------------------------------------------------
+# product
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bits,group", [(b, g) for b in synth.BITS for g in synth.GROUPS])
+def test_exact_rational_tiny(bits, group):
+    """y64 within (K-1)*2^-53*sum|w*x| of the exact rational sum, with an
+    independent brute-force unpack; abs64 likewise."""
+    n, k, m = 2, 128, 2
+    d = synth.matrix(7000 + bits * 10 + group, bits, group, n, k, m)
+    y, a, t = oracle.gemv(d["words"], d["scales"], d["biases"], d["x"], bits, group, n, k)
+    codes = brute_codes(d["words"], bits, k)
+    for r in range(n):
+        for i in range(m):
+            exact = Fraction(0)
+            mag = Fraction(0)
+            for kk in range(k):
+                s = bf16_fraction(d["scales"][r, kk // group])
+                b = bf16_fraction(d["biases"][r, kk // group])
+                xv = bf16_fraction(d["x"][i, kk])
+                term = (s * int(codes[r, kk]) + b) * xv
+                exact += term
+                mag += abs(term)
+            bound = Fraction(k - 1) * Fraction(1, 2 ** 53) * mag
+            assert abs(Fraction(y[i, r]) - exact) <= bound
+            assert abs(Fraction(a[i, r]) - mag) <= bound
+
+
+@pytest.mark.parametrize("bits,group", [(2, 32), (3, 128), (5, 64), (6, 32), (8, 128)])
+def test_exact_representable(bits, group):
+    """Inputs whose every partial sum is a multiple of 2^-8 below 2^15: the
+    fp64 result must equal an integer computation exactly."""
+    n, k, m = 5, 512, 3
+    d = synth.exact_case(11, bits, group, n, k, m)
+    y, _, _ = oracle.gemv(d["words"], d["scales"], d["biases"], d["x"], bits, group, n, k)
+    s = synth.bf16_bits_to_f32(d["scales"]).astype(np.float64)
+    b = synth.bf16_bits_to_f32(d["biases"]).astype(np.float64)
+    x = synth.bf16_bits_to_f32(d["x"]).astype(np.int64)
+    s256 = np.rint(s * 256).astype(np.int64)       # exact: s is 2^-6..2^-8
+    b256 = np.rint(b * 256).astype(np.int64)       # exact: multiples of 2^-8
+    assert np.array_equal(s256 / 256.0, s) and np.array_equal(b256 / 256.0, b)
+    g = np.arange(k) // group
+    w256 = s256[:, g] * d["codes"].astype(np.int64) + b256[:, g]   # [n, k]
+    want = (x @ w256.T)                                            # [m, n], integers
+    assert np.array_equal(y * 256.0, want.astype(np.float64))
+
+
+@pytest.mark.parametrize("bits", synth.BITS)
+def test_closed_forms(bits):
+    n, k, group = 3, 256, 64
+    qmax = (1 << bits) - 1
+    codes = np.full((n, k), qmax, dtype=np.uint8)
+    words = synth.pack_codes(codes, bits)
+    scales = synth.to_bf16_bits(np.full((n, k // group), 2.0 ** -4))
+    zeros = synth.to_bf16_bits(np.zeros((n, k // group)))
+    ones = synth.to_bf16_bits(np.ones((1, k)))
+    y, _, _ = oracle.gemv(words, scales, zeros, ones, bits, group, n, k)
+    assert np.all(y == k * qmax / 16.0)
+    # bias only: every code 0, y = sum over groups of bias * (sum of x in group)
+    rng = np.random.default_rng(bits)
+    words0 = synth.pack_codes(np.zeros((n, k), dtype=np.uint8), bits)
+    biases = synth.to_bf16_bits(rng.integers(-8, 9, size=(n, k // group)) / 64.0)
+    x = synth.to_bf16_bits(rng.integers(-4, 5, size=(2, k)) / 4.0)
+    y, _, _ = oracle.gemv(words0, scales, biases, x, bits, group, n, k)
+    bv = synth.bf16_bits_to_f32(biases).astype(np.float64)
+    xv = synth.bf16_bits_to_f32(x).astype(np.float64)
+    xg = xv.reshape(2, k // group, group).sum(axis=2)                 # exact (quarters)
+    assert np.array_equal(y, xg @ bv.T)
+
+
+@pytest.mark.parametrize("group", synth.GROUPS)
+def test_one_hot_places_scale_and_bias(group):
+    """x = e_k gives y[n] = s[n, k/G] * q[n, k] + bias[n, k/G] exactly; k runs
+    over both sides of every group edge."""
+    bits, n, k = 5, 4, 512
+    rng = np.random.default_rng(group)
+    codes = rng.integers(0, 32, size=(n, k)).astype(np.uint8)
+    d = synth.matrix(group, bits, group, n, k)
+    words = synth.pack_codes(codes, bits)
+    s = synth.bf16_bits_to_f32(d["scales"]).astype(np.float64)
+    b = synth.bf16_bits_to_f32(d["biases"]).astype(np.float64)
+    ks = sorted({e + o for e in range(0, k, group) for o in (-1, 0, 1) if 0 <= e + o < k})
+    x = np.zeros((len(ks), k))
+    for i, kk in enumerate(ks):
+        x[i, kk] = 1.0
+    y, _, _ = oracle.gemv(words, d["scales"], d["biases"], synth.to_bf16_bits(x), bits, group, n, k)
+    for i, kk in enumerate(ks):
+        want = [Fraction(s[r, kk // group]) * int(codes[r, kk]) + Fraction(b[r, kk // group])
+                for r in range(n)]
+        assert [Fraction(v) for v in y[i]] == want
+
+
+def test_terms_and_abs_relations():
+    bits, group, n, k = 4, 64, 8, 1024
+    d = synth.matrix(3, bits, group, n, k, 4)
+    y, a, t = oracle.gemv(d["words"], d["scales"], d["biases"], d["x"], bits, group, n, k)
+    assert np.all(np.abs(y) <= a * (1 + 1e-12))
+    assert np.all(a <= t * (1 + 1e-12))  # |sq x + b x| <= |sq x| + |b x|
+    # row split over threads computes the same numbers
+    y2, a2, t2 = oracle.gemv(d["words"], d["scales"], d["biases"], d["x"], bits, group, n, k, threads=3)
+    assert np.array_equal(y, y2) and np.array_equal(a, a2) and np.array_equal(t, t2)
+
+
+def test_negative_control_moves_outputs():
+    """Scales 1% off move the product by far more than the pages' bound."""
+    bits, group, n, k = 4, 64, 16, 2048
+    d = synth.matrix(5, bits, group, n, k, 1)
+    y, a, t = oracle.gemv(d["words"], d["scales"], d["biases"], d["x"], bits, group, n, k)
+    yb, _, _ = oracle.gemv(d["words"], d["scales"], d["biases"], d["x"], bits, group, n, k,
+                           scale_mult=1.01)
+    frac = np.abs(yb - y) / oracle.tol_pages(t, group, k)
+    assert frac.max() > 1.0
+
+
+def test_relu2_rule():
+    v = np.array([-1.0, 0.0, -0.0, 2.0, np.nan, 1e-3])
+    r = oracle.relu2(v)
+    assert r[0] == 0 and r[1] == 0 and r[2] == 0 and not np.signbit(r[2])
+    assert r[3] == 4.0 and np.isnan(r[4]) and r[5] == 1e-3 * 1e-3
+
+
+def test_indexed_is_plain_on_the_expert():
+    bits, group, n, k, e = 3, 32, 4, 256, 5
+    d = synth.matrix(9, bits, group, n, k, 3, n_experts=e)
+    idx = np.array([[4, 0], [2, 2], [1, 3]], dtype=np.int32)
+    y, _, _ = oracle.gemv_indexed(d["words"], d["scales"], d["biases"], d["x"], idx, bits, group, n, k)
+    for i in range(3):
+        for s in range(2):
+            ex = idx[i, s]
+            yy, _, _ = oracle.gemv(d["words"][ex], d["scales"][ex], d["biases"][ex], d["x"][i:i + 1],
+                                   bits, group, n, k)
+            assert np.array_equal(y[i, s], yy[0])
+
+
+# --------------------------------------------------------------------------
+# the pins reject plausible mistakes
+# --------------------------------------------------------------------------
+
+MUTANTS = {
+    "bit offset": ("return (window >> shift)", "return (window >> (shift ^ 1))"),
+    "byte order": ("<< (8 * i);", "<< (8 * (nbytes - 1 - i));"),
+    "code mask": ("((1u << bits) - 1u)", "((1u << (bits - 1)) - 1u)"),
+    "group index": ("const int64_t g = kk / group;", "const int64_t g = (kk + 1) / group % groups;"),
+    "dropped bias": ("w[kk] = sq[kk] + b;", "w[kk] = sq[kk];"),
+    "scale for bias": ("const double s = bf16_value(scales[", "const double s = bf16_value(biases["),
+    "code offset": ("const double q = (double)oracle_code(row, bits, kk);",
+                    "const double q = (double)oracle_code(row, bits, kk) + 1.0;"),
+    "row of x": ("const uint16_t *xr = x + i * k;", "const uint16_t *xr = x;"),
+    "sign": ("acc += prod;", "acc -= prod;"),
+    "row stride": ("const uint8_t *row = base + r * row_bytes;\n    for (int64_t kk = 0; kk < k; kk++) {",
+                   "const uint8_t *row = base + (r % 2) * row_bytes;\n    for (int64_t kk = 0; kk < k; kk++) {"),
+    "scale multiplier": (") * scale_mult;", ");"),
+    "relu2 sign": ("v > 0.0 ? v * v", "v < 0.0 ? v * v"),
+}
+
+
+def test_mutants_are_caught(tmp_path):
+    src = open(oracle.SOURCE).read()
+    missed = []
+    for name, (old, new) in MUTANTS.items():
+        assert src.count(old) == 1, f"mutation site for '{name}' not unique"
+        mut_c = tmp_path / f"mut_{abs(hash(name))}.c"
+        mut_c.write_text(src.replace(old, new))
+        lib = str(tmp_path / f"mut_{abs(hash(name))}.so")
+        oracle.build(str(mut_c), lib)
+        env = dict(os.environ, QGEMV_ORACLE_LIB=lib)
+        r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                            os.path.abspath(__file__), "-k", "not mutants"],
+                           env=env, cwd=ROOT, capture_output=True, text=True, timeout=600)
+        if r.returncode == 0:
+            missed.append(name)
+    assert not missed, f"pins did not catch: {missed}"
