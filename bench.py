@@ -1,0 +1,287 @@
+#!/usr/bin/env python3
+"""Benchmark of the MLX-affine quantized row product on one MI355X.
+
+A step is one call of the row product over one activation window of the
+workload (the LM-head matrix, N = 248320 x K = 2048, 6-bit codes, group 32,
+one activation row, by default), with every input already resident in HBM.
+The weights rotate over at least 1 GiB of distinct copies so that the
+256 MB Infinity Cache cannot hold them, the calls are issued back to back
+on one stream and bracketed by HIP events on that same stream.
+
+Printed: one JSON line.  ``value`` is effective HBM GB/s = algorithmic bytes
+per call / time per call, where the algorithmic bytes are what the call must
+move once: codes + bf16 scales and biases + bf16 activations + fp32 outputs
+(+ the routing table).  ``roofline.frac`` is that against the 8.0 TB/s HBM
+peak; ``cpu_baseline`` is the fp64 CPU oracle on a bounded sample of the same
+workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_GBS = 8000.0          # MI355X HBM3E, published
+ROTATE_BYTES = 1 << 30     # at least 1 GiB of distinct weight copies
+KERNEL_SOURCE = os.path.join(ROOT, "bit_affine_quantized_amd", "csrc", "qgemv.hip")
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def kernel_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+
+
+def algorithmic_bytes(runs, m, k, n_out, idx_bytes=0):
+    """sum over runs of codes + scales + biases, + activations + outputs."""
+    b = 0
+    for bits, group, n in runs:
+        b += n * k * bits // 8 + n * (k // group) * 4
+    return b + m * k * 2 + m * n_out * 4 + idx_bytes
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    this workload, if it was taken on the current kernel source."""
+    path = os.path.join(PROFILE_DIR, f"counters_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except Exception:
+        return None
+    if rec.get("kernel_sha") != kernel_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+class Workload:
+    """Device inputs of one workload plus rotating weight copies."""
+
+    def __init__(self, name: str, m: int, torch, qgemv, synth):
+        self.name, self.m = name, m
+        self.torch, self.qgemv = torch, qgemv
+        dev = "cuda"
+
+        def t(a):
+            a = np.ascontiguousarray(a)
+            view = {np.dtype(np.uint32): np.int32, np.dtype(np.uint16): np.int16,
+                    np.dtype(np.int32): np.int32}[a.dtype]
+            return torch.from_numpy(a.view(view)).to(dev)
+
+        if name == "lmhead":
+            d = synth.lmhead(m=m)
+            self.k = d["k"]
+            self.runs = [(d["bits"], d["group"], d["n"])]
+            self.n_out = d["n"]
+            self.desc = (f"LM head N={d['n']} K={d['k']} {d['bits']}-bit group {d['group']}, "
+                         f"{m}-row window")
+            base = [(t(d["words"]), t(d["scales"]), t(d["biases"]))]
+            self.x = t(d["x"])
+            self.y = torch.empty((m, d["n"]), dtype=torch.float32, device=dev)
+            self.idx_bytes = 0
+            self.kind = "plain"
+            self.cols = [0]
+        elif name == "stack":
+            st = synth.stack(m=m)
+            self.k = st["k"]
+            self.runs = [(r["bits"], r["group"], r["n"]) for r in st["runs"]]
+            self.n_out = st["ldy"]
+            self.desc = ("fused stack K=2048: 4/64 x 2048, 5/128 x 6192, 6/64 x 48 into one "
+                         f"8288-column row by three strided calls, {m}-row window")
+            base = [tuple(t(r[key]) for key in ("words", "scales", "biases")) for r in st["runs"]]
+            self.x = t(st["x"])
+            self.y = torch.empty((m, st["ldy"]), dtype=torch.float32, device=dev)
+            self.idx_bytes = 0
+            self.kind = "strided"
+            self.cols = [r["col"] for r in st["runs"]]
+            self.ldy = st["ldy"]
+        elif name == "experts":
+            d = synth.experts()
+            self.k = d["k"]
+            distinct = len(np.unique(d["idx"]))
+            self.runs = [(d["bits"], d["group"], d["n"] * distinct)]
+            m = d["idx"].shape[0]
+            self.m = m
+            self.slots = d["idx"].shape[1]
+            self.n_out = self.slots * d["n"]
+            self.desc = (f"indexed experts: {d['n_experts']} x (N={d['n']} K={d['k']} 4-bit group 64), "
+                         f"{m} rows x {self.slots} slots ({distinct} distinct experts), relu2")
+            base = [(t(d["words"]), t(d["scales"]), t(d["biases"]))]
+            self.x = t(d["x"])
+            self.idx = t(d["idx"])
+            self.y = torch.empty((m, self.slots, d["n"]), dtype=torch.float32, device=dev)
+            self.idx_bytes = d["idx"].size * 4
+            self.kind = "indexed"
+            self.n_experts = d["n_experts"]
+            self.n_each = d["n"]
+        else:
+            raise SystemExit(f"unknown workload {name}")
+        self.bytes = algorithmic_bytes(self.runs, self.m, self.k, self.n_out, self.idx_bytes)
+        wbytes = sum(sum(a.numel() * a.element_size() for a in trip) for trip in base)
+        copies = max(1, -(-ROTATE_BYTES // wbytes))
+        self.copies = []
+        for c in range(copies):
+            trip_list = base if c == 0 else [tuple(a.clone() for a in trip) for trip in base]
+            mats = []
+            for (w, s, b), run_ in zip(trip_list, self.runs if self.kind != "indexed" else [None]):
+                if self.kind == "indexed":
+                    mats.append(qgemv.Matrix(4, 64, self.n_each, self.k, w, s, b, n_experts=self.n_experts))
+                else:
+                    bits, group, n = run_
+                    mats.append(qgemv.Matrix(bits, group, n, self.k, w, s, b))
+            self.copies.append((trip_list, mats))
+        self.flat = self.y.view(-1)
+
+    def step(self, i: int, stream: int):
+        _, mats = self.copies[i % len(self.copies)]
+        q = self.qgemv
+        if self.kind == "plain":
+            rc = q.qgemv_run(mats[0].h, self.x, self.m, self.y, 0, stream)
+            assert rc == 0, q.qgemv_strerror(rc)
+        elif self.kind == "strided":
+            for mat, col in zip(mats, self.cols):
+                rc = q.qgemv_run_strided(mat.h, self.x, self.m, self.flat[col:], self.ldy, 0, stream)
+                assert rc == 0, q.qgemv_strerror(rc)
+        else:
+            rc = q.qgemv_run_indexed(mats[0].h, self.x, self.m, self.idx, self.slots, self.y,
+                                     q.QGEMV_EPI_RELU2, stream)
+            assert rc == 0, q.qgemv_strerror(rc)
+
+
+def time_workload(wl: Workload, steps: int, warmup: int, torch):
+    stream = torch.cuda.current_stream()
+    sid = stream.cuda_stream
+    for i in range(warmup):
+        wl.step(i, sid)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    batches = []
+    per = max(1, steps // 5)
+    done = 0
+    # five batches; the median batch gives the per-call time
+    while done < steps:
+        cnt = min(per, steps - done)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(cnt):
+            wl.step(done + i, sid)
+        end.record(stream)
+        end.synchronize()
+        batches.append(start.elapsed_time(end) / cnt)
+        done += cnt
+    torch.cuda.synchronize()
+    ms = float(np.median(batches))
+    return ms, batches
+
+
+def cpu_baseline(budget_s: float = 12.0):
+    """The oracle, as it stands, on a bounded sample of LM-head columns at a
+    1-row window, threads = host cores (capped at 16)."""
+    import oracle
+    from bit_affine_quantized_amd import synth
+
+    threads = max(1, min(16, os.cpu_count() or 1))
+    rng = np.random.default_rng(4000)
+    k, bits, group = synth.LMHEAD_K, synth.LMHEAD_BITS, synth.LMHEAD_GROUP
+    # calibrate on a small sample, then run a sample sized to the budget
+    def sample(n):
+        words = synth.draw_words(rng, (n,), k, bits)
+        scales = synth.draw_scales(rng, (n, k // group))
+        biases = synth.draw_biases(rng, (n, k // group))
+        x = synth.draw_x(rng, 1, k)
+        return words, scales, biases, x
+
+    n0 = 256 * threads
+    w, s, b, x = sample(n0)
+    t0 = time.perf_counter()
+    oracle.gemv(w, s, b, x, bits, group, n0, k, threads=threads)
+    dt = time.perf_counter() - t0
+    n1 = int(max(n0, min(synth.LMHEAD_N, n0 * budget_s / max(dt, 1e-6))))
+    w, s, b, x = sample(n1)
+    t0 = time.perf_counter()
+    oracle.gemv(w, s, b, x, bits, group, n1, k, threads=threads)
+    dt = time.perf_counter() - t0
+    nbytes = algorithmic_bytes([(bits, group, n1)], 1, k, n1)
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n1} of the LM head's 248320 columns (K=2048, 6-bit group 32), 1-row window, "
+                      f"fp64 oracle, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="lmhead", choices=["lmhead", "stack", "experts"])
+    ap.add_argument("--m", type=int, default=1, help="window rows")
+    ap.add_argument("--all", action="store_true", help="also time the other workloads and windows")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the row product shards along output columns with no "
+              "exchange, so a multi-GPU figure is one GPU's share; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from bit_affine_quantized_amd import qgemv, synth
+
+    qgemv.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wl = Workload(args.workload, args.m, torch, qgemv, synth)
+    ms, batches = time_workload(wl, args.steps, args.warmup, torch)
+    gbs = wl.bytes / (ms * 1e-3) / 1e9
+    traffic = read_traffic(f"{args.workload}_m{wl.m}")
+    out = {
+        "metric": "effective HBM GB/s (% of MI355X peak) for affine-quant GEMV, 1-16 row windows",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded uniform codes, bf16 scales/biases/activations)",
+        "config": {"workload": wl.desc, "m": wl.m, "k": wl.k, "algorithmic_bytes": wl.bytes,
+                   "weight_copies": len(wl.copies), "parallelism": "single GPU",
+                   "arithmetic": "exact codes as bf16, bf16 activations, fp32 sums"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_GBS, 4), "traffic": traffic},
+        "batch_ms": [round(b, 6) for b in batches],
+        "kernel_sha": kernel_hash(),
+    }
+    if args.all:
+        extra = {}
+        for name, m in [("lmhead", 1), ("lmhead", 8), ("lmhead", 16), ("stack", 1), ("stack", 16),
+                        ("experts", 16)]:
+            if name == args.workload and m == wl.m:
+                continue
+            w2 = Workload(name, m, torch, qgemv, synth)
+            ms2, _ = time_workload(w2, max(20, args.steps // 2), args.warmup, torch)
+            g2 = w2.bytes / (ms2 * 1e-3) / 1e9
+            extra[f"{name}_m{w2.m}"] = {"us_per_call": round(ms2 * 1e3, 3), "GB/s": round(g2, 1),
+                                        "frac": round(g2 / PEAK_GBS, 4), "bytes": w2.bytes}
+            del w2
+            torch.cuda.empty_cache()
+        out["workloads"] = extra
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

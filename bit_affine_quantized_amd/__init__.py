@@ -3,16 +3,6 @@ for decode windows of 1-16 activation rows).
 
 The product lives in a C-ABI shared library of hand-written HIP kernels for
 gfx950 (``csrc/``, declared in ``include/qgemv.h``); ``qgemv`` is its thin
-ctypes binding.  ``synth`` draws seeded synthetic inputs.
+ctypes binding (``from bit_affine_quantized_amd import qgemv``).  ``synth``
+draws seeded synthetic inputs.
 """
-
-from . import synth  # noqa: F401
-
-__all__ = ["synth", "qgemv"]
-
-
-def __getattr__(name):
-    if name == "qgemv":
-        from . import qgemv as mod
-        return mod
-    raise AttributeError(name)

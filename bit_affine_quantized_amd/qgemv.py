@@ -1,0 +1,180 @@
+"""ctypes binding of libqgemv.so (include/qgemv.h), argument marshalling only.
+
+The module-level functions carry the C names and take plain integers
+(device pointers) or torch tensors (their ``data_ptr()`` is passed).  Every
+step of the product runs in the library's HIP kernels; nothing here computes.
+Loading fails loudly when the library has not been built.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqgemv.so")
+
+QGEMV_OK = 0
+QGEMV_E_ARG, QGEMV_E_BITS, QGEMV_E_GROUP, QGEMV_E_SHAPE, QGEMV_E_STRIDE = -1, -2, -3, -4, -5
+QGEMV_E_ALIGN, QGEMV_E_WINDOW, QGEMV_E_ALIAS, QGEMV_E_NOKERNEL, QGEMV_E_HIP = -6, -7, -8, -9, -10
+QGEMV_EPI_NONE, QGEMV_EPI_RELU2 = 0, 1
+QGEMV_MAX_WINDOW = 16
+
+_lib = None
+_lock = threading.Lock()
+
+
+class QgemvError(RuntimeError):
+    def __init__(self, what: str, status: int):
+        super().__init__(f"{what}: {qgemv_strerror(status)}")
+        self.status = status
+
+
+class qgemv_desc(ctypes.Structure):
+    _fields_ = [("bits", ctypes.c_int32), ("group", ctypes.c_int32), ("n", ctypes.c_int64),
+                ("k", ctypes.c_int64), ("n_experts", ctypes.c_int32), ("w", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p)]
+
+
+def load(path: str = LIB_PATH):
+    """The loaded library; raises if it is not built (no fallback exists)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(path):
+                raise ImportError(f"libqgemv.so is not built ({path}); run __graft_entry__.build()")
+            lib = ctypes.CDLL(path)
+            p, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+            lib.qgemv_create.argtypes = [ctypes.POINTER(qgemv_desc), ctypes.POINTER(p)]
+            lib.qgemv_create.restype = ctypes.c_int
+            lib.qgemv_destroy.argtypes = [p]
+            lib.qgemv_destroy.restype = None
+            lib.qgemv_run.argtypes = [p, p, i32, p, i32, p]
+            lib.qgemv_run.restype = ctypes.c_int
+            lib.qgemv_run_strided.argtypes = [p, p, i32, p, i64, i32, p]
+            lib.qgemv_run_strided.restype = ctypes.c_int
+            lib.qgemv_run_indexed.argtypes = [p, p, i32, p, i32, p, i32, p]
+            lib.qgemv_run_indexed.restype = ctypes.c_int
+            lib.qgemv_debug_unpack.argtypes = [p, i32, p, p]
+            lib.qgemv_debug_unpack.restype = ctypes.c_int
+            lib.qgemv_strerror.argtypes = [ctypes.c_int]
+            lib.qgemv_strerror.restype = ctypes.c_char_p
+            lib.qgemv_query.argtypes = [p, ctypes.POINTER(ctypes.c_int64 * 6)]
+            lib.qgemv_query.restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def _addr(t) -> int:
+    if t is None:
+        return 0
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ---- the C entry points, same names -----------------------------------------
+
+def qgemv_strerror(status: int) -> str:
+    return load().qgemv_strerror(status).decode()
+
+
+def qgemv_create(bits, group, n, k, w, scales, biases, n_experts=1):
+    """Returns (status, handle); handle is None on a refusal."""
+    d = qgemv_desc(bits, group, n, k, n_experts, _addr(w), _addr(scales), _addr(biases))
+    h = ctypes.c_void_p()
+    rc = load().qgemv_create(ctypes.byref(d), ctypes.byref(h))
+    return rc, (h.value if rc == QGEMV_OK else None)
+
+
+def qgemv_destroy(h) -> None:
+    load().qgemv_destroy(h)
+
+
+def qgemv_run(h, x, m, y, epi=QGEMV_EPI_NONE, stream=None) -> int:
+    return load().qgemv_run(h, _addr(x), m, _addr(y), epi, _stream(stream))
+
+
+def qgemv_run_strided(h, x, m, y, ldy, epi=QGEMV_EPI_NONE, stream=None) -> int:
+    return load().qgemv_run_strided(h, _addr(x), m, _addr(y), ldy, epi, _stream(stream))
+
+
+def qgemv_run_indexed(h, x, m, idx, slots, y, epi=QGEMV_EPI_NONE, stream=None) -> int:
+    return load().qgemv_run_indexed(h, _addr(x), m, _addr(idx), slots, _addr(y), epi, _stream(stream))
+
+
+def qgemv_debug_unpack(h, expert, codes, stream=None) -> int:
+    return load().qgemv_debug_unpack(h, expert, _addr(codes), _stream(stream))
+
+
+def qgemv_query(h):
+    out = (ctypes.c_int64 * 6)()
+    rc = load().qgemv_query(h, ctypes.byref(out))
+    return rc, list(out)
+
+
+# ---- convenience wrapper over torch device tensors ---------------------------
+
+class Matrix:
+    """One handle over torch device tensors (kept alive with the handle).
+
+    w: int32/uint32 [E][N][K*bits/32]; scales, biases: int16/bf16 [E][N][K/G];
+    x: bf16 (or int16 bits) [M][K]; y: float32.  Statuses other than
+    QGEMV_OK raise QgemvError."""
+
+    def __init__(self, bits, group, n, k, w, scales, biases, n_experts=1):
+        self.bits, self.group, self.n, self.k, self.n_experts = bits, group, n, k, n_experts
+        self._keep = (w, scales, biases)
+        rc, h = qgemv_create(bits, group, n, k, w, scales, biases, n_experts)
+        if rc != QGEMV_OK:
+            raise QgemvError("qgemv_create", rc)
+        self.h = h
+
+    def _chk(self, rc, what):
+        if rc != QGEMV_OK:
+            raise QgemvError(what, rc)
+
+    def run(self, x, y, m=None, epi=QGEMV_EPI_NONE, stream=None):
+        m = x.shape[0] if m is None else m
+        self._chk(qgemv_run(self.h, x, m, y, epi, stream), "qgemv_run")
+        return y
+
+    def run_strided(self, x, y, ldy, m=None, epi=QGEMV_EPI_NONE, stream=None):
+        m = x.shape[0] if m is None else m
+        self._chk(qgemv_run_strided(self.h, x, m, y, ldy, epi, stream), "qgemv_run_strided")
+        return y
+
+    def run_indexed(self, x, idx, y, epi=QGEMV_EPI_NONE, stream=None):
+        m, slots = idx.shape
+        self._chk(qgemv_run_indexed(self.h, x, m, idx, slots, y, epi, stream), "qgemv_run_indexed")
+        return y
+
+    def debug_unpack(self, codes, expert=0, stream=None):
+        self._chk(qgemv_debug_unpack(self.h, expert, codes, stream), "qgemv_debug_unpack")
+        return codes
+
+    def query(self):
+        rc, out = qgemv_query(self.h)
+        self._chk(rc, "qgemv_query")
+        return out
+
+    def close(self):
+        if getattr(self, "h", None):
+            qgemv_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

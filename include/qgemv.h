@@ -1,0 +1,153 @@
+/*
+ * qgemv.h — C ABI of the MI355X (gfx950) MLX-affine quantized row product.
+ *
+ * The operation (one handle = one quantized matrix, or a stack of experts):
+ *
+ *   q[n,k]  = code k of row n: bits [k*bits, k*bits+bits) of the row's
+ *             bitstream, low code first, the bitstream cut into little-endian
+ *             32-bit words; a row of K codes ends on a word.
+ *   w[n,k]  = scale[n, k/group] * q[n,k] + bias[n, k/group]
+ *   y[i,n]  = epi( sum_k w[n,k] * x[i,k] )   for the rows i of a 1..16-row
+ *             activation window, in fp32 with fp32 group sums.
+ *
+ * Sources, on "Qwen3.8-Flash-Next faster kernels in Zig engine - #788":
+ *  - commit "...row kernel at every MLX width": every MLX affine width
+ *    (2, 3, 4, 5, 6, 8 bits) at groups of 32, 64 and 128; 3- and 5-bit rows
+ *    hold eight codes in three or five bytes, low code first; a row ends on a
+ *    word; a strided call writes one member of a fused stack straight into
+ *    the stack output; options relu2 and indexed slots; a row's bits are the
+ *    same alone and inside 2-, 3-, 8- and 16-row windows.
+ *  - commit "...lane kernel formats" (Layout.y_stride): a row stride below N
+ *    is refused; a strided write leaves the gaps untouched.
+ * and on "Qwen3.8-Flash-Next support for oQ in Zig engine - #774":
+ *  - "What this changes", item 3: every width kernel is resolved when the
+ *    weights are admitted ("fail closed"), so a bad width refuses the
+ *    handle, never a request; refusals are named.
+ *  - "Exactness", item "Precision": activations stay bf16, group sums fp32.
+ *
+ * Memory and ownership.  Every array argument is a DEVICE pointer (HIP
+ * device memory, e.g. a torch tensor's data_ptr()).  The library never
+ * allocates, frees or synchronises device memory: a handle BORROWS the
+ * weight pointers given at create, which must stay valid until
+ * qgemv_destroy.  A handle is immutable after create, so runs on different
+ * streams may share it.
+ *
+ * Error behaviour.  Every argument that can be checked on the host is
+ * checked before any HIP call; on a refusal nothing is launched and no
+ * output is touched.  Run calls enqueue on the given stream and return
+ * without waiting; a device-side fault surfaces at the caller's next
+ * synchronisation, as usual in HIP.  Statuses are the QGEMV_E_* values;
+ * qgemv_strerror names them.
+ */
+#ifndef QGEMV_H
+#define QGEMV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------- */
+#define QGEMV_OK 0
+#define QGEMV_E_ARG (-1)      /* null pointer or handle, bad enum, misuse   */
+#define QGEMV_E_BITS (-2)     /* bits not in {2,3,4,5,6,8}                  */
+#define QGEMV_E_GROUP (-3)    /* group not in {32,64,128}                   */
+#define QGEMV_E_SHAPE (-4)    /* n < 1, k < 1, group does not divide k,
+                                 k*bits not a multiple of 32, too large     */
+#define QGEMV_E_STRIDE (-5)   /* output row stride below n                  */
+#define QGEMV_E_ALIGN (-6)    /* pointer not aligned to its element type    */
+#define QGEMV_E_WINDOW (-7)   /* window rows outside 0..16                  */
+#define QGEMV_E_ALIAS (-8)    /* output overlaps an input                   */
+#define QGEMV_E_NOKERNEL (-9) /* no compiled kernel for this shape          */
+#define QGEMV_E_HIP (-10)     /* a HIP runtime call failed                  */
+
+/* ---- epilogues ------------------------------------------------------- */
+#define QGEMV_EPI_NONE 0
+#define QGEMV_EPI_RELU2 1     /* y > 0 ? y*y : (y is NaN ? y : +0), on fp32 y */
+
+#define QGEMV_MAX_WINDOW 16
+
+/* Weights of one handle.
+ *   bits       code width: 2, 3, 4, 5, 6 or 8.
+ *   group      codes per scale/bias along K: 32, 64 or 128.
+ *   n, k       output columns and reduction length; group | k,
+ *              k*bits % 32 == 0, n*k < 2^40.
+ *   n_experts  >= 1.  Expert e's arrays follow expert e-1's without gaps.
+ *   w          uint32 [n_experts][n][k*bits/32], 16-byte aligned.
+ *   scales     bf16 bits [n_experts][n][k/group], 2-byte aligned.
+ *   biases     bf16 bits [n_experts][n][k/group], 2-byte aligned.          */
+typedef struct qgemv_desc {
+  int32_t bits;
+  int32_t group;
+  int64_t n;
+  int64_t k;
+  int32_t n_experts;
+  const uint32_t* w;
+  const uint16_t* scales;
+  const uint16_t* biases;
+} qgemv_desc;
+
+typedef struct qgemv_handle* qgemv_t;
+
+/* Validate the weights' shape and pointers, resolve the compiled kernel for
+ * (bits, group) and fix the launch geometry from (bits, group, n, k) only —
+ * never from the window — so a row's bits cannot depend on the window it
+ * runs in.  Makes no HIP call (the current device's compute-unit count is
+ * read at the first run on each device).
+ * Returns QGEMV_OK and *out, or a refusal (then *out is untouched). */
+int qgemv_create(const qgemv_desc* d, qgemv_t* out);
+
+/* Free the host-side handle (never touches device memory). NULL is a no-op. */
+void qgemv_destroy(qgemv_t h);
+
+/* y[i][j] for i < m, j < n, contiguous (row stride n).
+ *   x  bf16 bits [m][k] device, 16-byte aligned.
+ *   m  window rows, 0..16; m == 0 launches nothing and returns QGEMV_OK.
+ *      A window whose staged activations exceed the LDS of one block
+ *      (m*k*2.125 bytes > 152 KiB) is refused with QGEMV_E_WINDOW.
+ *   y  fp32 [m][n] device, 4-byte aligned, must not overlap x or weights.
+ *   epi QGEMV_EPI_NONE or QGEMV_EPI_RELU2.
+ *   stream  hipStream_t (NULL = the null stream).
+ * Refused on a handle with n_experts > 1 (QGEMV_E_ARG): describe a single
+ * expert with its own qgemv_create over the expert's offset pointers. */
+int qgemv_run(qgemv_t h, const uint16_t* x, int32_t m, float* y, int32_t epi, void* stream);
+
+/* As qgemv_run, but writes y[i*ldy + j] for j < n only; every other element
+ * of y is left untouched.  ldy < n is refused (QGEMV_E_STRIDE).  One member
+ * (run) of a fused stack writes its columns into the stack output by
+ * passing y + first_column and the stack's ldy.  Each row's bits equal
+ * qgemv_run's. */
+int qgemv_run_strided(qgemv_t h, const uint16_t* x, int32_t m, float* y, int64_t ldy,
+                      int32_t epi, void* stream);
+
+/* Indexed expert slots: y[(i*slots + s)*n + j] = epi(row i times expert
+ * idx[i*slots + s]) for i < m, s < slots, j < n.
+ *   idx  int32 [m][slots] device.  Each value must lie in [0, n_experts):
+ *        a precondition on the caller (the values are read on the device
+ *        only); values outside it write nothing for that slot.
+ *   slots  0..64; slots == 0 or m == 0 launches nothing.
+ * Each expert named in idx is read once per call; each (i, s) output's bits
+ * equal qgemv_run on that expert's single-expert handle with row i. */
+int qgemv_run_indexed(qgemv_t h, const uint16_t* x, int32_t m, const int32_t* idx,
+                      int32_t slots, float* y, int32_t epi, void* stream);
+
+/* Test hook: the kernels' own unpack of expert `expert` into codes[n][k]
+ * (uint8, device, n*k bytes): each code is cut and converted exactly as the
+ * product kernels do it, then written back as an integer. */
+int qgemv_debug_unpack(qgemv_t h, int32_t expert, uint8_t* codes, void* stream);
+
+/* Name of a status code ("QGEMV_E_STRIDE", ...); never NULL. */
+const char* qgemv_strerror(int status);
+
+/* Launch geometry fixed at create (for tests and reports):
+ *   out[0] lanes per output column, out[1] output columns per wave,
+ *   out[2] codes per lane chunk, out[3] threads per block,
+ *   out[4] output columns per block tile, out[5] compute units seen.   */
+int qgemv_query(qgemv_t h, int64_t out[6]);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMV_H */

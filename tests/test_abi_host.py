@@ -1,0 +1,134 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, it
+exports every entry point include/qgemv.h declares, and every refusal is
+returned by name before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from bit_affine_quantized_amd import qgemv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qgemv.h")
+
+# Fake, suitably aligned device addresses: create() never dereferences them.
+W, S, B, X, Y, IDX = 0x100000, 0x200000, 0x300000, 0x400000, 0x800000, 0xC00000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qgemv_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = qgemv.load()
+    names = declared_functions()
+    assert {"qgemv_create", "qgemv_run", "qgemv_run_strided", "qgemv_run_indexed",
+            "qgemv_destroy", "qgemv_strerror", "qgemv_debug_unpack"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_names():
+    for code, name in [(0, "QGEMV_OK"), (-1, "QGEMV_E_ARG"), (-2, "QGEMV_E_BITS"), (-3, "QGEMV_E_GROUP"),
+                       (-4, "QGEMV_E_SHAPE"), (-5, "QGEMV_E_STRIDE"), (-6, "QGEMV_E_ALIGN"),
+                       (-7, "QGEMV_E_WINDOW"), (-8, "QGEMV_E_ALIAS"), (-9, "QGEMV_E_NOKERNEL"),
+                       (-10, "QGEMV_E_HIP")]:
+        assert qgemv.qgemv_strerror(code) == name
+    assert qgemv.qgemv_strerror(12345) == "QGEMV_E_UNKNOWN"
+
+
+@pytest.mark.parametrize("bits,group,n,k,w,want", [
+    (7, 64, 16, 2048, W, qgemv.QGEMV_E_BITS),
+    (1, 64, 16, 2048, W, qgemv.QGEMV_E_BITS),
+    (4, 16, 16, 2048, W, qgemv.QGEMV_E_GROUP),
+    (4, 256, 16, 2048, W, qgemv.QGEMV_E_GROUP),
+    (4, 64, 0, 2048, W, qgemv.QGEMV_E_SHAPE),
+    (4, 64, 16, 0, W, qgemv.QGEMV_E_SHAPE),
+    (4, 64, 16, 2080, W, qgemv.QGEMV_E_SHAPE),   # group does not divide K
+    (4, 64, 16, 2048, 0, qgemv.QGEMV_E_ARG),     # null weights
+    (4, 64, 16, 2048, W + 4, qgemv.QGEMV_E_ALIGN),
+])
+def test_create_refusals(bits, group, n, k, w, want):
+    rc, h = qgemv.qgemv_create(bits, group, n, k, w, S, B)
+    assert rc == want and h is None
+
+
+def test_create_refuses_misaligned_scales_and_bad_experts():
+    assert qgemv.qgemv_create(4, 64, 16, 2048, W, S + 1, B)[0] == qgemv.QGEMV_E_ALIGN
+    assert qgemv.qgemv_create(4, 64, 16, 2048, W, S, B + 1)[0] == qgemv.QGEMV_E_ALIGN
+    assert qgemv.qgemv_create(4, 64, 16, 2048, W, S, B, n_experts=0)[0] == qgemv.QGEMV_E_SHAPE
+    assert qgemv.qgemv_create(4, 64, 16, 2048, W, 0, B)[0] == qgemv.QGEMV_E_ARG
+
+
+def test_create_accepts_every_pair_without_a_device():
+    for bits in (2, 3, 4, 5, 6, 8):
+        for group in (32, 64, 128):
+            for k in (group, 2048, 4096, 96 * group // 32 if group == 32 else group * 3):
+                rc, h = qgemv.qgemv_create(bits, group, 48, k, W, S, B)
+                assert rc == 0, (bits, group, k, qgemv.qgemv_strerror(rc))
+                rc, geo = qgemv.qgemv_query(h)
+                assert rc == 0
+                lpr, cols_per_wave, codes_per_chunk = geo[0], geo[1], geo[2]
+                assert lpr & (lpr - 1) == 0 and 1 <= lpr <= 64
+                assert k % (codes_per_chunk * lpr) == 0
+                qgemv.qgemv_destroy(h)
+
+
+@pytest.fixture
+def handle():
+    rc, h = qgemv.qgemv_create(4, 64, 256, 2048, W, S, B)
+    assert rc == 0
+    yield h
+    qgemv.qgemv_destroy(h)
+
+
+def test_run_refusals(handle):
+    h = handle
+    run, strided = qgemv.qgemv_run, qgemv.qgemv_run_strided
+    assert run(None, X, 1, Y, 0, 0) == qgemv.QGEMV_E_ARG
+    assert run(h, X, 17, Y, 0, 0) == qgemv.QGEMV_E_WINDOW
+    assert run(h, X, -1, Y, 0, 0) == qgemv.QGEMV_E_WINDOW
+    assert run(h, X, 1, Y, 2, 0) == qgemv.QGEMV_E_ARG          # unknown epilogue
+    assert run(h, 0, 1, Y, 0, 0) == qgemv.QGEMV_E_ARG
+    assert run(h, X, 1, 0, 0, 0) == qgemv.QGEMV_E_ARG
+    assert run(h, X + 8, 1, Y, 0, 0) == qgemv.QGEMV_E_ALIGN
+    assert run(h, X, 1, Y + 2, 0, 0) == qgemv.QGEMV_E_ALIGN
+    assert strided(h, X, 1, Y, 255, 0, 0) == qgemv.QGEMV_E_STRIDE
+    # y overlapping x, or the weights
+    assert run(h, X, 2, X + 1024, 0, 0) == qgemv.QGEMV_E_ALIAS
+    assert run(h, X, 1, W + 64, 0, 0) == qgemv.QGEMV_E_ALIAS
+    assert run(h, X, 1, S, 0, 0) == qgemv.QGEMV_E_ALIAS
+    # a strided window's span runs to (m-1)*ldy + n
+    assert strided(h, X, 2, Y, 1 << 20, 0, 0) != qgemv.QGEMV_E_ALIAS or True
+    assert strided(h, X, 2, X - 4 * ((1 << 12) + 256) + 4 * 4096, 1 << 12, 0, 0) == qgemv.QGEMV_E_ALIAS
+
+
+def test_empty_window_is_a_no_op(handle):
+    # nothing is launched, so this succeeds without a device
+    assert qgemv.qgemv_run(handle, X, 0, Y, 0, 0) == qgemv.QGEMV_OK
+    assert qgemv.qgemv_run_strided(handle, X, 0, Y, 256, 0, 0) == qgemv.QGEMV_OK
+    assert qgemv.qgemv_run_indexed(handle, X, 0, IDX, 8, Y, 0, 0) == qgemv.QGEMV_OK
+    assert qgemv.qgemv_run_indexed(handle, X, 4, IDX, 0, Y, 0, 0) == qgemv.QGEMV_OK
+
+
+def test_indexed_refusals():
+    rc, h = qgemv.qgemv_create(4, 64, 256, 2048, W, S, B, n_experts=4)
+    assert rc == 0
+    assert qgemv.qgemv_run(h, X, 1, Y, 0, 0) == qgemv.QGEMV_E_ARG   # plain run on a stack
+    assert qgemv.qgemv_run_indexed(h, X, 2, IDX, 65, Y, 0, 0) == qgemv.QGEMV_E_ARG
+    assert qgemv.qgemv_run_indexed(h, X, 2, 0, 8, Y, 0, 0) == qgemv.QGEMV_E_ARG
+    assert qgemv.qgemv_run_indexed(h, X, 2, IDX + 2, 8, Y, 0, 0) == qgemv.QGEMV_E_ALIGN
+    assert qgemv.qgemv_run_indexed(h, X, 2, IDX, 8, IDX, 0, 0) == qgemv.QGEMV_E_ALIAS
+    assert qgemv.qgemv_debug_unpack(h, 4, Y, 0) == qgemv.QGEMV_E_ARG
+    qgemv.qgemv_destroy(h)
+
+
+def test_valid_run_without_a_device_reports_hip(handle):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert qgemv.qgemv_run(handle, X, 1, Y, 0, 0) == qgemv.QGEMV_E_HIP

@@ -1,0 +1,366 @@
+"""GPU parity of the HIP row product against the CPU oracle, through the C ABI.
+
+Bars (fp32 outputs):
+  * unpacked codes: bit for bit equal to the oracle's, every width;
+  * outputs: |y - y64| <= K * 2^-24 * sum|w*x| + 1e-7 (y64, sum from the oracle);
+  * relu2: within the bound that y's bound implies, and bit for bit equal to
+    fp32 y*y of the plain call;
+  * a row alone equals the same row in 2-, 3-, 8- and 16-row windows at every
+    position, bit for bit; strided and indexed outputs equal the plain call
+    bit for bit; a repeat gives the same bytes;
+  * exact-representable inputs give y == y64 exactly;
+  * scales 1% off (negative control) exceed the pages' bound.
+"""
+
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from bit_affine_quantized_amd import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+from bit_affine_quantized_amd import qgemv  # noqa: E402
+
+THREADS = max(1, min(16, os.cpu_count() or 1))
+PAIRS = list(synth.PAIRS)
+DEV = "cuda"
+
+
+def dev(a: np.ndarray):
+    a = np.ascontiguousarray(a)
+    view = {np.dtype(np.uint32): np.int32, np.dtype(np.uint16): np.int16,
+            np.dtype(np.int32): np.int32, np.dtype(np.uint8): np.uint8}[a.dtype]
+    return torch.from_numpy(a.view(view)).to(DEV)
+
+
+def matrix_of(d, expert=None):
+    w, s, b = d["words"], d["scales"], d["biases"]
+    if expert is not None:
+        w, s, b = w[expert], s[expert], b[expert]
+    tw, ts, tb = dev(w), dev(s), dev(b)
+    return qgemv.Matrix(d["bits"], d["group"], d["n"], d["k"], tw, ts, tb)
+
+
+def run(mat, xt, m=None, epi=0):
+    m = xt.shape[0] if m is None else m
+    y = torch.empty((m, mat.n), dtype=torch.float32, device=DEV)
+    mat.run(xt[:m], y, m=m, epi=epi)
+    return y
+
+
+def bits_equal(a, b) -> bool:
+    return torch.equal(a.contiguous().view(torch.int32), b.contiguous().view(torch.int32))
+
+
+def check_bound(y_gpu: np.ndarray, y64, a64, k, label=""):
+    err = np.abs(y_gpu.astype(np.float64) - y64)
+    tol = oracle.tol_y(a64, k)
+    bad = np.argwhere(~(err <= tol))
+    assert bad.size == 0, f"{label}: {len(bad)} outputs outside the bound, first {bad[:3].tolist()}, " \
+                          f"worst err/bound {oracle.worst_fraction(err, tol):.3f}"
+    return oracle.worst_fraction(err, tol)
+
+
+def print_case(*a):
+    print(*a, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# codes
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bits,group", PAIRS)
+def test_unpacked_codes_bit_exact(bits, group):
+    print_case("unpack", bits, group)
+    n, k = 24, 4096
+    d = synth.matrix(synth.sweep_seed(bits, group) + 1, bits, group, n, k)
+    mat = matrix_of(d)
+    codes = torch.empty((n, k), dtype=torch.uint8, device=DEV)
+    mat.debug_unpack(codes)
+    torch.cuda.synchronize()
+    assert np.array_equal(codes.cpu().numpy(), oracle.unpack(d["words"], bits, n, k))
+    # every value at every bit offset of a word
+    kk = 32 * (1 << bits)
+    kk = ((kk + group - 1) // group) * group
+    sc = synth.sweep_codes(3, kk, bits)
+    words = synth.pack_codes(sc, bits)
+    ones = synth.to_bf16_bits(np.ones((3, kk // group)))
+    m2 = qgemv.Matrix(bits, group, 3, kk, dev(words), dev(ones), dev(ones))
+    c2 = torch.empty((3, kk), dtype=torch.uint8, device=DEV)
+    m2.debug_unpack(c2)
+    torch.cuda.synchronize()
+    assert np.array_equal(c2.cpu().numpy(), oracle.unpack(words, bits, 3, kk))
+    assert np.array_equal(c2.cpu().numpy(), sc)
+
+
+# ---------------------------------------------------------------------------
+# the width sweep: N = K = 4096 at every pair, a 16-row window
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bits,group", PAIRS)
+def test_sweep_within_bound(bits, group):
+    print_case("sweep", bits, group)
+    d = synth.sweep(bits, group, m=16)
+    n, k = d["n"], d["k"]
+    mat = matrix_of(d)
+    xt = dev(d["x"])
+    y16 = run(mat, xt).cpu().numpy()
+    y64, a64, t64 = oracle.gemv(d["words"], d["scales"], d["biases"], d["x"], bits, group, n, k,
+                                threads=THREADS)
+    frac = check_bound(y16, y64, a64, k, f"{bits}/{group}")
+    pages = oracle.worst_fraction(np.abs(y16 - y64), oracle.tol_pages(t64, group, k))
+    print_case(f"  worst err/bound {frac:.4f}; of the pages' bound {pages:.4f}")
+    # negative control: scales 1% off must exceed the pages' bound (row 0)
+    yb, _, _ = oracle.gemv(d["words"], d["scales"], d["biases"], d["x"][:1], bits, group, n, k,
+                           scale_mult=1.01, threads=THREADS)
+    ctrl = oracle.worst_fraction(np.abs(y16[:1] - yb), oracle.tol_pages(t64[:1], group, k))
+    assert ctrl > 1.0, f"negative control only {ctrl:.3f} of the bound"
+
+
+@pytest.mark.parametrize("bits,group", PAIRS)
+def test_window_invariance(bits, group):
+    """Every row of a 64-row pool alone equals itself at every position of
+    every 2-, 3-, 8- and 16-row window, bit for bit."""
+    print_case("windows", bits, group)
+    d = synth.sweep(bits, group, m=0)
+    rng = np.random.default_rng(synth.sweep_seed(bits, group) + 7)
+    pool = dev(synth.draw_x(rng, 64, d["k"]))
+    mat = matrix_of(d)
+    alone = torch.empty((64, d["n"]), dtype=torch.float32, device=DEV)
+    for r in range(64):
+        mat.run(pool[r:r + 1], alone[r:r + 1], m=1)
+    for m in (2, 3, 8, 16):
+        y = torch.empty((m, d["n"]), dtype=torch.float32, device=DEV)
+        for s0 in range(0, 64 - m + 1):
+            mat.run(pool[s0:s0 + m], y, m=m)
+            assert bits_equal(y, alone[s0:s0 + m]), f"window {m} at {s0}"
+
+
+@pytest.mark.parametrize("bits,group", PAIRS)
+def test_exact_representable_inputs(bits, group):
+    """s in {2^-8, 2^-7, 2^-6}, bias a multiple of 2^-8, x in {-1, 0, 1}: every
+    summation order is exact, so y must equal y64 exactly."""
+    n, k = 72, 4096
+    d = synth.exact_case(9000 + bits * 10 + group, bits, group, n, k, 16)
+    mat = matrix_of(d)
+    xt = dev(d["x"])
+    y64, _, _ = oracle.gemv(d["words"], d["scales"], d["biases"], d["x"], bits, group, n, k)
+    for m in (1, 16):
+        y = run(mat, xt, m).cpu().numpy().astype(np.float64)
+        assert np.array_equal(y, y64[:m]), f"m={m}"
+
+
+# ---------------------------------------------------------------------------
+# epilogue, stride, repeat, NaN
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bits,group", [(2, 32), (3, 64), (4, 64), (5, 128), (6, 32), (8, 128)])
+def test_relu2_and_strided(bits, group):
+    print_case("relu2/strided", bits, group)
+    n, k = 1000, 2048      # ragged against every tile size
+    d = synth.matrix(6000 + bits * 10 + group, bits, group, n, k, 8)
+    mat = matrix_of(d)
+    xt = dev(d["x"])
+    y = run(mat, xt)
+    r = run(mat, xt, epi=qgemv.QGEMV_EPI_RELU2)
+    want = torch.where(y > 0, y * y, torch.zeros_like(y))
+    assert bits_equal(r, want)
+    r1 = run(mat, xt[3:4], epi=qgemv.QGEMV_EPI_RELU2)
+    assert bits_equal(r1[0], r[3])
+    y64, a64, _ = oracle.gemv(d["words"], d["scales"], d["biases"], d["x"], bits, group, n, k)
+    tol = oracle.tol_relu2(y64, oracle.tol_y(a64, k))
+    r64 = oracle.relu2(y64)
+    assert np.all(np.abs(r.cpu().numpy() - r64) <= tol)
+    # strided: a sentinel-filled wider output; gaps must keep their bytes
+    ldy = n + 37
+    sentinel = torch.full((8, ldy), 0x7FC0BEEF, dtype=torch.int32, device=DEV)
+    ys = sentinel.clone().view(torch.float32)
+    col = 5
+    flat = ys.view(-1)[col:]
+    mat.run_strided(xt, flat, ldy)
+    assert bits_equal(ys[:, col:col + n], y)
+    gap = torch.ones((8, ldy), dtype=torch.bool, device=DEV)
+    gap[:, col:col + n] = False
+    assert torch.equal(ys.view(torch.int32)[gap], sentinel[gap])
+    # repeat: the same bytes
+    y2 = run(mat, xt)
+    assert bits_equal(y, y2)
+
+
+def test_nan_row_stays_in_its_row():
+    bits, group, n, k = 4, 64, 512, 2048
+    d = synth.matrix(77, bits, group, n, k, 3)
+    x = d["x"].copy()
+    x[1, 100] = 0x7FC0  # bf16 NaN
+    mat = matrix_of(d)
+    y = run(mat, dev(x)).cpu().numpy()
+    yc = run(mat, dev(d["x"])).cpu().numpy()
+    assert np.all(np.isnan(y[1]))
+    assert np.array_equal(y[0].view(np.int32), yc[0].view(np.int32))
+    assert np.array_equal(y[2].view(np.int32), yc[2].view(np.int32))
+
+
+def test_refusals_leave_output_untouched():
+    bits, group, n, k = 4, 64, 256, 2048
+    d = synth.matrix(78, bits, group, n, k, 2)
+    mat = matrix_of(d)
+    xt = dev(d["x"])
+    y = torch.full((2, n), 3.0, device=DEV)
+    assert qgemv.qgemv_run(mat.h, xt, 0, y) == qgemv.QGEMV_OK
+    assert qgemv.qgemv_run(mat.h, xt, 17, y) == qgemv.QGEMV_E_WINDOW
+    assert qgemv.qgemv_run_strided(mat.h, xt, 2, y, n - 1) == qgemv.QGEMV_E_STRIDE
+    assert qgemv.qgemv_run(mat.h, xt, 2, xt) == qgemv.QGEMV_E_ALIAS
+    torch.cuda.synchronize()
+    assert torch.all(y == 3.0)
+
+
+# ---------------------------------------------------------------------------
+# edge shapes: narrow, ragged, tiny K (one-unit geometry), one column
+# ---------------------------------------------------------------------------
+
+EDGE = [(6, 64, 48, 2048), (5, 128, 6192, 2048), (4, 32, 1, 2048), (3, 32, 33, 32),
+        (5, 32, 65, 96), (6, 64, 17, 192), (2, 128, 129, 384), (8, 32, 3, 32), (3, 128, 40, 4096 + 128)]
+
+
+@pytest.mark.parametrize("bits,group,n,k", EDGE)
+def test_edge_shapes(bits, group, n, k):
+    print_case("edge", bits, group, n, k)
+    d = synth.matrix(8000 + n + k, bits, group, n, k, 3)
+    mat = matrix_of(d)
+    xt = dev(d["x"])
+    y3 = run(mat, xt)
+    y64, a64, _ = oracle.gemv(d["words"], d["scales"], d["biases"], d["x"], bits, group, n, k)
+    check_bound(y3.cpu().numpy(), y64, a64, k, f"edge {bits}/{group} {n}x{k}")
+    for r in range(3):
+        assert bits_equal(run(mat, xt[r:r + 1])[0], y3[r])
+    codes = torch.empty((n, k), dtype=torch.uint8, device=DEV)
+    mat.debug_unpack(codes)
+    torch.cuda.synchronize()
+    assert np.array_equal(codes.cpu().numpy(), oracle.unpack(d["words"], bits, n, k))
+
+
+# ---------------------------------------------------------------------------
+# the named workloads at full size
+# ---------------------------------------------------------------------------
+
+def test_single_matrix_config():
+    d = synth.single(m=1)
+    n, k, bits, group = d["n"], d["k"], d["bits"], d["group"]
+    mat = matrix_of(d)
+    y = run(mat, dev(d["x"])).cpu().numpy()
+    y64, a64, t64 = oracle.gemv(d["words"], d["scales"], d["biases"], d["x"], bits, group, n, k)
+    frac = check_bound(y, y64, a64, k, "single")
+    yb, _, _ = oracle.gemv(d["words"], d["scales"], d["biases"], d["x"], bits, group, n, k, scale_mult=1.01)
+    assert oracle.worst_fraction(np.abs(y - yb), oracle.tol_pages(t64, group, k)) > 1.0
+    print_case(f"single: worst err/bound {frac:.4f}")
+
+
+@pytest.mark.parametrize("m", [1, 16])
+def test_stack_config(m):
+    """Three runs (4/64 x 2048, 5/128 x 6192, 6/64 x 48) written by strided
+    calls into one 8288-column output row."""
+    st = synth.stack(m=m)
+    k, ldy = st["k"], st["ldy"]
+    xt = dev(st["x"])
+    y = torch.full((m, ldy), float("nan"), device=DEV)
+    flat = y.view(-1)
+    mats = []
+    for run_ in st["runs"]:
+        d = dict(run_, n_experts=1)
+        mat = matrix_of(d)
+        mats.append(mat)
+        mat.run_strided(xt, flat[run_["col"]:], ldy)
+    for run_, mat in zip(st["runs"], mats):
+        n, col = run_["n"], run_["col"]
+        plain = run(mat, xt)
+        assert bits_equal(y[:, col:col + n], plain)
+        y64, a64, _ = oracle.gemv(run_["words"], run_["scales"], run_["biases"], st["x"],
+                                  run_["bits"], run_["group"], n, k, threads=THREADS)
+        check_bound(y[:, col:col + n].cpu().numpy(), y64, a64, k, f"stack run at {col}")
+    assert not torch.any(torch.isnan(y))
+
+
+@pytest.fixture(scope="module")
+def lmhead():
+    d = synth.lmhead(m=16)
+    d["mat"] = matrix_of(d)
+    d["xt"] = dev(d["x"])
+    return d
+
+
+@pytest.mark.parametrize("m", [1, 8, 16])
+def test_lmhead_sampled(lmhead, m):
+    d = lmhead
+    n, k, bits, group = d["n"], d["k"], d["bits"], d["group"]
+    y = run(d["mat"], d["xt"], m)
+    rng = np.random.default_rng(m)
+    cols = np.unique(np.concatenate([np.arange(64), np.arange(n - 64, n),
+                                     rng.integers(0, n, 384)]))
+    y64, a64, _ = oracle.gemv(d["words"][cols], d["scales"][cols], d["biases"][cols], d["x"][:m],
+                              bits, group, len(cols), k, threads=THREADS)
+    check_bound(y[:, cols].cpu().numpy(), y64, a64, k, f"lmhead m={m}")
+    # the same rows alone, at full size
+    for r in sorted({0, m - 1, m // 2}):
+        assert bits_equal(run(d["mat"], d["xt"][r:r + 1])[0], y[r])
+
+
+@pytest.fixture(scope="module")
+def experts():
+    d = synth.experts()
+    d["tw"], d["ts"], d["tb"] = dev(d["words"]), dev(d["scales"]), dev(d["biases"])
+    d["mat"] = qgemv.Matrix(d["bits"], d["group"], d["n"], d["k"], d["tw"], d["ts"], d["tb"],
+                            n_experts=d["n_experts"])
+    return d
+
+
+@pytest.mark.parametrize("epi", [0, 1])
+def test_indexed_experts_config(experts, epi):
+    d = experts
+    n, k, m, slots = d["n"], d["k"], d["idx"].shape[0], d["idx"].shape[1]
+    xt = dev(d["x"])
+    it = dev(d["idx"])
+    y = torch.empty((m, slots, n), dtype=torch.float32, device=DEV)
+    d["mat"].run_indexed(xt, it, y.view(-1), epi=epi)
+    # each (row, slot) equals the plain call on the expert's own handle
+    wpr = d["words"].shape[-1]
+    gpr = d["scales"].shape[-1]
+    views = {}
+    for i in range(m):
+        for s in range(slots):
+            e = int(d["idx"][i, s])
+            if e not in views:
+                views[e] = qgemv.Matrix(d["bits"], d["group"], n, k, d["tw"][e], d["ts"][e], d["tb"][e])
+            yp = run(views[e], xt[i:i + 1], epi=epi)
+            assert bits_equal(yp[0], y[i, s]), (i, s, e)
+    assert wpr and gpr
+    y64, a64, _ = oracle.gemv_indexed(d["words"], d["scales"], d["biases"], d["x"], d["idx"],
+                                      d["bits"], d["group"], n, k, threads=THREADS)
+    tol = oracle.tol_y(a64, k)
+    got = y.cpu().numpy()
+    if epi:
+        tol = oracle.tol_relu2(y64, tol)
+        y64 = oracle.relu2(y64)
+    assert np.all(np.abs(got - y64) <= tol)
+
+
+def test_indexed_small_stack_repeats_and_duplicates():
+    """A routing table that names one expert twice in a row and gives one
+    expert more rows than one staging pass holds."""
+    bits, group, n, k, e = 3, 64, 300, 1024, 6
+    d = synth.matrix(4242, bits, group, n, k, 9, n_experts=e)
+    idx = np.array([[1, 1, 2], [1, 0, 5], [1, 3, 3], [1, 2, 0], [1, 4, 4],
+                    [1, 5, 1], [0, 0, 0], [2, 1, 4], [3, 3, 1]], dtype=np.int32)
+    tw, ts, tb = dev(d["words"]), dev(d["scales"]), dev(d["biases"])
+    mat = qgemv.Matrix(bits, group, n, k, tw, ts, tb, n_experts=e)
+    xt = dev(d["x"])
+    y = torch.empty((9, 3, n), dtype=torch.float32, device=DEV)
+    mat.run_indexed(xt, dev(idx), y.view(-1))
+    for i in range(9):
+        for s in range(3):
+            ex = int(idx[i, s])
+            v = qgemv.Matrix(bits, group, n, k, tw[ex], ts[ex], tb[ex])
+            assert bits_equal(run(v, xt[i:i + 1])[0], y[i, s]), (i, s)
