@@ -1,5 +1,7 @@
 """Build the HIP library ``libqgemv.so`` for gfx950, in-tree.
 
+The kernels are instantiated per code width in csrc/qgemv_b<bits>.hip and
+compiled in parallel with the host code (csrc/qgemv.hip), then linked.
 Flags: -ffp-contract=off (every fused operation in the kernels is an explicit
 builtin, so no instantiation contracts differently from another), and the
 packed-fp32 feature switched off for device code.
@@ -10,28 +12,45 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCE = os.path.join(HERE, "csrc", "qgemv.hip")
+CSRC = os.path.join(HERE, "csrc")
+SOURCES = ["qgemv.hip"] + [f"qgemv_b{b}.hip" for b in (2, 3, 4, 5, 6, 8)]
 LIB = os.path.join(HERE, "libqgemv.so")
+BUILD_DIR = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-I", os.path.join(ROOT, "include"),
+    "-Wall", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 
 
-def build(out: str = LIB, extra=()) -> str:
-    """Compile csrc/qgemv.hip into ``out`` (always recompiles)."""
-    tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, *extra, SOURCE, "-o", tmp]
+def _run(cmd):
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed building libqgemv.so")
+        sys.stderr.write(" ".join(cmd) + "\n" + r.stdout + r.stderr)
+        raise RuntimeError(f"hipcc failed: {cmd[-3]}")
+    return r
+
+
+def build(out: str = LIB, extra=(), jobs: int | None = None) -> str:
+    """Compile every translation unit and link ``out`` (always recompiles)."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    jobs = jobs or max(1, min(len(SOURCES), os.cpu_count() or 1))
+    objs = []
+    cmds = []
+    for src in SOURCES:
+        obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
+        objs.append(obj)
+        cmds.append([HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
+    with ThreadPoolExecutor(jobs) as ex:
+        list(ex.map(_run, cmds))
+    tmp = out + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, out)
     return out
 

@@ -1,0 +1,926 @@
+// qgemv_kernels.h — device code of the row product (templates), shared by
+// the per-width translation units and the host code.
+#pragma once
+// Row product kernels for gfx950 (MI355X).
+//
+// y[i,n] = epi( sum_g ( s[n,g] * A[i,n,g] + b[n,g] * X[i,g] ) )
+//   A[i,n,g] = sum over the 32-code units of group g of (fp32 chain of
+//              exact bf16 code x bf16 activation products),
+//   X[i,g]   = sum of the activations over the same units.
+// The affine form and the fp32 group sums follow "Qwen3.8-Flash-Next faster
+// kernels in Zig engine - #788" (commit "...row kernel at every MLX width":
+// an fp64 product from the MLX reference dequantization is the check;
+// commit "2-bit prompt product": codes enter exactly, with no offset) and
+// "Qwen3.8-Flash-Next support for oQ in Zig engine - #774" ("Exactness",
+// "Precision": activations stay bf16, group sums fp32).
+//
+// Design for CDNA4 (what differs from the pages' Metal lane kernels):
+//  * One output column (a weight row) is shared by LPR lanes of a 64-wide
+//    wave; each lane owns whole 128-bit-aligned chunks of the row's
+//    bitstream (16/48/16/80/48/32 bytes for 2/3/4/5/6/8 bits), so every
+//    code fetch is a global_load_dwordx4 and no code straddles two lanes.
+//  * Codes are cut once (v_bfe/v_alignbit or byte converts, specialised per
+//    width at compile time), converted to exact bf16 pairs and multiplied by
+//    bf16 activation pairs with v_dot2c_f32_bf16 (fp32 accumulate): one
+//    instruction per two products, and activations never leave bf16.
+//  * The activation window is staged once per block in LDS, laid out so the
+//    lanes' 16-byte reads are conflict-free; per-unit activation sums are
+//    computed there once.
+//  * Lanes reduce with a fixed xor butterfly; no float atomics anywhere.
+//
+// Row invariance (a row's bits are the same alone, in any window, and in
+// plain, strided and indexed calls — commit "...row kernel at every MLX
+// width"): the lane->K mapping, the unit order, the dot2 chain, the group
+// epilogue and the butterfly depend on (bits, group, N, K) only.  The
+// window size changes how many rows run side by side, never the operations
+// any one row sees.  Built with -ffp-contract=off; every fused op is an
+// explicit builtin.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <atomic>
+#include <memory>
+#include <mutex>
+#include <new>
+
+#include "qgemv.h"
+
+namespace qg {
+
+constexpr int kWave = 64;
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kMaxSlots = 64;
+constexpr int kMaxList = QGEMV_MAX_WINDOW * kMaxSlots;
+// 160 KiB of LDS per CU on gfx950, less the kernels' static arrays.
+constexpr size_t kMaxDynamicLds = 160 * 1024 - 8 * 1024;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Output columns each lane carries side by side (more loads in flight,
+// activations read from LDS once for all of them).
+template <int B, int MB> struct RowsPerLane {
+  static constexpr int v = (MB == 1) ? ((B == 2 || B == 4 || B == 8) ? 4 : 2) : (MB >= 8 ? 1 : 2);
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Two fp32 integers (< 2^8, so their low 16 bits are zero) -> bf16 pair
+// {lo = f0, hi = f1}, exactly.
+__device__ __forceinline__ uint32_t pack_bf16x2(float f0, float f1) {
+  return __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+}
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Code J of a 32-code unit held in B words (bit J*B of the unit's stream).
+template <int B, int J>
+__device__ __forceinline__ uint32_t unit_code(const uint32_t* w) {
+  constexpr int o = J * B, wi = o / 32, sh = o % 32;
+  if constexpr (sh + B <= 32) {
+    return __builtin_amdgcn_ubfe(w[wi], sh, B);
+  } else {
+    return __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & ((1u << B) - 1u);
+  }
+}
+
+template <int B, int P>
+__device__ __forceinline__ void unpack_pairs_generic(const uint32_t* w, uint32_t* q) {
+  if constexpr (P < 16) {
+    q[P] = pack_bf16x2(static_cast<float>(unit_code<B, 2 * P>(w)),
+                       static_cast<float>(unit_code<B, 2 * P + 1>(w)));
+    unpack_pairs_generic<B, P + 1>(w, q);
+  }
+}
+
+// One 32-code unit (B words) -> 16 bf16 pairs q[p] = {code 2p, code 2p+1}.
+template <int B>
+__device__ __forceinline__ void unpack_unit(const uint32_t* w, uint32_t* q) {
+  if constexpr (B == 8) {
+#pragma unroll
+    for (int wi = 0; wi < 8; ++wi) {
+      const uint32_t v = w[wi];
+      q[2 * wi] = pack_bf16x2(static_cast<float>(v & 0xffu), static_cast<float>((v >> 8) & 0xffu));
+      q[2 * wi + 1] = pack_bf16x2(static_cast<float>((v >> 16) & 0xffu), static_cast<float>(v >> 24));
+    }
+  } else if constexpr (B == 4) {
+#pragma unroll
+    for (int wi = 0; wi < 4; ++wi) {
+      const uint32_t lo = w[wi] & 0x0f0f0f0fu;          // codes 0,2,4,6 of the word
+      const uint32_t hi = (w[wi] >> 4) & 0x0f0f0f0fu;   // codes 1,3,5,7
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        q[4 * wi + b] = pack_bf16x2(static_cast<float>((lo >> (8 * b)) & 0xffu),
+                                    static_cast<float>((hi >> (8 * b)) & 0xffu));
+    }
+  } else if constexpr (B == 2) {
+#pragma unroll
+    for (int wi = 0; wi < 2; ++wi) {
+      uint32_t t[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) t[s] = (w[wi] >> (2 * s)) & 0x03030303u;  // code 4b+s in byte b
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        q[8 * wi + 2 * b] = pack_bf16x2(static_cast<float>((t[0] >> (8 * b)) & 0xffu),
+                                        static_cast<float>((t[1] >> (8 * b)) & 0xffu));
+        q[8 * wi + 2 * b + 1] = pack_bf16x2(static_cast<float>((t[2] >> (8 * b)) & 0xffu),
+                                            static_cast<float>((t[3] >> (8 * b)) & 0xffu));
+      }
+    }
+  } else {
+    unpack_pairs_generic<B, 0>(w, q);
+  }
+}
+
+// WPC words of one lane chunk, as 128-bit loads when the chunk is a whole
+// number of 16-byte pieces (always, for the main geometry), else dwords.
+template <int WPC>
+__device__ __forceinline__ void load_chunk(const uint32_t* __restrict__ p, uint32_t* out) {
+  if constexpr (WPC % 4 == 0) {
+    const u32x4* p4 = reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < WPC / 4; ++i) {
+      const u32x4 v = __builtin_nontemporal_load(p4 + i);
+      out[4 * i] = v.x;
+      out[4 * i + 1] = v.y;
+      out[4 * i + 2] = v.z;
+      out[4 * i + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < WPC; ++i) out[i] = __builtin_nontemporal_load(p + i);
+  }
+}
+
+struct Params {
+  const uint32_t* w;        // [E][N][WPR]
+  const uint16_t* scales;   // [E][N][GPR]
+  const uint16_t* biases;
+  const uint16_t* x;        // [M][K] bf16
+  float* y;
+  const int32_t* idx;       // indexed: [M][slots]
+  int64_t n;                // output columns
+  int64_t k;
+  int64_t wpr;              // words per row
+  int64_t gpr;              // groups per row
+  int64_t ldy;              // plain/strided row stride of y
+  int32_t m;                // window rows
+  int32_t slots;            // indexed only
+  int32_t n_experts;
+  int32_t epi;
+  int32_t lpr;              // lanes per output column (power of two <= 64)
+  int32_t cpl;              // chunks per lane
+  int32_t nchunks;          // chunks per row = lpr * cpl
+  int32_t tiles;            // column tiles per expert
+  int32_t indexed;          // 0: plain/strided, 1: indexed
+  int32_t vec_groups;       // scales/biases aligned for packed loads
+  int64_t y_bytes;          // extent of y written by this call (fast kernel stores)
+};
+
+__device__ __forceinline__ float apply_epi(float v, int epi) {
+  if (epi == QGEMV_EPI_RELU2) return v > 0.0f ? v * v : (v != v ? v : 0.0f);
+  return v;
+}
+
+// Block-wide list of the (row, slot) pairs routed to `expert`, in index
+// order.  Returns the count.
+__device__ inline int build_route_list(const int32_t* __restrict__ idx, int total, int expert,
+                                int* list, int* wave_cnt) {
+  const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+  int base_count = 0;
+  for (int base = 0; base < total; base += kThreads) {
+    const int t = base + tid;
+    const bool hit = t < total && idx[t] == expert;
+    const uint64_t mask = __ballot(hit);
+    if (lane == 0) wave_cnt[wv] = __popcll(mask);
+    __syncthreads();
+    int before = base_count;
+    for (int i = 0; i < wv; ++i) before += wave_cnt[i];
+    if (hit) {
+      const uint64_t lower = lane ? (mask & (~0ull >> (64 - lane))) : 0ull;
+      list[before + __popcll(lower)] = t;
+    }
+    int all = 0;
+    for (int i = 0; i < kWaves; ++i) all += wave_cnt[i];
+    __syncthreads();
+    base_count += all;
+  }
+  return base_count;
+}
+
+// Sum of v over the lpr lanes of its column group (a power of two <= 64).
+// The tree is fixed: within a 16-lane DPP row, rotate by 8, rotate by 4,
+// swap pairs of 2, swap neighbours; then across rows, xor 16 and xor 32.
+// Every lane of the group ends with the same bits.
+__device__ __forceinline__ float dpp_add(float v, int ctrl_sel) {
+  int o = 0;
+  switch (ctrl_sel) {
+    case 0: o = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false); break;  // row_ror:8
+    case 1: o = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xf, 0xf, false); break;  // row_ror:4
+    case 2: o = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4e, 0xf, 0xf, false); break;   // quad [2,3,0,1]
+    default: o = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xb1, 0xf, 0xf, false); break;  // quad [1,0,3,2]
+  }
+  return v + __int_as_float(o);
+}
+
+__device__ __forceinline__ float group_sum(float v, int lpr) {
+  if (lpr >= 16) {
+    v = dpp_add(v, 0);
+    v = dpp_add(v, 1);
+    v = dpp_add(v, 2);
+    v = dpp_add(v, 3);
+    if (lpr >= 32) v += __shfl_xor(v, 16);
+    if (lpr >= 64) v += __shfl_xor(v, 32);
+  } else {
+    if (lpr >= 8) v += __shfl_xor(v, 4);
+    if (lpr >= 4) v = dpp_add(v, 2);
+    if (lpr >= 2) v = dpp_add(v, 3);
+  }
+  return v;
+}
+
+// Scales (or biases) of one lane chunk: GPC consecutive bf16 values, read as
+// one 2-, 4- or 8-byte load when the arrays are aligned for it.
+template <int GPC>
+__device__ __forceinline__ void load_groups(const uint16_t* __restrict__ p, bool vec, uint32_t* out) {
+  if constexpr (GPC == 1) {
+    out[0] = __builtin_nontemporal_load(p);
+  } else if constexpr (GPC == 2) {
+    if (vec) {
+      out[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+    } else {
+      out[0] = static_cast<uint32_t>(p[0]) | (static_cast<uint32_t>(p[1]) << 16);
+    }
+  } else {
+    static_assert(GPC == 4, "groups per chunk");
+    if (vec) {
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+      out[0] = v.x;
+      out[1] = v.y;
+    } else {
+      out[0] = static_cast<uint32_t>(p[0]) | (static_cast<uint32_t>(p[1]) << 16);
+      out[1] = static_cast<uint32_t>(p[2]) | (static_cast<uint32_t>(p[3]) << 16);
+    }
+  }
+}
+
+// bf16 value number i of a packed group array (two per 32-bit word).
+template <int GPC>
+__device__ __forceinline__ float group_value(const uint32_t* g, int i) {
+  if constexpr (GPC == 1) {
+    return __uint_as_float(g[0] << 16);
+  } else {
+    const uint32_t w = g[i >> 1];
+    return (i & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+  }
+}
+
+template <int B, int G, int UPC, int MB>
+__global__ __launch_bounds__(kThreads) void qrow_generic(const Params p) {
+  constexpr int WPC = B * UPC;                       // words per lane chunk
+  constexpr int UPG = G / 32;                        // units per group
+  constexpr int GPC = UPC >= UPG ? UPC / UPG : 1;    // groups per lane chunk
+  constexpr int SW = GPC >= 2 ? GPC / 2 : 1;         // packed scale words per chunk
+  constexpr int R = RowsPerLane<B, MB>::v;
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int s_list[kMaxList];
+  __shared__ int s_wave_cnt[kWaves];
+  __shared__ int s_xrow[MB];
+  __shared__ int64_t s_yoff[MB];
+
+  const int nchunks = p.nchunks;
+  const int units = nchunks * UPC;
+  // LDS: x pieces [MB][UPC][4][nchunks] of 16 bytes, then unit sums [MB][UPC][nchunks]
+  u32x4* xs = reinterpret_cast<u32x4*>(smem);
+  float* xsum = reinterpret_cast<float*>(smem + static_cast<size_t>(MB) * units * 64);
+
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wv = tid / kWave;
+  const int lpr = p.lpr;
+  const int slot = lane / lpr;
+  const int li = lane % lpr;
+  const int slots_per_wave = kWave / lpr;
+  const int tile_rows = kWaves * slots_per_wave * R;
+  const int cpl = p.cpl;
+  const bool vec = p.vec_groups != 0;
+
+  int expert = 0;
+  int total = p.m;
+  if (p.indexed) {
+    expert = blockIdx.y;
+    total = build_route_list(p.idx, p.m * p.slots, expert, s_list, s_wave_cnt);
+    if (total == 0) return;
+  }
+  const uint32_t* __restrict__ wbase = p.w + static_cast<int64_t>(expert) * p.n * p.wpr;
+  const uint16_t* __restrict__ sbase = p.scales + static_cast<int64_t>(expert) * p.n * p.gpr;
+  const uint16_t* __restrict__ bbase = p.biases + static_cast<int64_t>(expert) * p.n * p.gpr;
+  const int n = static_cast<int>(p.n);
+  const int wpr = static_cast<int>(p.wpr);
+  const int gpr = static_cast<int>(p.gpr);
+  // this lane's first row in a tile, before the r offset
+  const int lane_row = wv * slots_per_wave * R + slot;
+  const int my_tiles = blockIdx.x < p.tiles ? (p.tiles - 1 - blockIdx.x) / gridDim.x + 1 : 0;
+  const int steps = my_tiles * cpl;
+
+  for (int c0 = 0; c0 < total; c0 += MB) {
+    const int mcount = min(MB, total - c0);
+    // ---- stage the window: x pieces and per-unit activation sums ----
+    if (tid < mcount) {
+      const int e = c0 + tid;
+      if (p.indexed) {
+        const int t = s_list[e];
+        const int row = t / p.slots, sl = t % p.slots;
+        s_xrow[tid] = row;
+        s_yoff[tid] = (static_cast<int64_t>(row) * p.slots + sl) * p.n;
+      } else {
+        s_xrow[tid] = e;
+        s_yoff[tid] = static_cast<int64_t>(e) * p.ldy;
+      }
+    }
+    __syncthreads();
+    for (int t = tid; t < mcount * units; t += kThreads) {
+      const int mi = t / units, u = t % units;
+      const int c = u / UPC, ui = u % UPC;
+      const u32x4* src = reinterpret_cast<const u32x4*>(p.x + static_cast<int64_t>(s_xrow[mi]) * p.k +
+                                                        static_cast<int64_t>(u) * 32);
+      u32x4 v[4];
+#pragma unroll
+      for (int pc = 0; pc < 4; ++pc) v[pc] = src[pc];
+      float X = 0.0f;
+      const uint32_t ones = 0x3f803f80u;  // bf16 pair {1, 1}
+#pragma unroll
+      for (int pc = 0; pc < 4; ++pc) {
+        X = dot2(v[pc].x, ones, X);
+        X = dot2(v[pc].y, ones, X);
+        X = dot2(v[pc].z, ones, X);
+        X = dot2(v[pc].w, ones, X);
+        xs[((mi * UPC + ui) * 4 + pc) * nchunks + c] = v[pc];
+      }
+      xsum[(mi * UPC + ui) * nchunks + c] = X;
+    }
+    __syncthreads();
+
+    // ---- steps: (tile, chunk) pairs of this block, loads one step ahead ----
+    struct Stage {
+      uint32_t w[R][WPC];
+      uint32_t s[R][SW];
+      uint32_t b[R][SW];
+    };
+    auto load_stage = [&](Stage& st, int step) {
+      const int i = step / cpl, j = step - (step / cpl) * cpl;
+      const int tile = blockIdx.x + i * gridDim.x;
+      const int c = li + lpr * j;
+      const int g0 = (c * UPC) / UPG;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int row = min(tile * tile_rows + lane_row + r * slots_per_wave, n - 1);
+        load_chunk<WPC>(wbase + static_cast<int64_t>(row) * wpr + c * WPC, st.w[r]);
+        const int64_t go = static_cast<int64_t>(row) * gpr + g0;
+        load_groups<GPC>(sbase + go, vec, st.s[r]);
+        load_groups<GPC>(bbase + go, vec, st.b[r]);
+      }
+    };
+
+    float acc[R][MB];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int mi = 0; mi < MB; ++mi) acc[r][mi] = 0.0f;
+
+    auto compute_stage = [&](const Stage& st, int step) {
+      const int i = step / cpl, j = step - (step / cpl) * cpl;
+      const int c = li + lpr * j;
+#pragma unroll
+      for (int ui = 0; ui < UPC; ++ui) {
+        uint32_t q[R][16];
+#pragma unroll
+        for (int r = 0; r < R; ++r) unpack_unit<B>(&st.w[r][ui * B], q[r]);
+        const int gi = (UPC >= UPG) ? ui / UPG : 0;
+#pragma unroll
+        for (int mi = 0; mi < MB; ++mi) {
+          if (mi < mcount) {
+            uint32_t xv[16];
+#pragma unroll
+            for (int pc = 0; pc < 4; ++pc) {
+              const u32x4 v = xs[((mi * UPC + ui) * 4 + pc) * nchunks + c];
+              xv[4 * pc] = v.x;
+              xv[4 * pc + 1] = v.y;
+              xv[4 * pc + 2] = v.z;
+              xv[4 * pc + 3] = v.w;
+            }
+            const float X = xsum[(mi * UPC + ui) * nchunks + c];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+              float a = 0.0f;
+#pragma unroll
+              for (int pp = 0; pp < 16; ++pp) a = dot2(q[r][pp], xv[pp], a);
+              acc[r][mi] = __builtin_fmaf(group_value<GPC>(st.s[r], gi), a, acc[r][mi]);
+              acc[r][mi] = __builtin_fmaf(group_value<GPC>(st.b[r], gi), X, acc[r][mi]);
+            }
+          }
+        }
+      }
+      if (j == cpl - 1) {
+        // ---- the tile's columns are complete: reduce over lanes, store ----
+        const int tile = blockIdx.x + i * gridDim.x;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int row = tile * tile_rows + lane_row + r * slots_per_wave;
+#pragma unroll
+          for (int mi = 0; mi < MB; ++mi) {
+            const float v = group_sum(acc[r][mi], lpr);
+            acc[r][mi] = 0.0f;
+            if (li == 0 && mi < mcount && row < n) p.y[s_yoff[mi] + row] = apply_epi(v, p.epi);
+          }
+        }
+      }
+    };
+
+    // The prefetch is unconditional (its step index is clamped; the last
+    // one re-reads the current step, a cache hit) so the loop body is
+    // straight-line and each compute waits only for its own stage's loads.
+    Stage sa, sb;
+    if (steps > 0) {
+      load_stage(sa, 0);
+      int step = 0;
+      for (; step + 1 < steps; step += 2) {
+        load_stage(sb, step + 1);
+        compute_stage(sa, step);
+        load_stage(sa, min(step + 2, steps - 1));
+        compute_stage(sb, step + 1);
+      }
+      if (step < steps) compute_stage(sa, step);
+    }
+    __syncthreads();  // LDS window reused by the next chunk of routed rows
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Fast kernel: whole 128-bit pieces, perfectly coalesced.
+//
+// A lane chunk is PPC 16-byte pieces of one row's bitstream holding CPC
+// codes: one piece (64/32/16 codes) for 2/4/8 bits, three pieces (128/64
+// codes) for 3/6 bits, five pieces (128 codes) for 5 bits.  For 2/4/8 bits
+// the lanes of a column group read consecutive pieces of the row, so every
+// load instruction is fully coalesced.  For 3/5/6 bits a chunk spans
+// several pieces; the wave reads its step's rows as consecutive pieces
+// (lane l takes piece l, l+64, ...) and hands each lane its chunk through
+// a wave-private LDS buffer (STAGE), or, when LDS is short, each lane
+// loads its own chunk (!STAGE).  Both modes feed the same registers to the
+// same arithmetic, so a row's bits do not depend on the mode.
+// ---------------------------------------------------------------------------
+
+template <int B> struct Geo;
+template <> struct Geo<2> { static constexpr int PPC = 1, CPC = 64; };
+template <> struct Geo<3> { static constexpr int PPC = 3, CPC = 128; };
+template <> struct Geo<4> { static constexpr int PPC = 1, CPC = 32; };
+template <> struct Geo<5> { static constexpr int PPC = 5, CPC = 128; };
+template <> struct Geo<6> { static constexpr int PPC = 3, CPC = 64; };
+template <> struct Geo<8> { static constexpr int PPC = 1, CPC = 16; };
+
+#ifndef QG_ODD_ROWS_M1
+#define QG_ODD_ROWS_M1 2
+#endif
+template <int B, int MB> struct FastRows {
+  static constexpr int v = (MB == 1) ? ((B == 2 || B == 4 || B == 8) ? 4 : QG_ODD_ROWS_M1) : (MB <= 4 ? 2 : 1);
+};
+
+// NC codes (NC * B a multiple of 32) from NC*B/32 words -> NC/2 bf16 pairs.
+template <int B, int NC>
+__device__ __forceinline__ void unpack_codes(const uint32_t* w, uint32_t* q) {
+  static_assert((NC * B) % 32 == 0 && NC % 16 == 0, "whole words");
+  if constexpr (B == 8 || B == 4 || B == 2) {
+    constexpr int PER = 32 / B;  // codes per word
+#pragma unroll
+    for (int wi = 0; wi < NC * B / 32; ++wi) {
+      if constexpr (B == 8) {
+        const uint32_t v = w[wi];
+        q[2 * wi] = pack_bf16x2(static_cast<float>(v & 0xffu), static_cast<float>((v >> 8) & 0xffu));
+        q[2 * wi + 1] = pack_bf16x2(static_cast<float>((v >> 16) & 0xffu), static_cast<float>(v >> 24));
+      } else if constexpr (B == 4) {
+        const uint32_t lo = w[wi] & 0x0f0f0f0fu;
+        const uint32_t hi = (w[wi] >> 4) & 0x0f0f0f0fu;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          q[4 * wi + b] = pack_bf16x2(static_cast<float>((lo >> (8 * b)) & 0xffu),
+                                      static_cast<float>((hi >> (8 * b)) & 0xffu));
+      } else {
+        uint32_t t[4];
+#pragma unroll
+        for (int sft = 0; sft < 4; ++sft) t[sft] = (w[wi] >> (2 * sft)) & 0x03030303u;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          q[8 * wi + 2 * b] = pack_bf16x2(static_cast<float>((t[0] >> (8 * b)) & 0xffu),
+                                          static_cast<float>((t[1] >> (8 * b)) & 0xffu));
+          q[8 * wi + 2 * b + 1] = pack_bf16x2(static_cast<float>((t[2] >> (8 * b)) & 0xffu),
+                                              static_cast<float>((t[3] >> (8 * b)) & 0xffu));
+        }
+      }
+      (void)PER;
+    }
+  } else {
+    // odd widths: NC is a multiple of 32; each 32-code unit is B words
+#pragma unroll
+    for (int u = 0; u < NC / 32; ++u) unpack_pairs_generic<B, 0>(w + u * B, q + 16 * u);
+  }
+}
+
+// Branch-light butterfly for 16, 32 or 64 lanes per column: the same tree
+// as group_sum (rotate 8, rotate 4, swap 2, swap 1 inside a DPP row, then
+// xor 16, xor 32), with the cross-row steps selected by lane count.
+__device__ __forceinline__ float group_sum16(float v, int lpr) {
+  v = dpp_add(v, 0);
+  v = dpp_add(v, 1);
+  v = dpp_add(v, 2);
+  v = dpp_add(v, 3);
+  const float a = __shfl_xor(v, 16);
+  v = lpr >= 32 ? v + a : v;
+  const float b = __shfl_xor(v, 32);
+  v = lpr >= 64 ? v + b : v;
+  return v;
+}
+
+// Buffer resource over [base, base + bytes): loads past the end read 0 and
+// stores past it are dropped (bytes is clamped to the 32-bit field).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int nr = bytes > 0x7fffffff ? 0x7fffffff : static_cast<int>(bytes < 0 ? 0 : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, nr, 0x00020000);
+}
+
+constexpr int kNt = 2;  // buffer cache policy: non-temporal (weights are read once)
+
+template <int GPC>
+__device__ __forceinline__ void load_groups_buf(__amdgpu_buffer_rsrc_t r, int off, bool vec, uint32_t* out) {
+  if constexpr (GPC == 1) {
+    out[0] = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, kNt);
+  } else if constexpr (GPC == 2) {
+    if (vec) {
+      out[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kNt);
+    } else {
+      out[0] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, kNt)) |
+               (static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, off + 2, 0, kNt)) << 16);
+    }
+  } else {
+    static_assert(GPC == 4, "groups per chunk");
+    if (vec) {
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kNt);
+      out[0] = v.x;
+      out[1] = v.y;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        out[i] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, off + 4 * i, 0, kNt)) |
+                 (static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, off + 4 * i + 2, 0, kNt)) << 16);
+    }
+  }
+}
+
+template <int B, int G, int MB, bool STAGE>
+__global__ __launch_bounds__(kThreads) void qrow_fast(const Params p) {
+  constexpr int PPC = Geo<B>::PPC, CPC = Geo<B>::CPC;
+  constexpr int WPC = 4 * PPC;                      // words per chunk
+  constexpr int CB = 16 * PPC;                      // bytes per chunk
+  constexpr int EU = CPC < G ? CPC : G;             // codes per epilogue unit
+  constexpr int NEU = CPC / EU;                     // epilogue units (groups) per chunk
+  constexpr int EUW = EU * B / 32;                  // words per epilogue unit
+  constexpr int XP = EU / 8;                        // 16-byte activation pieces per unit
+  constexpr int SW = NEU >= 2 ? NEU / 2 : 1;        // packed scale words per chunk
+  constexpr int R = FastRows<B, MB>::v;
+  constexpr int GSPAN = NEU >= 2 ? NEU : 1;         // groups read per chunk
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int s_list[kMaxList];
+  __shared__ int s_wave_cnt[kWaves];
+  __shared__ int s_xrow[MB];
+  __shared__ int64_t s_yoff[MB];
+
+  const int nchunks = p.nchunks;
+  // LDS: x pieces [MB][NEU][XP][nchunks] x 16 B, unit sums [MB][NEU][nchunks],
+  // then (STAGE) one staging buffer of R*PPC*64 pieces per wave.
+  u32x4* xs = reinterpret_cast<u32x4*>(smem);
+  float* xsum = reinterpret_cast<float*>(smem + static_cast<size_t>(MB) * NEU * XP * nchunks * 16);
+  unsigned char* stage_all = smem + static_cast<size_t>(MB) * NEU * nchunks * (XP * 16 + 4);
+
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lpr = p.lpr;
+  const int slot = lane / lpr;
+  const int li = lane % lpr;
+  const int slots_per_wave = kWave / lpr;
+  const int wave_rows = slots_per_wave * R;
+  const int tile_rows = kWaves * wave_rows;
+  const int cpl = p.cpl;
+  const bool vec = p.vec_groups != 0;
+  u32x4* stage = reinterpret_cast<u32x4*>(stage_all) + wv * (R * PPC * kWave);
+  const uint32_t* stage32 = reinterpret_cast<const uint32_t*>(stage);
+
+  int expert = 0;
+  int total = p.m;
+  if (p.indexed) {
+    expert = blockIdx.y;
+    total = build_route_list(p.idx, p.m * p.slots, expert, s_list, s_wave_cnt);
+    if (total == 0) return;
+  }
+  const int n = static_cast<int>(p.n);
+  const int64_t row_bytes = p.wpr * 4;
+  const int gpr2 = static_cast<int>(p.gpr) * 2;     // scale bytes per row
+  const unsigned char* wexp = reinterpret_cast<const unsigned char*>(p.w) + static_cast<int64_t>(expert) * p.n * row_bytes;
+  const unsigned char* sexp = reinterpret_cast<const unsigned char*>(p.scales) + static_cast<int64_t>(expert) * p.n * gpr2;
+  const unsigned char* bexp = reinterpret_cast<const unsigned char*>(p.biases) + static_cast<int64_t>(expert) * p.n * gpr2;
+  const int my_tiles = blockIdx.x < p.tiles ? (p.tiles - 1 - blockIdx.x) / gridDim.x + 1 : 0;
+  const int steps = my_tiles * cpl;
+  // y as one buffer resource: lanes with nothing to store aim past its end
+  const __amdgpu_buffer_rsrc_t yres = make_rsrc(p.y, p.y_bytes);
+
+  for (int c0 = 0; c0 < total; c0 += MB) {
+    const int mcount = min(MB, total - c0);
+    if (tid < mcount) {
+      const int e = c0 + tid;
+      if (p.indexed) {
+        const int t = s_list[e];
+        const int row = t / p.slots, sl = t % p.slots;
+        s_xrow[tid] = row;
+        s_yoff[tid] = (static_cast<int64_t>(row) * p.slots + sl) * p.n;
+      } else {
+        s_xrow[tid] = e;
+        s_yoff[tid] = static_cast<int64_t>(e) * p.ldy;
+      }
+    }
+    __syncthreads();
+    // ---- stage the window: activation pieces and per-unit sums ----
+    for (int t = tid; t < mcount * nchunks * NEU; t += kThreads) {
+      const int mi = t / (nchunks * NEU);
+      const int rest = t % (nchunks * NEU);
+      const int c = rest / NEU, e = rest % NEU;
+      const u32x4* src = reinterpret_cast<const u32x4*>(
+          p.x + static_cast<int64_t>(s_xrow[mi]) * p.k + static_cast<int64_t>(c) * CPC + e * EU);
+      float X = 0.0f;
+      const uint32_t ones = 0x3f803f80u;  // bf16 pair {1, 1}
+#pragma unroll
+      for (int pc = 0; pc < XP; ++pc) {
+        const u32x4 v = src[pc];
+        X = dot2(v.x, ones, X);
+        X = dot2(v.y, ones, X);
+        X = dot2(v.z, ones, X);
+        X = dot2(v.w, ones, X);
+        xs[((mi * NEU + e) * XP + pc) * nchunks + c] = v;
+      }
+      xsum[(mi * NEU + e) * nchunks + c] = X;
+    }
+    __syncthreads();
+
+    struct Stage {
+      uint32_t w[R * WPC];
+      uint32_t s[R][SW];
+      uint32_t b[R][SW];
+    };
+    // step -> (tile, chunk column j); the wave's rows are
+    // [wrow0, wrow0 + wave_rows), lane (slot, li) owns rows wrow0 + r*S + slot
+    auto load_stage = [&](Stage& st, int step) {
+      const int i = step / cpl, j = step - (step / cpl) * cpl;
+      const int tile = blockIdx.x + i * gridDim.x;
+      const int wrow0 = tile * tile_rows + wv * wave_rows;
+      const __amdgpu_buffer_rsrc_t wr = make_rsrc(wexp + wrow0 * row_bytes, (n - wrow0) * row_bytes);
+      const __amdgpu_buffer_rsrc_t sr = make_rsrc(sexp + static_cast<int64_t>(wrow0) * gpr2,
+                                                  static_cast<int64_t>(n - wrow0) * gpr2);
+      const __amdgpu_buffer_rsrc_t br = make_rsrc(bexp + static_cast<int64_t>(wrow0) * gpr2,
+                                                  static_cast<int64_t>(n - wrow0) * gpr2);
+      const int c = li + lpr * j;
+      if constexpr (STAGE) {
+        // piece P = lane + 64*t of the wave's chunk column: segment (row)
+        // P / (lpr*PPC), piece within it P % (lpr*PPC)
+        const int seg_pieces = lpr * PPC;
+#pragma unroll
+        for (int t = 0; t < R * PPC; ++t) {
+          const int P = lane + kWave * t;
+          const int sg = P / seg_pieces, within = P - sg * seg_pieces;
+          const int off = static_cast<int>(sg * row_bytes) + (lpr * j) * CB + within * 16;
+          const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, kNt);
+          st.w[4 * t] = v.x;
+          st.w[4 * t + 1] = v.y;
+          st.w[4 * t + 2] = v.z;
+          st.w[4 * t + 3] = v.w;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int sg = r * slots_per_wave + slot;
+        if constexpr (!STAGE) {
+#pragma unroll
+          for (int pp = 0; pp < PPC; ++pp) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(
+                wr, static_cast<int>(sg * row_bytes) + c * CB + pp * 16, 0, kNt);
+            st.w[r * WPC + 4 * pp] = v.x;
+            st.w[r * WPC + 4 * pp + 1] = v.y;
+            st.w[r * WPC + 4 * pp + 2] = v.z;
+            st.w[r * WPC + 4 * pp + 3] = v.w;
+          }
+        }
+        const int goff = sg * gpr2 + ((c * CPC) / G) * 2;
+        load_groups_buf<GSPAN>(sr, goff, vec, st.s[r]);
+        load_groups_buf<GSPAN>(br, goff, vec, st.b[r]);
+      }
+    };
+
+    float acc[R][MB];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int mi = 0; mi < MB; ++mi) acc[r][mi] = 0.0f;
+
+    auto compute_stage = [&](const Stage& st, int step) {
+      const int i = step / cpl, j = step - (step / cpl) * cpl;
+      const int c = li + lpr * j;
+      if constexpr (STAGE) {
+        // hand the pieces over: lane order in, chunk order out
+#pragma unroll
+        for (int t = 0; t < R * PPC; ++t) {
+          u32x4 v;
+          v.x = st.w[4 * t];
+          v.y = st.w[4 * t + 1];
+          v.z = st.w[4 * t + 2];
+          v.w = st.w[4 * t + 3];
+          stage[lane + kWave * t] = v;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < NEU; ++e) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          // cut this row's codes of the unit once, for every window row
+          uint32_t wu[EUW];
+          if constexpr (STAGE) {
+            const int sg = r * slots_per_wave + slot;
+            const int base = (sg * lpr + li) * WPC + e * EUW;
+#pragma unroll
+            for (int h = 0; h < EUW; ++h) wu[h] = stage32[base + h];
+          } else {
+#pragma unroll
+            for (int h = 0; h < EUW; ++h) wu[h] = st.w[r * WPC + e * EUW + h];
+          }
+          uint32_t q[EU / 2];
+          unpack_codes<B, EU>(wu, q);
+          const float sv = group_value<GSPAN>(st.s[r], e);
+          const float bv = group_value<GSPAN>(st.b[r], e);
+#pragma unroll
+          for (int mi = 0; mi < MB; ++mi) {
+            if (mi < mcount) {
+              uint32_t xv[EU / 2];
+#pragma unroll
+              for (int pc = 0; pc < XP; ++pc) {
+                const u32x4 v = xs[((mi * NEU + e) * XP + pc) * nchunks + c];
+                xv[4 * pc] = v.x;
+                xv[4 * pc + 1] = v.y;
+                xv[4 * pc + 2] = v.z;
+                xv[4 * pc + 3] = v.w;
+              }
+              const float X = xsum[(mi * NEU + e) * nchunks + c];
+              float a = 0.0f;
+#pragma unroll
+              for (int pp = 0; pp < EU / 2; ++pp) a = dot2(q[pp], xv[pp], a);
+              acc[r][mi] = __builtin_fmaf(sv, a, acc[r][mi]);
+              acc[r][mi] = __builtin_fmaf(bv, X, acc[r][mi]);
+            }
+          }
+        }
+      }
+      if (j == cpl - 1) {
+        const int tile = blockIdx.x + i * gridDim.x;
+        const int wrow0 = tile * tile_rows + wv * wave_rows;
+        float red[R][MB];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int mi = 0; mi < MB; ++mi) {
+            red[r][mi] = group_sum16(acc[r][mi], lpr);
+            acc[r][mi] = 0.0f;
+          }
+        // lane li of a column group stores element li (+ 16, ...) of its
+        // R x MB results; lanes with nothing to store aim past the buffer
+#pragma unroll
+        for (int e0 = 0; e0 < R * MB; e0 += 16) {
+          const int e = e0 + li;
+          float v = 0.0f;
+#pragma unroll
+          for (int k2 = e0; k2 < e0 + 16 && k2 < R * MB; ++k2) v = (e == k2) ? red[k2 / MB][k2 % MB] : v;
+          const int r = e / MB, mi = e - (e / MB) * MB;
+          const int row = wrow0 + r * slots_per_wave + slot;
+          const bool ok = e < R * MB && li < 16 && mi < mcount && row < n;
+          const int off = ok ? static_cast<int>((s_yoff[ok ? mi : 0] + row) * 4) : 0x7ffffff0;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(apply_epi(v, p.epi)), yres, off, 0, 0);
+        }
+      }
+    };
+
+    Stage sa, sb;
+    if (steps > 0) {
+      load_stage(sa, 0);
+      int step = 0;
+      for (; step + 1 < steps; step += 2) {
+        load_stage(sb, step + 1);
+        compute_stage(sa, step);
+        load_stage(sa, min(step + 2, steps - 1));
+        compute_stage(sb, step + 1);
+      }
+      if (step < steps) compute_stage(sa, step);
+    }
+    __syncthreads();  // LDS window reused by the next chunk of routed rows
+  }
+}
+
+// The product kernels' own unpack, written back as integer codes.
+template <int B>
+__global__ __launch_bounds__(kThreads) void unpack_kernel(const uint32_t* __restrict__ w, int64_t n,
+                                                          int64_t k, uint8_t* __restrict__ codes) {
+  const int64_t units = k / 32;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (t >= n * units) return;
+  const int64_t row = t / units, u = t % units;
+  uint32_t wu[B];
+  const uint32_t* src = w + row * (k * B / 32) + u * B;
+#pragma unroll
+  for (int i = 0; i < B; ++i) wu[i] = src[i];
+  uint32_t q[16];
+  unpack_unit<B>(wu, q);
+  uint8_t* dst = codes + row * k + u * 32;
+#pragma unroll
+  for (int pp = 0; pp < 16; ++pp) {
+    dst[2 * pp] = static_cast<uint8_t>(__uint_as_float(q[pp] << 16));
+    dst[2 * pp + 1] = static_cast<uint8_t>(__uint_as_float(q[pp] & 0xffff0000u));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// kernel table
+// ---------------------------------------------------------------------------
+
+typedef void (*KernelFn)(const Params);
+
+constexpr int kBits[6] = {2, 3, 4, 5, 6, 8};
+constexpr int kGroups[3] = {32, 64, 128};
+constexpr int kWindows[5] = {1, 2, 4, 8, 16};
+constexpr int kIndexedWindow = 4;  // routed rows staged per pass
+
+struct Entry {
+  KernelFn fast[5][2];  // by window variant and staging (0: direct loads, 1: LDS hand-off)
+  KernelFn generic[5];  // by window variant: one-unit chunks, any lane count
+  int fast_rows[5];     // columns per lane of the fast kernels
+  int generic_rows[5];
+};
+
+template <int B, int G>
+Entry make_entry() {
+  Entry e{};
+  e.fast[0][0] = qrow_fast<B, G, 1, false>;
+  e.fast[1][0] = qrow_fast<B, G, 2, false>;
+  e.fast[2][0] = qrow_fast<B, G, 4, false>;
+  e.fast[3][0] = qrow_fast<B, G, 8, false>;
+  e.fast[4][0] = qrow_fast<B, G, 16, false>;
+  if constexpr (Geo<B>::PPC > 1) {
+    e.fast[0][1] = qrow_fast<B, G, 1, true>;
+    e.fast[1][1] = qrow_fast<B, G, 2, true>;
+    e.fast[2][1] = qrow_fast<B, G, 4, true>;
+    e.fast[3][1] = qrow_fast<B, G, 8, true>;
+    e.fast[4][1] = qrow_fast<B, G, 16, true>;
+  }
+  e.generic[0] = qrow_generic<B, G, 1, 1>;
+  e.generic[1] = qrow_generic<B, G, 1, 2>;
+  e.generic[2] = qrow_generic<B, G, 1, 4>;
+  e.generic[3] = qrow_generic<B, G, 1, 8>;
+  e.generic[4] = qrow_generic<B, G, 1, 16>;
+  e.fast_rows[0] = FastRows<B, 1>::v;
+  e.fast_rows[1] = FastRows<B, 2>::v;
+  e.fast_rows[2] = FastRows<B, 4>::v;
+  e.fast_rows[3] = FastRows<B, 8>::v;
+  e.fast_rows[4] = FastRows<B, 16>::v;
+  e.generic_rows[0] = RowsPerLane<B, 1>::v;
+  e.generic_rows[1] = RowsPerLane<B, 2>::v;
+  e.generic_rows[2] = RowsPerLane<B, 4>::v;
+  e.generic_rows[3] = RowsPerLane<B, 8>::v;
+  e.generic_rows[4] = RowsPerLane<B, 16>::v;
+  return e;
+}
+
+// One table of kernels per code width, each built in its own translation
+// unit: index [group 32/64/128].
+const Entry* entries_b2();
+const Entry* entries_b3();
+const Entry* entries_b4();
+const Entry* entries_b5();
+const Entry* entries_b6();
+const Entry* entries_b8();
+
+}  // namespace qg

@@ -37,9 +37,11 @@ class qgemv_desc(ctypes.Structure):
                 ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p)]
 
 
-def load(path: str = LIB_PATH):
-    """The loaded library; raises if it is not built (no fallback exists)."""
+def load(path: str | None = None):
+    """The loaded library; raises if it is not built (no fallback exists).
+    QGEMV_LIB names another build of the same library (e.g. a tuning build)."""
     global _lib
+    path = path or os.environ.get("QGEMV_LIB") or LIB_PATH
     with _lock:
         if _lib is None:
             if not os.path.exists(path):
