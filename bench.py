@@ -33,12 +33,18 @@ sys.path.insert(0, ROOT)
 
 PEAK_GBS = 8000.0          # MI355X HBM3E, published
 ROTATE_BYTES = 1 << 30     # at least 1 GiB of distinct weight copies
-KERNEL_SOURCE = os.path.join(ROOT, "bit_affine_quantized_amd", "csrc", "qgemv.hip")
+KERNEL_DIR = os.path.join(ROOT, "bit_affine_quantized_amd", "csrc")
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
 def kernel_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+    """Hash of every kernel and host source of the library."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(KERNEL_DIR)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            h.update(open(os.path.join(KERNEL_DIR, name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def algorithmic_bytes(runs, m, k, n_out, idx_bytes=0):
@@ -51,17 +57,23 @@ def algorithmic_bytes(runs, m, k, n_out, idx_bytes=0):
 
 def read_traffic(workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary of
-    this workload, if it was taken on the current kernel source."""
-    path = os.path.join(PROFILE_DIR, f"counters_{workload}.json")
+    this workload (profiles/counters_<workload>.txt), if it was taken on the
+    current kernel sources; else None."""
+    path = os.path.join(PROFILE_DIR, f"counters_{workload}.txt")
     if not os.path.exists(path):
         return None
-    try:
-        rec = json.load(open(path))
-    except Exception:
-        return None
+    rec = {}
+    for line in open(path):
+        line = line.strip()
+        if line and not line.startswith("#") and ":" in line:
+            key, val = line.split(":", 1)
+            rec[key.strip()] = val.strip()
     if rec.get("kernel_sha") != kernel_hash():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    try:
+        return int(rec["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 class Workload:
@@ -159,29 +171,27 @@ class Workload:
 
 
 def time_workload(wl: Workload, steps: int, warmup: int, torch):
+    """W untimed warmup steps, then exactly K steps issued back to back on
+    one stream, bracketed by a synchronize on both sides.  Events recorded
+    on that stream split the K steps into five batches with no host wait in
+    between, so the GPU never idles inside the timed region.  Returns the
+    mean time per step over all K steps and the per-batch means."""
     stream = torch.cuda.current_stream()
     sid = stream.cuda_stream
     for i in range(warmup):
         wl.step(i, sid)
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    batches = []
-    per = max(1, steps // 5)
-    done = 0
-    # five batches; the median batch gives the per-call time
-    while done < steps:
-        cnt = min(per, steps - done)
-        torch.cuda.synchronize()
-        start.record(stream)
-        for i in range(cnt):
-            wl.step(done + i, sid)
-        end.record(stream)
-        end.synchronize()
-        batches.append(start.elapsed_time(end) / cnt)
-        done += cnt
+    nb = min(5, steps)
+    bounds = [round(steps * b / nb) for b in range(nb + 1)]
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)]
+    events[0].record(stream)
+    for b in range(nb):
+        for i in range(bounds[b], bounds[b + 1]):
+            wl.step(warmup + i, sid)
+        events[b + 1].record(stream)
     torch.cuda.synchronize()
-    ms = float(np.median(batches))
+    batches = [events[b].elapsed_time(events[b + 1]) / (bounds[b + 1] - bounds[b]) for b in range(nb)]
+    ms = events[0].elapsed_time(events[nb]) / steps
     return ms, batches
 
 
@@ -202,31 +212,34 @@ def cpu_baseline(budget_s: float = 12.0):
         x = synth.draw_x(rng, 1, k)
         return words, scales, biases, x
 
-    n0 = 256 * threads
-    w, s, b, x = sample(n0)
-    t0 = time.perf_counter()
-    oracle.gemv(w, s, b, x, bits, group, n0, k, threads=threads)
-    dt = time.perf_counter() - t0
-    n1 = int(max(n0, min(synth.LMHEAD_N, n0 * budget_s / max(dt, 1e-6))))
-    w, s, b, x = sample(n1)
-    t0 = time.perf_counter()
-    oracle.gemv(w, s, b, x, bits, group, n1, k, threads=threads)
-    dt = time.perf_counter() - t0
-    nbytes = algorithmic_bytes([(bits, group, n1)], 1, k, n1)
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n1} of the LM head's 248320 columns (K=2048, 6-bit group 32), 1-row window, "
-                      f"fp64 oracle, {dt:.1f} s"}
+    # one block of LM-head-shaped columns, passed over repeatedly until the
+    # budget of oracle work is spent
+    nblk = 32768
+    w, s, b, x = sample(nblk)
+    passes, t_total = 0, 0.0
+    while t_total < budget_s and passes < 10000:
+        t0 = time.perf_counter()
+        oracle.gemv(w, s, b, x, bits, group, nblk, k, threads=threads)
+        t_total += time.perf_counter() - t0
+        passes += 1
+    nbytes = algorithmic_bytes([(bits, group, nblk)], 1, k, nblk) * passes
+    return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{passes} passes over {nblk} LM-head-shaped columns (K=2048, 6-bit group 32), "
+                      f"1-row window, fp64 oracle, {t_total:.1f} s"}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=300,
+                    help="untimed steps; the GPU clock needs ~20 ms of load to settle")
     ap.add_argument("--workload", default="lmhead", choices=["lmhead", "stack", "experts"])
     ap.add_argument("--m", type=int, default=1, help="window rows")
     ap.add_argument("--all", action="store_true", help="also time the other workloads and windows")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device-to-device copy (known bytes) for counter scaling")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -236,6 +249,17 @@ def main():
 
     import torch
     from bit_affine_quantized_amd import qgemv, synth
+
+    if args.copy_calibration:
+        # a copy kernel of known size: 1 GiB read and 1 GiB written per launch
+        src = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": src.numel() * 4,
+                          "copy_calibration_bytes_written": dst.numel() * 4, "launches": 5}))
+        return
 
     qgemv.load()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -271,7 +295,7 @@ def main():
             if name == args.workload and m == wl.m:
                 continue
             w2 = Workload(name, m, torch, qgemv, synth)
-            ms2, _ = time_workload(w2, max(20, args.steps // 2), args.warmup, torch)
+            ms2, _ = time_workload(w2, max(50, args.steps // 2), args.warmup, torch)
             g2 = w2.bytes / (ms2 * 1e-3) / 1e9
             extra[f"{name}_m{w2.m}"] = {"us_per_call": round(ms2 * 1e3, 3), "GB/s": round(g2, 1),
                                         "frac": round(g2 / PEAK_GBS, 4), "bytes": w2.bytes}

@@ -92,52 +92,93 @@ __device__ __forceinline__ uint32_t unit_code(const uint32_t* w) {
   }
 }
 
+// Byte pair {c0, c1} (codes 0..15) -> exact bf16 pair, two codes per
+// instruction: a byte holding c < 16 reads as an fp8 e4m3 value c * 2^-9
+// (exponent field 0 or 1, both on the same linear scale), and the scaled
+// conversion multiplies by 2^9 exactly.  hi selects bytes 2,3 instead of 0,1.
+template <bool HI>
+__device__ __forceinline__ uint32_t bytes_to_bf16x2(uint32_t bytes) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(bytes, 512.0f, HI));
+}
+
 template <int B, int P>
-__device__ __forceinline__ void unpack_pairs_generic(const uint32_t* w, uint32_t* q) {
+__device__ __forceinline__ void unpack_pairs_odd(const uint32_t* w, uint32_t* q) {
   if constexpr (P < 16) {
-    q[P] = pack_bf16x2(static_cast<float>(unit_code<B, 2 * P>(w)),
-                       static_cast<float>(unit_code<B, 2 * P + 1>(w)));
-    unpack_pairs_generic<B, P + 1>(w, q);
+    if constexpr (B == 3) {
+      // two 3-bit codes -> bytes {c0, c1} -> one conversion
+      q[P] = bytes_to_bf16x2<false>(unit_code<B, 2 * P>(w) | (unit_code<B, 2 * P + 1>(w) << 8));
+    } else {
+      q[P] = pack_bf16x2(static_cast<float>(unit_code<B, 2 * P>(w)),
+                         static_cast<float>(unit_code<B, 2 * P + 1>(w)));
+    }
+    unpack_pairs_odd<B, P + 1>(w, q);
   }
 }
 
-// One 32-code unit (B words) -> 16 bf16 pairs q[p] = {code 2p, code 2p+1}.
+// NC codes (NC*B a multiple of 32) held in NC*B/32 words -> NC/2 exact bf16
+// pairs q[p] = {code slot_code<B>(2p), code slot_code<B>(2p+1)}.  2- and
+// 4-bit codes are split into bytes with masks and converted two per
+// instruction, which pairs them in the order slot_code gives; the
+// activations are staged in the same order, so each pair still meets its
+// own two activations.
 template <int B>
-__device__ __forceinline__ void unpack_unit(const uint32_t* w, uint32_t* q) {
+__host__ __device__ constexpr int slot_code(int slot) {
+  if constexpr (B == 2) {
+    // per 16-code word: t_s = (w >> 2s) & 0x03030303 holds codes s, 4+s, 8+s, 12+s
+    const int wi = slot / 16, r = slot % 16, sft = r / 4, half = (r / 2) % 2, el = r % 2;
+    return 16 * wi + sft + 4 * el + 8 * half;
+  } else if constexpr (B == 4) {
+    // per 8-code word: low nibbles hold codes 0,2,4,6; high nibbles 1,3,5,7
+    const int wi = slot / 8, r = slot % 8, b = r / 2, el = r % 2;
+    return 8 * wi + b / 2 + 4 * (b % 2) + 2 * el;
+  } else {
+    return slot;
+  }
+}
+
+template <int B, int NC>
+__device__ __forceinline__ void unpack_codes(const uint32_t* w, uint32_t* q) {
+  static_assert((NC * B) % 32 == 0 && NC % 16 == 0, "whole words");
   if constexpr (B == 8) {
 #pragma unroll
-    for (int wi = 0; wi < 8; ++wi) {
+    for (int wi = 0; wi < NC / 4; ++wi) {
       const uint32_t v = w[wi];
       q[2 * wi] = pack_bf16x2(static_cast<float>(v & 0xffu), static_cast<float>((v >> 8) & 0xffu));
       q[2 * wi + 1] = pack_bf16x2(static_cast<float>((v >> 16) & 0xffu), static_cast<float>(v >> 24));
     }
   } else if constexpr (B == 4) {
 #pragma unroll
-    for (int wi = 0; wi < 4; ++wi) {
-      const uint32_t lo = w[wi] & 0x0f0f0f0fu;          // codes 0,2,4,6 of the word
-      const uint32_t hi = (w[wi] >> 4) & 0x0f0f0f0fu;   // codes 1,3,5,7
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-        q[4 * wi + b] = pack_bf16x2(static_cast<float>((lo >> (8 * b)) & 0xffu),
-                                    static_cast<float>((hi >> (8 * b)) & 0xffu));
+    for (int wi = 0; wi < NC / 8; ++wi) {
+      const uint32_t lo = w[wi] & 0x0f0f0f0fu;
+      const uint32_t hi = (w[wi] >> 4) & 0x0f0f0f0fu;
+      q[4 * wi] = bytes_to_bf16x2<false>(lo);
+      q[4 * wi + 1] = bytes_to_bf16x2<true>(lo);
+      q[4 * wi + 2] = bytes_to_bf16x2<false>(hi);
+      q[4 * wi + 3] = bytes_to_bf16x2<true>(hi);
     }
   } else if constexpr (B == 2) {
 #pragma unroll
-    for (int wi = 0; wi < 2; ++wi) {
-      uint32_t t[4];
+    for (int wi = 0; wi < NC / 16; ++wi) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) t[s] = (w[wi] >> (2 * s)) & 0x03030303u;  // code 4b+s in byte b
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        q[8 * wi + 2 * b] = pack_bf16x2(static_cast<float>((t[0] >> (8 * b)) & 0xffu),
-                                        static_cast<float>((t[1] >> (8 * b)) & 0xffu));
-        q[8 * wi + 2 * b + 1] = pack_bf16x2(static_cast<float>((t[2] >> (8 * b)) & 0xffu),
-                                            static_cast<float>((t[3] >> (8 * b)) & 0xffu));
+      for (int sft = 0; sft < 4; ++sft) {
+        const uint32_t t = (w[wi] >> (2 * sft)) & 0x03030303u;
+        q[8 * wi + 2 * sft] = bytes_to_bf16x2<false>(t);
+        q[8 * wi + 2 * sft + 1] = bytes_to_bf16x2<true>(t);
       }
     }
   } else {
-    unpack_pairs_generic<B, 0>(w, q);
+#pragma unroll
+    for (int u = 0; u < NC / 32; ++u) unpack_pairs_odd<B, 0>(w + u * B, q + 16 * u);
   }
+}
+
+// Activation pair p of an NC-code unit in the order unpack_codes pairs the
+// codes: x holds the unit's activations as natural bf16 pairs.
+template <int B>
+__device__ __forceinline__ uint32_t slot_pair(const uint32_t* x, int p) {
+  const int a = slot_code<B>(2 * p), b = slot_code<B>(2 * p + 1);
+  const uint32_t sel = ((a & 1) ? 0x0302u : 0x0100u) | ((b & 1) ? 0x07060000u : 0x05040000u);
+  return __builtin_amdgcn_perm(x[b >> 1], x[a >> 1], sel);
 }
 
 // WPC words of one lane chunk, as 128-bit loads when the chunk is a whole
@@ -354,18 +395,30 @@ __global__ __launch_bounds__(kThreads) void qrow_generic(const Params p) {
       const int c = u / UPC, ui = u % UPC;
       const u32x4* src = reinterpret_cast<const u32x4*>(p.x + static_cast<int64_t>(s_xrow[mi]) * p.k +
                                                         static_cast<int64_t>(u) * 32);
-      u32x4 v[4];
+      uint32_t xin[16];
 #pragma unroll
-      for (int pc = 0; pc < 4; ++pc) v[pc] = src[pc];
+      for (int pc = 0; pc < 4; ++pc) {
+        const u32x4 v = src[pc];
+        xin[4 * pc] = v.x;
+        xin[4 * pc + 1] = v.y;
+        xin[4 * pc + 2] = v.z;
+        xin[4 * pc + 3] = v.w;
+      }
+      // pairs in the order the unpack pairs the codes; X over those pairs
       float X = 0.0f;
       const uint32_t ones = 0x3f803f80u;  // bf16 pair {1, 1}
 #pragma unroll
       for (int pc = 0; pc < 4; ++pc) {
-        X = dot2(v[pc].x, ones, X);
-        X = dot2(v[pc].y, ones, X);
-        X = dot2(v[pc].z, ones, X);
-        X = dot2(v[pc].w, ones, X);
-        xs[((mi * UPC + ui) * 4 + pc) * nchunks + c] = v[pc];
+        u32x4 o;
+        o.x = slot_pair<B>(xin, 4 * pc);
+        o.y = slot_pair<B>(xin, 4 * pc + 1);
+        o.z = slot_pair<B>(xin, 4 * pc + 2);
+        o.w = slot_pair<B>(xin, 4 * pc + 3);
+        X = dot2(o.x, ones, X);
+        X = dot2(o.y, ones, X);
+        X = dot2(o.z, ones, X);
+        X = dot2(o.w, ones, X);
+        xs[((mi * UPC + ui) * 4 + pc) * nchunks + c] = o;
       }
       xsum[(mi * UPC + ui) * nchunks + c] = X;
     }
@@ -405,7 +458,7 @@ __global__ __launch_bounds__(kThreads) void qrow_generic(const Params p) {
       for (int ui = 0; ui < UPC; ++ui) {
         uint32_t q[R][16];
 #pragma unroll
-        for (int r = 0; r < R; ++r) unpack_unit<B>(&st.w[r][ui * B], q[r]);
+        for (int r = 0; r < R; ++r) unpack_codes<B, 32>(&st.w[r][ui * B], q[r]);
         const int gi = (UPC >= UPG) ? ui / UPG : 0;
 #pragma unroll
         for (int mi = 0; mi < MB; ++mi) {
@@ -496,58 +549,21 @@ template <int B, int MB> struct FastRows {
   static constexpr int v = (MB == 1) ? ((B == 2 || B == 4 || B == 8) ? 4 : QG_ODD_ROWS_M1) : (MB <= 4 ? 2 : 1);
 };
 
-// NC codes (NC * B a multiple of 32) from NC*B/32 words -> NC/2 bf16 pairs.
-template <int B, int NC>
-__device__ __forceinline__ void unpack_codes(const uint32_t* w, uint32_t* q) {
-  static_assert((NC * B) % 32 == 0 && NC % 16 == 0, "whole words");
-  if constexpr (B == 8 || B == 4 || B == 2) {
-    constexpr int PER = 32 / B;  // codes per word
-#pragma unroll
-    for (int wi = 0; wi < NC * B / 32; ++wi) {
-      if constexpr (B == 8) {
-        const uint32_t v = w[wi];
-        q[2 * wi] = pack_bf16x2(static_cast<float>(v & 0xffu), static_cast<float>((v >> 8) & 0xffu));
-        q[2 * wi + 1] = pack_bf16x2(static_cast<float>((v >> 16) & 0xffu), static_cast<float>(v >> 24));
-      } else if constexpr (B == 4) {
-        const uint32_t lo = w[wi] & 0x0f0f0f0fu;
-        const uint32_t hi = (w[wi] >> 4) & 0x0f0f0f0fu;
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-          q[4 * wi + b] = pack_bf16x2(static_cast<float>((lo >> (8 * b)) & 0xffu),
-                                      static_cast<float>((hi >> (8 * b)) & 0xffu));
-      } else {
-        uint32_t t[4];
-#pragma unroll
-        for (int sft = 0; sft < 4; ++sft) t[sft] = (w[wi] >> (2 * sft)) & 0x03030303u;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          q[8 * wi + 2 * b] = pack_bf16x2(static_cast<float>((t[0] >> (8 * b)) & 0xffu),
-                                          static_cast<float>((t[1] >> (8 * b)) & 0xffu));
-          q[8 * wi + 2 * b + 1] = pack_bf16x2(static_cast<float>((t[2] >> (8 * b)) & 0xffu),
-                                              static_cast<float>((t[3] >> (8 * b)) & 0xffu));
-        }
-      }
-      (void)PER;
-    }
-  } else {
-    // odd widths: NC is a multiple of 32; each 32-code unit is B words
-#pragma unroll
-    for (int u = 0; u < NC / 32; ++u) unpack_pairs_generic<B, 0>(w + u * B, q + 16 * u);
-  }
-}
-
-// Branch-light butterfly for 16, 32 or 64 lanes per column: the same tree
-// as group_sum (rotate 8, rotate 4, swap 2, swap 1 inside a DPP row, then
-// xor 16, xor 32), with the cross-row steps selected by lane count.
-__device__ __forceinline__ float group_sum16(float v, int lpr) {
+// Sum over a column group of LPR = 16, 32 or 64 lanes: rotate 8, rotate 4,
+// swap pairs of 2, swap neighbours inside each 16-lane DPP row, then swap
+// the 16-lane halves of each 32 (ds_swizzle), then add the two 32-lane
+// halves.  Every lane of the group ends with the same bits.
+template <int LPR>
+__device__ __forceinline__ float gsum(float v) {
   v = dpp_add(v, 0);
   v = dpp_add(v, 1);
   v = dpp_add(v, 2);
   v = dpp_add(v, 3);
-  const float a = __shfl_xor(v, 16);
-  v = lpr >= 32 ? v + a : v;
-  const float b = __shfl_xor(v, 32);
-  v = lpr >= 64 ? v + b : v;
+  // (the swizzle and readlane builtins move 32-bit integers: bit-cast)
+  if constexpr (LPR >= 32) v = v + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+  if constexpr (LPR >= 64)
+    v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) +
+        __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
   return v;
 }
 
@@ -667,20 +683,59 @@ __global__ __launch_bounds__(kThreads) void qrow_fast(const Params p) {
       const int c = rest / NEU, e = rest % NEU;
       const u32x4* src = reinterpret_cast<const u32x4*>(
           p.x + static_cast<int64_t>(s_xrow[mi]) * p.k + static_cast<int64_t>(c) * CPC + e * EU);
+      uint32_t xin[EU / 2];
+#pragma unroll
+      for (int pc = 0; pc < XP; ++pc) {
+        const u32x4 v = src[pc];
+        xin[4 * pc] = v.x;
+        xin[4 * pc + 1] = v.y;
+        xin[4 * pc + 2] = v.z;
+        xin[4 * pc + 3] = v.w;
+      }
+      // pairs in the order the unpack pairs the codes; X over those pairs
       float X = 0.0f;
       const uint32_t ones = 0x3f803f80u;  // bf16 pair {1, 1}
 #pragma unroll
       for (int pc = 0; pc < XP; ++pc) {
-        const u32x4 v = src[pc];
-        X = dot2(v.x, ones, X);
-        X = dot2(v.y, ones, X);
-        X = dot2(v.z, ones, X);
-        X = dot2(v.w, ones, X);
-        xs[((mi * NEU + e) * XP + pc) * nchunks + c] = v;
+        u32x4 o;
+        o.x = slot_pair<B>(xin, 4 * pc);
+        o.y = slot_pair<B>(xin, 4 * pc + 1);
+        o.z = slot_pair<B>(xin, 4 * pc + 2);
+        o.w = slot_pair<B>(xin, 4 * pc + 3);
+        X = dot2(o.x, ones, X);
+        X = dot2(o.y, ones, X);
+        X = dot2(o.z, ones, X);
+        X = dot2(o.w, ones, X);
+        xs[((mi * NEU + e) * XP + pc) * nchunks + c] = o;
       }
       xsum[(mi * NEU + e) * nchunks + c] = X;
     }
     __syncthreads();
+
+    // One-row windows with chunks of at most 64 codes keep the lane's
+    // activations in registers across steps (refreshed only when the chunk
+    // column changes, i.e. never when a lane owns one chunk per row).
+    constexpr bool XH = (MB == 1) && (CPC <= 64);
+    uint32_t xh[XH ? NEU : 1][XH ? EU / 2 : 1];
+    float Xh[XH ? NEU : 1];
+    auto load_xh = [&](int j) {
+      if constexpr (XH) {
+        const int c = li + lpr * j;
+#pragma unroll
+        for (int e = 0; e < NEU; ++e) {
+#pragma unroll
+          for (int pc = 0; pc < XP; ++pc) {
+            const u32x4 v = xs[(e * XP + pc) * nchunks + c];
+            xh[e][4 * pc] = v.x;
+            xh[e][4 * pc + 1] = v.y;
+            xh[e][4 * pc + 2] = v.z;
+            xh[e][4 * pc + 3] = v.w;
+          }
+          Xh[e] = xsum[e * nchunks + c];
+        }
+      }
+    };
+    load_xh(0);
 
     struct Stage {
       uint32_t w[R * WPC];
@@ -744,6 +799,9 @@ __global__ __launch_bounds__(kThreads) void qrow_fast(const Params p) {
     auto compute_stage = [&](const Stage& st, int step) {
       const int i = step / cpl, j = step - (step / cpl) * cpl;
       const int c = li + lpr * j;
+      if constexpr (XH) {
+        if (cpl > 1) load_xh(j);
+      }
       if constexpr (STAGE) {
         // hand the pieces over: lane order in, chunk order out
 #pragma unroll
@@ -779,15 +837,22 @@ __global__ __launch_bounds__(kThreads) void qrow_fast(const Params p) {
           for (int mi = 0; mi < MB; ++mi) {
             if (mi < mcount) {
               uint32_t xv[EU / 2];
+              float X;
+              if constexpr (XH) {
 #pragma unroll
-              for (int pc = 0; pc < XP; ++pc) {
-                const u32x4 v = xs[((mi * NEU + e) * XP + pc) * nchunks + c];
-                xv[4 * pc] = v.x;
-                xv[4 * pc + 1] = v.y;
-                xv[4 * pc + 2] = v.z;
-                xv[4 * pc + 3] = v.w;
+                for (int pp = 0; pp < EU / 2; ++pp) xv[pp] = xh[e][pp];
+                X = Xh[e];
+              } else {
+#pragma unroll
+                for (int pc = 0; pc < XP; ++pc) {
+                  const u32x4 v = xs[((mi * NEU + e) * XP + pc) * nchunks + c];
+                  xv[4 * pc] = v.x;
+                  xv[4 * pc + 1] = v.y;
+                  xv[4 * pc + 2] = v.z;
+                  xv[4 * pc + 3] = v.w;
+                }
+                X = xsum[(mi * NEU + e) * nchunks + c];
               }
-              const float X = xsum[(mi * NEU + e) * nchunks + c];
               float a = 0.0f;
 #pragma unroll
               for (int pp = 0; pp < EU / 2; ++pp) a = dot2(q[pp], xv[pp], a);
@@ -805,7 +870,7 @@ __global__ __launch_bounds__(kThreads) void qrow_fast(const Params p) {
         for (int r = 0; r < R; ++r)
 #pragma unroll
           for (int mi = 0; mi < MB; ++mi) {
-            red[r][mi] = group_sum16(acc[r][mi], lpr);
+            red[r][mi] = lpr == 64 ? gsum<64>(acc[r][mi]) : (lpr == 32 ? gsum<32>(acc[r][mi]) : gsum<16>(acc[r][mi]));
             acc[r][mi] = 0.0f;
           }
         // lane li of a column group stores element li (+ 16, ...) of its
@@ -854,12 +919,12 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(const uint32_t* __rest
 #pragma unroll
   for (int i = 0; i < B; ++i) wu[i] = src[i];
   uint32_t q[16];
-  unpack_unit<B>(wu, q);
+  unpack_codes<B, 32>(wu, q);
   uint8_t* dst = codes + row * k + u * 32;
 #pragma unroll
   for (int pp = 0; pp < 16; ++pp) {
-    dst[2 * pp] = static_cast<uint8_t>(__uint_as_float(q[pp] << 16));
-    dst[2 * pp + 1] = static_cast<uint8_t>(__uint_as_float(q[pp] & 0xffff0000u));
+    dst[slot_code<B>(2 * pp)] = static_cast<uint8_t>(__uint_as_float(q[pp] << 16));
+    dst[slot_code<B>(2 * pp + 1)] = static_cast<uint8_t>(__uint_as_float(q[pp] & 0xffff0000u));
   }
 }
 
