@@ -103,20 +103,23 @@ class Workload:
             self.idx_bytes = 0
             self.kind = "plain"
             self.cols = [0]
-        elif name == "stack":
+        elif name in ("stack", "stack3"):
             st = synth.stack(m=m)
             self.k = st["k"]
             self.runs = [(r["bits"], r["group"], r["n"]) for r in st["runs"]]
             self.n_out = st["ldy"]
-            self.desc = ("fused stack K=2048: 4/64 x 2048, 5/128 x 6192, 6/64 x 48 into one "
-                         f"8288-column row by three strided calls, {m}-row window")
+            how = "one fused dispatch" if name == "stack" else "three strided calls"
+            self.desc = ("fused stack K=2048: 4/64 x 2048, 5/128 x 6192 (6144 + 48), 6/64 x 48 into one "
+                         f"8288-column row by {how}, {m}-row window")
             base = [tuple(t(r[key]) for key in ("words", "scales", "biases")) for r in st["runs"]]
             self.x = t(st["x"])
             self.y = torch.empty((m, st["ldy"]), dtype=torch.float32, device=dev)
             self.idx_bytes = 0
-            self.kind = "strided"
+            self.kind = "strided" if name == "stack3" else "fused"
             self.cols = [r["col"] for r in st["runs"]]
             self.ldy = st["ldy"]
+            self.members = [[(6144, 2048), (48, 8192)] if r["n"] == 6192 else [(r["n"], r["col"])]
+                            for r in st["runs"]]
         elif name == "experts":
             d = synth.experts()
             self.k = d["k"]
@@ -145,6 +148,11 @@ class Workload:
         for c in range(copies):
             trip_list = base if c == 0 else [tuple(a.clone() for a in trip) for trip in base]
             mats = []
+            if self.kind == "fused":
+                specs = [dict(bits=bits, group=group, n=n, k=self.k, w=w, scales=s, biases=b, members=mem)
+                         for (w, s, b), (bits, group, n), mem in zip(trip_list, self.runs, self.members)]
+                self.copies.append((trip_list, [qgemv.Stack(specs, self.ldy)]))
+                continue
             for (w, s, b), run_ in zip(trip_list, self.runs if self.kind != "indexed" else [None]):
                 if self.kind == "indexed":
                     mats.append(qgemv.Matrix(4, 64, self.n_each, self.k, w, s, b, n_experts=self.n_experts))
@@ -159,6 +167,9 @@ class Workload:
         q = self.qgemv
         if self.kind == "plain":
             rc = q.qgemv_run(mats[0].h, self.x, self.m, self.y, 0, stream)
+            assert rc == 0, q.qgemv_strerror(rc)
+        elif self.kind == "fused":
+            rc = q.qgemv_stack_run(mats[0].h, self.x, self.m, self.y, 0, stream)
             assert rc == 0, q.qgemv_strerror(rc)
         elif self.kind == "strided":
             for mat, col in zip(mats, self.cols):
@@ -234,7 +245,7 @@ def main():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=300,
                     help="untimed steps; the GPU clock needs ~20 ms of load to settle")
-    ap.add_argument("--workload", default="lmhead", choices=["lmhead", "stack", "experts"])
+    ap.add_argument("--workload", default="lmhead", choices=["lmhead", "stack", "stack3", "experts"])
     ap.add_argument("--m", type=int, default=1, help="window rows")
     ap.add_argument("--all", action="store_true", help="also time the other workloads and windows")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -291,7 +302,7 @@ def main():
     if args.all:
         extra = {}
         for name, m in [("lmhead", 1), ("lmhead", 8), ("lmhead", 16), ("stack", 1), ("stack", 16),
-                        ("experts", 16)]:
+                        ("stack3", 1), ("stack3", 16), ("experts", 16)]:
             if name == args.workload and m == wl.m:
                 continue
             w2 = Workload(name, m, torch, qgemv, synth)

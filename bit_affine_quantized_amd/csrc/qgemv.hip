@@ -105,6 +105,11 @@ void init_device(DeviceInfo* info) {
                                         static_cast<int>(qg::kMaxDynamicLds)) != hipSuccess)
             return;
     }
+  for (qg::StackFn fn : {qg::stack_kernel_m1(), qg::stack_kernel_m2(), qg::stack_kernel_m4(),
+                         qg::stack_kernel_m8(), qg::stack_kernel_m16()})
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(qg::kMaxDynamicLds)) != hipSuccess)
+      return;
   info->cus = cus;
   info->status = QGEMV_OK;
 }
@@ -194,6 +199,9 @@ int launch(const qgemv_handle* h, const uint16_t* x, int32_t m, float* y, int64_
   p.indexed = indexed;
   p.vec_groups = h->vec_groups;
   p.y_bytes = static_cast<int64_t>(ybytes);
+  p.nseg = 1;
+  p.seg_row0[0] = 0;
+  p.seg_delta[0] = 0;
 
   // A persistent grid: as many blocks as the CUs hold at once, each walking
   // its tiles with the staged window reused (grid size never changes bits:
@@ -212,7 +220,10 @@ int launch(const qgemv_handle* h, const uint16_t* x, int32_t m, float* y, int64_
   if (blocks > cap) blocks = cap;
   dim3 grid(static_cast<unsigned>(blocks), 1u);
   if (indexed) {
-    grid.x = static_cast<unsigned>(tiles < 8 ? tiles : 8);
+    // blocks per expert: enough that the experts a call routes to (not known
+    // on the host) keep every CU's waves streaming
+    const int64_t per = tiles < 32 ? tiles : 32;
+    grid.x = static_cast<unsigned>(per);
     grid.y = static_cast<unsigned>(h->d.n_experts);
   }
   hipLaunchKernelGGL(fn, grid, dim3(qg::kThreads), lds, static_cast<hipStream_t>(stream), p);
@@ -360,6 +371,170 @@ int qgemv_debug_unpack(qgemv_t h, int32_t expert, uint8_t* codes, void* stream) 
   if (!fn) return QGEMV_E_NOKERNEL;
   hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(blocks)), dim3(qg::kThreads), 0,
                      static_cast<hipStream_t>(stream), w, n, k, codes);
+  return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_E_HIP;
+}
+
+
+struct qgemv_stack {
+  int n_runs;
+  int64_t ldy;
+  int64_t col_end;                       // one past the last member column
+  qgemv_handle* run[qg::kMaxRuns];
+  int n_members[qg::kMaxRuns];
+  int64_t member_rows[qg::kMaxRuns][qg::kMaxSeg];
+  int64_t member_cols[qg::kMaxRuns][qg::kMaxSeg];
+  mutable std::atomic<int> occupancy[5];
+  ~qgemv_stack() {
+    for (int r = 0; r < n_runs; ++r) delete run[r];
+  }
+};
+
+int qgemv_stack_create(const qgemv_run_spec* runs, int32_t n_runs, int64_t ldy, qgemv_stack_t* out) {
+  if (!runs || !out) return QGEMV_E_ARG;
+  if (n_runs < 1 || n_runs > qg::kMaxRuns) return QGEMV_E_ARG;
+  if (ldy < 1) return QGEMV_E_STRIDE;
+  std::unique_ptr<qgemv_stack> st(new (std::nothrow) qgemv_stack());
+  if (!st) return QGEMV_E_ARG;
+  for (auto& o : st->occupancy) o.store(0);
+  st->ldy = ldy;
+  st->n_runs = 0;
+  int64_t ranges[qg::kMaxRuns * qg::kMaxSeg][2];
+  int nranges = 0;
+  for (int r = 0; r < n_runs; ++r) {
+    const qgemv_run_spec& rr = runs[r];
+    qgemv_t h = nullptr;
+    const int rc = qgemv_create(&rr.w, &h);
+    if (rc != QGEMV_OK) return rc;
+    st->run[st->n_runs++] = h;
+    if (rr.w.n_experts != 1) return QGEMV_E_ARG;
+    if (rr.w.k != runs[0].w.k) return QGEMV_E_SHAPE;
+    if (!h->fast) return QGEMV_E_NOKERNEL;
+    if (rr.n_members < 1 || rr.n_members > qg::kMaxSeg) return QGEMV_E_ARG;
+    int64_t rows = 0;
+    for (int mbr = 0; mbr < rr.n_members; ++mbr) {
+      const int64_t nr = rr.member_rows[mbr], c = rr.member_cols[mbr];
+      if (nr < 1) return QGEMV_E_SHAPE;
+      if (c < 0 || c + nr > ldy) return QGEMV_E_STRIDE;
+      for (int q = 0; q < nranges; ++q)
+        if (c < ranges[q][1] && ranges[q][0] < c + nr) return QGEMV_E_ALIAS;
+      ranges[nranges][0] = c;
+      ranges[nranges][1] = c + nr;
+      ++nranges;
+      st->member_rows[r][mbr] = nr;
+      st->member_cols[r][mbr] = c;
+      if (c + nr > st->col_end) st->col_end = c + nr;
+      rows += nr;
+    }
+    if (rows != rr.w.n) return QGEMV_E_SHAPE;
+    st->n_members[r] = rr.n_members;
+  }
+  *out = st.release();
+  return QGEMV_OK;
+}
+
+void qgemv_stack_destroy(qgemv_stack_t s) { delete s; }
+
+int qgemv_stack_run(qgemv_stack_t s, const uint16_t* x, int32_t m, float* y, int32_t epi, void* stream) {
+  if (!s) return QGEMV_E_ARG;
+  if (m < 0 || m > QGEMV_MAX_WINDOW) return QGEMV_E_WINDOW;
+  if (epi != QGEMV_EPI_NONE && epi != QGEMV_EPI_RELU2) return QGEMV_E_ARG;
+  if (m == 0) return QGEMV_OK;
+  if (!x || !y) return QGEMV_E_ARG;
+  if ((reinterpret_cast<uintptr_t>(x) & 15) || (reinterpret_cast<uintptr_t>(y) & 3)) return QGEMV_E_ALIGN;
+  const int64_t k = s->run[0]->d.k;
+  const size_t xbytes = static_cast<size_t>(m) * k * 2;
+  const size_t ybytes = (static_cast<size_t>(m - 1) * s->ldy + s->col_end) * 4;
+  if (ybytes > 0x7fffffffu) return QGEMV_E_STRIDE;
+  for (int r = 0; r < s->n_runs; ++r) {
+    const int rc = check_y_alias(s->run[r], y, ybytes, x, xbytes, nullptr, 0);
+    if (rc != QGEMV_OK) return rc;
+  }
+  const DeviceInfo* dev = current_device();
+  if (!dev) return QGEMV_E_HIP;
+  const int var = window_variant(m);
+  qg::StackParams sp{};
+  sp.nruns = s->n_runs;
+  size_t lds = 0;
+  int64_t tiles[qg::kMaxRuns];
+  int64_t total_tiles = 0;
+  for (int r = 0; r < s->n_runs; ++r) {
+    const qgemv_handle* h = s->run[r];
+    int stage = h->ppc > 1 ? 1 : 0;
+    if (stage && lds_bytes(h, var, 1) > qg::kMaxDynamicLds) stage = 0;
+    const size_t l = lds_bytes(h, var, stage);
+    if (l > qg::kMaxDynamicLds) return QGEMV_E_WINDOW;
+    if (l > lds) lds = l;
+    const int R = h->entry->fast_rows[var];
+    const int64_t tile_rows = static_cast<int64_t>(qg::kWaves) * (qg::kWave / h->lpr) * R;
+    tiles[r] = (h->d.n + tile_rows - 1) / tile_rows;
+    total_tiles += tiles[r];
+    const int bi = qg::bits_index(h->d.bits), gi = qg::group_index(h->d.group);
+    sp.kind[r] = (bi * 3 + gi) * 2 + stage;
+    qg::Params& p = sp.run[r];
+    p.w = h->d.w;
+    p.scales = h->d.scales;
+    p.biases = h->d.biases;
+    p.x = x;
+    p.y = y;
+    p.idx = nullptr;
+    p.n = h->d.n;
+    p.k = h->d.k;
+    p.wpr = h->wpr;
+    p.gpr = h->gpr;
+    p.ldy = s->ldy;
+    p.m = m;
+    p.slots = 0;
+    p.n_experts = 1;
+    p.epi = epi;
+    p.lpr = h->lpr;
+    p.cpl = h->cpl;
+    p.nchunks = h->nchunks;
+    p.tiles = static_cast<int32_t>(tiles[r]);
+    p.indexed = 0;
+    p.vec_groups = h->vec_groups;
+    p.y_bytes = static_cast<int64_t>(ybytes);
+    p.nseg = s->n_members[r];
+    int64_t row0 = 0;
+    for (int mbr = 0; mbr < s->n_members[r]; ++mbr) {
+      p.seg_row0[mbr] = static_cast<int32_t>(row0);
+      p.seg_delta[mbr] = s->member_cols[r][mbr] - row0;
+      row0 += s->member_rows[r][mbr];
+    }
+  }
+  qg::StackFn fn = nullptr;
+  switch (var) {
+    case 0: fn = qg::stack_kernel_m1(); break;
+    case 1: fn = qg::stack_kernel_m2(); break;
+    case 2: fn = qg::stack_kernel_m4(); break;
+    case 3: fn = qg::stack_kernel_m8(); break;
+    default: fn = qg::stack_kernel_m16(); break;
+  }
+  int occ = s->occupancy[var].load(std::memory_order_relaxed);
+  if (occ == 0) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(fn), qg::kThreads,
+                                                     lds) != hipSuccess || nb < 1)
+      nb = 1;
+    occ = nb;
+    s->occupancy[var].store(occ, std::memory_order_relaxed);
+  }
+  // blocks per run: every tile its own block when the CUs hold them all,
+  // else a share of the resident blocks in proportion to the run's tiles
+  const int64_t cap = static_cast<int64_t>(dev->cus) * occ;
+  int64_t b0 = 0;
+  for (int r = 0; r < s->n_runs; ++r) {
+    int64_t nb = tiles[r];
+    if (total_tiles > cap) {
+      nb = cap * tiles[r] / total_tiles;
+      if (nb < 1) nb = 1;
+      if (nb > tiles[r]) nb = tiles[r];
+    }
+    sp.block0[r] = static_cast<int32_t>(b0);
+    b0 += nb;
+  }
+  sp.block0[s->n_runs] = static_cast<int32_t>(b0);
+  hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(b0)), dim3(qg::kThreads), lds,
+                     static_cast<hipStream_t>(stream), sp);
   return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_E_HIP;
 }
 

@@ -54,6 +54,8 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxSlots = 64;
 constexpr int kMaxList = QGEMV_MAX_WINDOW * kMaxSlots;
+constexpr int kMaxSeg = 4;    // members per run of a fused stack
+constexpr int kMaxRuns = 8;   // runs per fused stack
 // 160 KiB of LDS per CU on gfx950, less the kernels' static arrays.
 constexpr size_t kMaxDynamicLds = 160 * 1024 - 8 * 1024;
 
@@ -224,6 +226,11 @@ struct Params {
   int32_t indexed;          // 0: plain/strided, 1: indexed
   int32_t vec_groups;       // scales/biases aligned for packed loads
   int64_t y_bytes;          // extent of y written by this call (fast kernel stores)
+  // column map: rows [seg_row0[s], seg_row0[s+1]) are written at column
+  // row + seg_delta[s] (one segment {0, 0} for plain, strided and indexed calls)
+  int32_t nseg;
+  int32_t seg_row0[kMaxSeg];
+  int64_t seg_delta[kMaxSeg];
 };
 
 __device__ __forceinline__ float apply_epi(float v, int epi) {
@@ -603,8 +610,22 @@ __device__ __forceinline__ void load_groups_buf(__amdgpu_buffer_rsrc_t r, int of
   }
 }
 
+// Output column of weight row `row` under the call's column map.
+// (constant indices only, so a Params copy can live in registers)
+__device__ __forceinline__ int64_t mapped_column(const Params& p, int row) {
+  int64_t d = p.seg_delta[0];
+#pragma unroll
+  for (int sg = 1; sg < kMaxSeg; ++sg)
+    if (sg < p.nseg && row >= p.seg_row0[sg]) d = p.seg_delta[sg];
+  return row + d;
+}
+
+// The fast row product for block bx of gx blocks (tiles bx, bx + gx, ...).
+// Shared arrays come from the calling kernel so that several bodies can be
+// inlined into one fused-stack kernel without their LDS adding up.
 template <int B, int G, int MB, bool STAGE>
-__global__ __launch_bounds__(kThreads) void qrow_fast(const Params p) {
+__device__ __forceinline__ void fast_body(const Params& p, const int bx, const int gx, unsigned char* smem,
+                                          int* s_list, int* s_wave_cnt, int* s_xrow, int64_t* s_yoff) {
   constexpr int PPC = Geo<B>::PPC, CPC = Geo<B>::CPC;
   constexpr int WPC = 4 * PPC;                      // words per chunk
   constexpr int CB = 16 * PPC;                      // bytes per chunk
@@ -615,12 +636,6 @@ __global__ __launch_bounds__(kThreads) void qrow_fast(const Params p) {
   constexpr int SW = NEU >= 2 ? NEU / 2 : 1;        // packed scale words per chunk
   constexpr int R = FastRows<B, MB>::v;
   constexpr int GSPAN = NEU >= 2 ? NEU : 1;         // groups read per chunk
-
-  extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ int s_list[kMaxList];
-  __shared__ int s_wave_cnt[kWaves];
-  __shared__ int s_xrow[MB];
-  __shared__ int64_t s_yoff[MB];
 
   const int nchunks = p.nchunks;
   // LDS: x pieces [MB][NEU][XP][nchunks] x 16 B, unit sums [MB][NEU][nchunks],
@@ -656,62 +671,13 @@ __global__ __launch_bounds__(kThreads) void qrow_fast(const Params p) {
   const unsigned char* wexp = reinterpret_cast<const unsigned char*>(p.w) + static_cast<int64_t>(expert) * p.n * row_bytes;
   const unsigned char* sexp = reinterpret_cast<const unsigned char*>(p.scales) + static_cast<int64_t>(expert) * p.n * gpr2;
   const unsigned char* bexp = reinterpret_cast<const unsigned char*>(p.biases) + static_cast<int64_t>(expert) * p.n * gpr2;
-  const int my_tiles = blockIdx.x < p.tiles ? (p.tiles - 1 - blockIdx.x) / gridDim.x + 1 : 0;
+  const int my_tiles = bx < p.tiles ? (p.tiles - 1 - bx) / gx + 1 : 0;
   const int steps = my_tiles * cpl;
   // y as one buffer resource: lanes with nothing to store aim past its end
   const __amdgpu_buffer_rsrc_t yres = make_rsrc(p.y, p.y_bytes);
 
   for (int c0 = 0; c0 < total; c0 += MB) {
     const int mcount = min(MB, total - c0);
-    if (tid < mcount) {
-      const int e = c0 + tid;
-      if (p.indexed) {
-        const int t = s_list[e];
-        const int row = t / p.slots, sl = t % p.slots;
-        s_xrow[tid] = row;
-        s_yoff[tid] = (static_cast<int64_t>(row) * p.slots + sl) * p.n;
-      } else {
-        s_xrow[tid] = e;
-        s_yoff[tid] = static_cast<int64_t>(e) * p.ldy;
-      }
-    }
-    __syncthreads();
-    // ---- stage the window: activation pieces and per-unit sums ----
-    for (int t = tid; t < mcount * nchunks * NEU; t += kThreads) {
-      const int mi = t / (nchunks * NEU);
-      const int rest = t % (nchunks * NEU);
-      const int c = rest / NEU, e = rest % NEU;
-      const u32x4* src = reinterpret_cast<const u32x4*>(
-          p.x + static_cast<int64_t>(s_xrow[mi]) * p.k + static_cast<int64_t>(c) * CPC + e * EU);
-      uint32_t xin[EU / 2];
-#pragma unroll
-      for (int pc = 0; pc < XP; ++pc) {
-        const u32x4 v = src[pc];
-        xin[4 * pc] = v.x;
-        xin[4 * pc + 1] = v.y;
-        xin[4 * pc + 2] = v.z;
-        xin[4 * pc + 3] = v.w;
-      }
-      // pairs in the order the unpack pairs the codes; X over those pairs
-      float X = 0.0f;
-      const uint32_t ones = 0x3f803f80u;  // bf16 pair {1, 1}
-#pragma unroll
-      for (int pc = 0; pc < XP; ++pc) {
-        u32x4 o;
-        o.x = slot_pair<B>(xin, 4 * pc);
-        o.y = slot_pair<B>(xin, 4 * pc + 1);
-        o.z = slot_pair<B>(xin, 4 * pc + 2);
-        o.w = slot_pair<B>(xin, 4 * pc + 3);
-        X = dot2(o.x, ones, X);
-        X = dot2(o.y, ones, X);
-        X = dot2(o.z, ones, X);
-        X = dot2(o.w, ones, X);
-        xs[((mi * NEU + e) * XP + pc) * nchunks + c] = o;
-      }
-      xsum[(mi * NEU + e) * nchunks + c] = X;
-    }
-    __syncthreads();
-
     // One-row windows with chunks of at most 64 codes keep the lane's
     // activations in registers across steps (refreshed only when the chunk
     // column changes, i.e. never when a lane owns one chunk per row).
@@ -735,8 +701,6 @@ __global__ __launch_bounds__(kThreads) void qrow_fast(const Params p) {
         }
       }
     };
-    load_xh(0);
-
     struct Stage {
       uint32_t w[R * WPC];
       uint32_t s[R][SW];
@@ -746,7 +710,7 @@ __global__ __launch_bounds__(kThreads) void qrow_fast(const Params p) {
     // [wrow0, wrow0 + wave_rows), lane (slot, li) owns rows wrow0 + r*S + slot
     auto load_stage = [&](Stage& st, int step) {
       const int i = step / cpl, j = step - (step / cpl) * cpl;
-      const int tile = blockIdx.x + i * gridDim.x;
+      const int tile = bx + i * gx;
       const int wrow0 = tile * tile_rows + wv * wave_rows;
       const __amdgpu_buffer_rsrc_t wr = make_rsrc(wexp + wrow0 * row_bytes, (n - wrow0) * row_bytes);
       const __amdgpu_buffer_rsrc_t sr = make_rsrc(sexp + static_cast<int64_t>(wrow0) * gpr2,
@@ -863,7 +827,7 @@ __global__ __launch_bounds__(kThreads) void qrow_fast(const Params p) {
         }
       }
       if (j == cpl - 1) {
-        const int tile = blockIdx.x + i * gridDim.x;
+        const int tile = bx + i * gx;
         const int wrow0 = tile * tile_rows + wv * wave_rows;
         float red[R][MB];
 #pragma unroll
@@ -884,15 +848,66 @@ __global__ __launch_bounds__(kThreads) void qrow_fast(const Params p) {
           const int r = e / MB, mi = e - (e / MB) * MB;
           const int row = wrow0 + r * slots_per_wave + slot;
           const bool ok = e < R * MB && li < 16 && mi < mcount && row < n;
-          const int off = ok ? static_cast<int>((s_yoff[ok ? mi : 0] + row) * 4) : 0x7ffffff0;
+          const int off = ok ? static_cast<int>((s_yoff[ok ? mi : 0] + mapped_column(p, row)) * 4) : 0x7ffffff0;
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(apply_epi(v, p.epi)), yres, off, 0, 0);
         }
       }
     };
 
+    // the first step's weights are in flight while the window is staged
     Stage sa, sb;
+    if (steps > 0) load_stage(sa, 0);
+    if (tid < mcount) {
+      const int e = c0 + tid;
+      if (p.indexed) {
+        const int t = s_list[e];
+        const int row = t / p.slots, sl = t % p.slots;
+        s_xrow[tid] = row;
+        s_yoff[tid] = (static_cast<int64_t>(row) * p.slots + sl) * p.n;
+      } else {
+        s_xrow[tid] = e;
+        s_yoff[tid] = static_cast<int64_t>(e) * p.ldy;
+      }
+    }
+    __syncthreads();
+    // ---- stage the window: activation pieces and per-unit sums ----
+    for (int t = tid; t < mcount * nchunks * NEU; t += kThreads) {
+      const int mi = t / (nchunks * NEU);
+      const int rest = t % (nchunks * NEU);
+      const int c = rest / NEU, e = rest % NEU;
+      const u32x4* src = reinterpret_cast<const u32x4*>(
+          p.x + static_cast<int64_t>(s_xrow[mi]) * p.k + static_cast<int64_t>(c) * CPC + e * EU);
+      uint32_t xin[EU / 2];
+#pragma unroll
+      for (int pc = 0; pc < XP; ++pc) {
+        const u32x4 v = src[pc];
+        xin[4 * pc] = v.x;
+        xin[4 * pc + 1] = v.y;
+        xin[4 * pc + 2] = v.z;
+        xin[4 * pc + 3] = v.w;
+      }
+      // pairs in the order the unpack pairs the codes; X over those pairs
+      float X = 0.0f;
+      const uint32_t ones = 0x3f803f80u;  // bf16 pair {1, 1}
+#pragma unroll
+      for (int pc = 0; pc < XP; ++pc) {
+        u32x4 o;
+        o.x = slot_pair<B>(xin, 4 * pc);
+        o.y = slot_pair<B>(xin, 4 * pc + 1);
+        o.z = slot_pair<B>(xin, 4 * pc + 2);
+        o.w = slot_pair<B>(xin, 4 * pc + 3);
+        X = dot2(o.x, ones, X);
+        X = dot2(o.y, ones, X);
+        X = dot2(o.z, ones, X);
+        X = dot2(o.w, ones, X);
+        xs[((mi * NEU + e) * XP + pc) * nchunks + c] = o;
+      }
+      xsum[(mi * NEU + e) * nchunks + c] = X;
+    }
+    __syncthreads();
+
+    load_xh(0);
     if (steps > 0) {
-      load_stage(sa, 0);
       int step = 0;
       for (; step + 1 < steps; step += 2) {
         load_stage(sb, step + 1);
@@ -904,6 +919,95 @@ __global__ __launch_bounds__(kThreads) void qrow_fast(const Params p) {
     }
     __syncthreads();  // LDS window reused by the next chunk of routed rows
   }
+}
+
+template <int B, int G, int MB, bool STAGE>
+__global__ __launch_bounds__(kThreads) void qrow_fast(const Params p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int s_list[kMaxList];
+  __shared__ int s_wave_cnt[kWaves];
+  __shared__ int s_xrow[QGEMV_MAX_WINDOW];
+  __shared__ int64_t s_yoff[QGEMV_MAX_WINDOW];
+  fast_body<B, G, MB, STAGE>(p, blockIdx.x, gridDim.x, smem, s_list, s_wave_cnt, s_xrow, s_yoff);
+}
+
+// ---------------------------------------------------------------------------
+// Fused stack: the runs of a fused projection (each a matrix of one width and
+// group whose members write their own output columns) in one dispatch.  The
+// blocks are split among the runs; each run executes exactly the body of its
+// own strided call, so every member's bits equal that call's.
+// ---------------------------------------------------------------------------
+
+struct StackParams {
+  Params run[kMaxRuns];
+  int32_t kind[kMaxRuns];         // (bits index * 3 + group index) * 2 + staging
+  int32_t block0[kMaxRuns + 1];   // first block of each run; block0[nruns] = grid
+  int32_t nruns;
+};
+
+template <int MB>
+__global__ __launch_bounds__(kThreads) void qrow_stack(const StackParams sp) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int s_list[kMaxList];
+  __shared__ int s_wave_cnt[kWaves];
+  __shared__ int s_xrow[QGEMV_MAX_WINDOW];
+  __shared__ int64_t s_yoff[QGEMV_MAX_WINDOW];
+  int r = 0, lo = sp.block0[0], hi = sp.block0[1];
+#pragma unroll
+  for (int q = 1; q < kMaxRuns; ++q)
+    if (q < sp.nruns && static_cast<int>(blockIdx.x) >= sp.block0[q]) {
+      r = q;
+      lo = sp.block0[q];
+      hi = sp.block0[q + 1];
+    }
+  const int bx = static_cast<int>(blockIdx.x) - lo;
+  const int gx = hi - lo;
+  // the run's parameters, selected with constant indices (a run-time index
+  // into the argument struct would copy all of it to scratch)
+  Params p;
+  switch (r) {
+    case 0: p = sp.run[0]; break;
+    case 1: p = sp.run[1]; break;
+    case 2: p = sp.run[2]; break;
+    case 3: p = sp.run[3]; break;
+    case 4: p = sp.run[4]; break;
+    case 5: p = sp.run[5]; break;
+    case 6: p = sp.run[6]; break;
+    default: p = sp.run[7]; break;
+  }
+  static_assert(kMaxRuns == 8, "one case per run");
+// (the empty asm keeps each case's parameter loads inside the case, so no
+// value is live across the switch)
+#define QG_BODY(B, G, STG)               \
+  do {                                   \
+    asm volatile("" ::: "memory");       \
+    fast_body<B, G, MB, STG>(p, bx, gx, smem, s_list, s_wave_cnt, s_xrow, s_yoff); \
+  } while (0)
+#define QG_PAIR(BI, B, GI, G)                  \
+  case ((BI) * 3 + (GI)) * 2:                   \
+    QG_BODY(B, G, false);                       \
+    break;                                      \
+  case ((BI) * 3 + (GI)) * 2 + 1:               \
+    if constexpr (Geo<B>::PPC > 1) QG_BODY(B, G, true); \
+    break;
+#define QG_WIDTH(BI, B) QG_PAIR(BI, B, 0, 32) QG_PAIR(BI, B, 1, 64) QG_PAIR(BI, B, 2, 128)
+  int kind = sp.kind[0];
+#pragma unroll
+  for (int q = 1; q < kMaxRuns; ++q)
+    if (q == r) kind = sp.kind[q];
+  switch (kind) {
+    QG_WIDTH(0, 2)
+    QG_WIDTH(1, 3)
+    QG_WIDTH(2, 4)
+    QG_WIDTH(3, 5)
+    QG_WIDTH(4, 6)
+    QG_WIDTH(5, 8)
+    default:
+      break;
+  }
+#undef QG_WIDTH
+#undef QG_PAIR
+#undef QG_BODY
 }
 
 // The product kernels' own unpack, written back as integer codes.
@@ -987,5 +1091,14 @@ const Entry* entries_b4();
 const Entry* entries_b5();
 const Entry* entries_b6();
 const Entry* entries_b8();
+
+// Fused-stack kernels by window variant (1, 2, 4, 8, 16 rows), one
+// translation unit each.
+typedef void (*StackFn)(const StackParams);
+StackFn stack_kernel_m1();
+StackFn stack_kernel_m2();
+StackFn stack_kernel_m4();
+StackFn stack_kernel_m8();
+StackFn stack_kernel_m16();
 
 }  // namespace qg

@@ -37,6 +37,15 @@ class qgemv_desc(ctypes.Structure):
                 ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p)]
 
 
+QGEMV_MAX_RUNS, QGEMV_MAX_MEMBERS = 8, 4
+
+
+class qgemv_run_spec(ctypes.Structure):
+    _fields_ = [("w", qgemv_desc), ("n_members", ctypes.c_int32),
+                ("member_rows", ctypes.c_int64 * QGEMV_MAX_MEMBERS),
+                ("member_cols", ctypes.c_int64 * QGEMV_MAX_MEMBERS)]
+
+
 def load(path: str | None = None):
     """The loaded library; raises if it is not built (no fallback exists).
     QGEMV_LIB names another build of the same library (e.g. a tuning build)."""
@@ -64,6 +73,12 @@ def load(path: str | None = None):
             lib.qgemv_strerror.restype = ctypes.c_char_p
             lib.qgemv_query.argtypes = [p, ctypes.POINTER(ctypes.c_int64 * 6)]
             lib.qgemv_query.restype = ctypes.c_int
+            lib.qgemv_stack_create.argtypes = [ctypes.POINTER(qgemv_run_spec), i32, i64, ctypes.POINTER(p)]
+            lib.qgemv_stack_create.restype = ctypes.c_int
+            lib.qgemv_stack_run.argtypes = [p, p, i32, p, i32, p]
+            lib.qgemv_stack_run.restype = ctypes.c_int
+            lib.qgemv_stack_destroy.argtypes = [p]
+            lib.qgemv_stack_destroy.restype = None
             _lib = lib
     return _lib
 
@@ -125,6 +140,31 @@ def qgemv_query(h):
     return rc, list(out)
 
 
+def qgemv_stack_create(runs, ldy):
+    """runs: list of dicts with bits, group, n, k, w, scales, biases and
+    members = [(rows, first_column), ...].  Returns (status, handle)."""
+    arr = (qgemv_run_spec * max(1, len(runs)))()
+    for i, r in enumerate(runs):
+        arr[i].w = qgemv_desc(r["bits"], r["group"], r["n"], r["k"], 1, _addr(r["w"]),
+                              _addr(r["scales"]), _addr(r["biases"]))
+        members = r["members"]
+        arr[i].n_members = len(members)
+        for j, (rows, col) in enumerate(members[:QGEMV_MAX_MEMBERS]):
+            arr[i].member_rows[j] = rows
+            arr[i].member_cols[j] = col
+    h = ctypes.c_void_p()
+    rc = load().qgemv_stack_create(arr, len(runs), ldy, ctypes.byref(h))
+    return rc, (h.value if rc == QGEMV_OK else None)
+
+
+def qgemv_stack_run(h, x, m, y, epi=QGEMV_EPI_NONE, stream=None) -> int:
+    return load().qgemv_stack_run(h, _addr(x), m, _addr(y), epi, _stream(stream))
+
+
+def qgemv_stack_destroy(h) -> None:
+    load().qgemv_stack_destroy(h)
+
+
 # ---- convenience wrapper over torch device tensors ---------------------------
 
 class Matrix:
@@ -173,6 +213,36 @@ class Matrix:
     def close(self):
         if getattr(self, "h", None):
             qgemv_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Stack:
+    """A fused stack over torch device tensors (kept alive with the handle)."""
+
+    def __init__(self, runs, ldy):
+        self._keep = [(r["w"], r["scales"], r["biases"]) for r in runs]
+        self.ldy = ldy
+        rc, h = qgemv_stack_create(runs, ldy)
+        if rc != QGEMV_OK:
+            raise QgemvError("qgemv_stack_create", rc)
+        self.h = h
+
+    def run(self, x, y, m=None, epi=QGEMV_EPI_NONE, stream=None):
+        m = x.shape[0] if m is None else m
+        rc = qgemv_stack_run(self.h, x, m, y, epi, stream)
+        if rc != QGEMV_OK:
+            raise QgemvError("qgemv_stack_run", rc)
+        return y
+
+    def close(self):
+        if getattr(self, "h", None):
+            qgemv_stack_destroy(self.h)
             self.h = None
 
     def __del__(self):

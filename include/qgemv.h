@@ -140,6 +140,49 @@ int qgemv_debug_unpack(qgemv_t h, int32_t expert, uint8_t* codes, void* stream);
 /* Name of a status code ("QGEMV_E_STRIDE", ...); never NULL. */
 const char* qgemv_strerror(int status);
 
+/* ---- fused stacks ------------------------------------------------------
+ * A fused projection is a set of runs sharing one input: each run is one
+ * matrix of one width and group, and its members (consecutive row ranges of
+ * the run) write their own columns of one output row of ldy columns, with no
+ * scratch copy.  qgemv_stack_run computes every run in ONE dispatch; each
+ * member's columns are bit for bit what qgemv_run_strided of that run's own
+ * handle writes there (same kernels, same arithmetic).  Columns outside every
+ * member are left untouched.
+ * Sources, on "Qwen3.8-Flash-Next faster kernels in Zig engine - #788":
+ * commit "...row kernel at every MLX width" (callStrided: one member of a
+ * fused stack writes its columns straight into the stack output), and on
+ * "Qwen3.8-Flash-Next support for oQ in Zig engine - #774", "What this
+ * changes" items 2-3 (runs grouped by width, placed at their members'
+ * columns through a column map; oQ4e's ragged 6192/48 runs). */
+#define QGEMV_MAX_RUNS 8
+#define QGEMV_MAX_MEMBERS 4
+
+typedef struct qgemv_run_spec {
+  qgemv_desc w;                            /* the run's weights; w.n_experts must be 1 */
+  int32_t n_members;                       /* 1..QGEMV_MAX_MEMBERS */
+  int64_t member_rows[QGEMV_MAX_MEMBERS];  /* rows of each member in the run's row order; sum = w.n */
+  int64_t member_cols[QGEMV_MAX_MEMBERS];  /* first output column of each member */
+} qgemv_run_spec;
+
+typedef struct qgemv_stack* qgemv_stack_t;
+
+/* Validate every run as qgemv_create does (its status is returned as is),
+ * then: 1 <= n_runs <= QGEMV_MAX_RUNS, every run has the same k (else
+ * QGEMV_E_SHAPE), member rows are >= 1 and sum to the run's n (QGEMV_E_SHAPE),
+ * every member's columns lie in [0, ldy) (QGEMV_E_STRIDE), no two members
+ * share a column (QGEMV_E_ALIAS), and every run has k a whole number of
+ * 16-lane chunks (QGEMV_E_NOKERNEL otherwise).  Borrows the weight pointers;
+ * makes no HIP call. */
+int qgemv_stack_create(const qgemv_run_spec* runs, int32_t n_runs, int64_t ldy, qgemv_stack_t* out);
+
+/* y[i*ldy + c] for every member column c and window row i < m, in one
+ * dispatch; x bf16 [m][k]; m 0..16 (0: nothing launched); epi as qgemv_run.
+ * y must not overlap x or any run's weights (QGEMV_E_ALIAS). */
+int qgemv_stack_run(qgemv_stack_t s, const uint16_t* x, int32_t m, float* y, int32_t epi, void* stream);
+
+/* Free the host-side stack handle. NULL is a no-op. */
+void qgemv_stack_destroy(qgemv_stack_t s);
+
 /* Launch geometry fixed at create (for tests and reports):
  *   out[0] lanes per output column, out[1] output columns per wave,
  *   out[2] codes per lane chunk, out[3] threads per block,

@@ -132,3 +132,36 @@ def test_valid_run_without_a_device_reports_hip(handle):
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert qgemv.qgemv_run(handle, X, 1, Y, 0, 0) == qgemv.QGEMV_E_HIP
+
+
+def _run(bits, group, n, k, members, w=W):
+    return dict(bits=bits, group=group, n=n, k=k, w=w, scales=S, biases=B, members=members)
+
+
+def test_stack_create_rules():
+    ok = [_run(4, 64, 2048, 2048, [(2048, 0)]), _run(5, 128, 6192, 2048, [(6144, 2048), (48, 8192)]),
+          _run(6, 64, 48, 2048, [(48, 8240)])]
+    rc, h = qgemv.qgemv_stack_create(ok, 8288)
+    assert rc == 0, qgemv.qgemv_strerror(rc)
+    # m == 0 launches nothing; refusals before any HIP call
+    assert qgemv.qgemv_stack_run(h, X, 0, Y, 0, 0) == qgemv.QGEMV_OK
+    assert qgemv.qgemv_stack_run(h, X, 17, Y, 0, 0) == qgemv.QGEMV_E_WINDOW
+    assert qgemv.qgemv_stack_run(h, X + 8, 1, Y, 0, 0) == qgemv.QGEMV_E_ALIGN
+    assert qgemv.qgemv_stack_run(h, X, 1, X, 0, 0) == qgemv.QGEMV_E_ALIAS
+    assert qgemv.qgemv_stack_run(None, X, 1, Y, 0, 0) == qgemv.QGEMV_E_ARG
+    qgemv.qgemv_stack_destroy(h)
+    bad = [
+        ([_run(4, 64, 2048, 2048, [(2048, 0)]), _run(6, 64, 48, 1024, [(48, 4000)])], 8288, qgemv.QGEMV_E_SHAPE),
+        ([_run(4, 64, 2048, 2048, [(2000, 0)])], 8288, qgemv.QGEMV_E_SHAPE),            # rows do not sum
+        ([_run(4, 64, 2048, 2048, [(2048, 7000)])], 8288, qgemv.QGEMV_E_STRIDE),        # past the row
+        ([_run(4, 64, 2048, 2048, [(2048, 0)]), _run(6, 64, 48, 2048, [(48, 2000)])], 8288,
+         qgemv.QGEMV_E_ALIAS),                                                         # columns overlap
+        ([_run(7, 64, 2048, 2048, [(2048, 0)])], 8288, qgemv.QGEMV_E_BITS),
+        ([_run(4, 64, 16, 2080, [(16, 0)])], 8288, qgemv.QGEMV_E_SHAPE),                # group does not divide K
+        ([_run(4, 32, 16, 96, [(16, 0)])], 8288, qgemv.QGEMV_E_NOKERNEL),               # no 16-lane chunks
+        ([], 8288, qgemv.QGEMV_E_ARG),
+        ([_run(4, 64, 64, 2048, [(64, 0)])] * 9, 1 << 20, qgemv.QGEMV_E_ARG),           # too many runs
+    ]
+    for runs, ldy, want in bad:
+        rc, h = qgemv.qgemv_stack_create(runs, ldy)
+        assert rc == want and h is None, (runs[:1], qgemv.qgemv_strerror(rc))

@@ -364,3 +364,68 @@ def test_indexed_small_stack_repeats_and_duplicates():
             ex = int(idx[i, s])
             v = qgemv.Matrix(bits, group, n, k, tw[ex], ts[ex], tb[ex])
             assert bits_equal(run(v, xt[i:i + 1])[0], y[i, s]), (i, s)
+
+
+# ---------------------------------------------------------------------------
+# fused stacks: one dispatch, each member equal to its run's strided call
+# ---------------------------------------------------------------------------
+
+def _stack_runs(specs, k, seed):
+    """specs: [(bits, group, [(rows, col), ...])]; returns runs for qgemv.Stack
+    plus the host copies."""
+    runs, host = [], []
+    for i, (bits, group, members) in enumerate(specs):
+        n = sum(r for r, _ in members)
+        d = synth.matrix(seed + i, bits, group, n, k)
+        host.append(d)
+        runs.append(dict(bits=bits, group=group, n=n, k=k, w=dev(d["words"]), scales=dev(d["scales"]),
+                         biases=dev(d["biases"]), members=members))
+    return runs, host
+
+
+def _check_stack(specs, k, ldy, m, seed, epi=0):
+    runs, host = _stack_runs(specs, k, seed)
+    rng = np.random.default_rng(seed)
+    x = synth.draw_x(rng, m, k)
+    xt = dev(x)
+    st = qgemv.Stack(runs, ldy)
+    sentinel = torch.full((m, ldy), 0x7FC0BEEF, dtype=torch.int32, device=DEV)
+    y = sentinel.clone().view(torch.float32)
+    st.run(xt, y.view(-1), epi=epi)
+    covered = torch.zeros((m, ldy), dtype=torch.bool, device=DEV)
+    for r, d in zip(runs, host):
+        mat = qgemv.Matrix(r["bits"], r["group"], r["n"], k, r["w"], r["scales"], r["biases"])
+        plain = run(mat, xt, epi=epi)
+        row0 = 0
+        for rows, col in r["members"]:
+            assert bits_equal(y[:, col:col + rows], plain[:, row0:row0 + rows]), (r["bits"], col)
+            covered[:, col:col + rows] = True
+            row0 += rows
+        y64, a64, _ = oracle.gemv(d["words"], d["scales"], d["biases"], x, r["bits"], r["group"], r["n"], k,
+                                  threads=THREADS)
+        if not epi:
+            check_bound(plain.cpu().numpy(), y64, a64, k, f"stack run {r['bits']}/{r['group']}")
+    assert torch.equal(y.view(torch.int32)[~covered], sentinel[~covered])
+
+
+@pytest.mark.parametrize("m", [1, 16])
+def test_fused_stack_config(m):
+    """The stack workload in one dispatch: 4/64 x 2048 at column 0, the 5/128
+    run of two members (6144 + 48) at 2048, 6/64 x 48 at 8240; ldy 8288."""
+    print_case("fused stack", m)
+    specs = [(4, 64, [(2048, 0)]), (5, 128, [(6144, 2048), (48, 8192)]), (6, 64, [(48, 8240)])]
+    _check_stack(specs, synth.STACK_K, synth.STACK_LDY, m, 3100 + m)
+
+
+def test_fused_stack_column_map_gaps():
+    """Members of one run placed apart, runs interleaved, gaps untouched."""
+    specs = [(5, 128, [(6144, 2100), (48, 8400)]), (4, 64, [(2048, 0)]), (6, 64, [(48, 8300)])]
+    _check_stack(specs, 2048, 9000, 3, 3200)
+
+
+@pytest.mark.parametrize("epi", [0, 1])
+def test_fused_stack_all_widths(epi):
+    """Every width in one stack, members of different sizes, K = 4096."""
+    specs = [(2, 32, [(300, 5000)]), (3, 64, [(128, 0), (72, 4000)]), (4, 128, [(512, 200)]),
+             (5, 32, [(64, 712)]), (6, 128, [(1000, 3000)]), (8, 64, [(256, 776), (16, 1100)])]
+    _check_stack(specs, 4096, 5400, 5, 3300 + epi, epi)
