@@ -76,12 +76,16 @@ def read_traffic(workload: str):
         return None
 
 
+ARITH_NAMES = {1: "dot", 2: "mfma"}
+
+
 class Workload:
     """Device inputs of one workload plus rotating weight copies."""
 
-    def __init__(self, name: str, m: int, torch, qgemv, synth):
+    def __init__(self, name: str, m: int, torch, qgemv, synth, arith: int = 0):
         self.name, self.m = name, m
         self.torch, self.qgemv = torch, qgemv
+        self.arith = arith
         dev = "cuda"
 
         def t(a):
@@ -155,12 +159,15 @@ class Workload:
                 continue
             for (w, s, b), run_ in zip(trip_list, self.runs if self.kind != "indexed" else [None]):
                 if self.kind == "indexed":
-                    mats.append(qgemv.Matrix(4, 64, self.n_each, self.k, w, s, b, n_experts=self.n_experts))
+                    mats.append(qgemv.Matrix(4, 64, self.n_each, self.k, w, s, b, n_experts=self.n_experts,
+                                             arith=arith))
                 else:
                     bits, group, n = run_
-                    mats.append(qgemv.Matrix(bits, group, n, self.k, w, s, b))
+                    mats.append(qgemv.Matrix(bits, group, n, self.k, w, s, b, arith=arith))
             self.copies.append((trip_list, mats))
         self.flat = self.y.view(-1)
+        first = self.copies[0][1][0]
+        self.arith_used = "dot" if self.kind == "fused" else ARITH_NAMES[first.arith]
 
     def step(self, i: int, stream: int):
         _, mats = self.copies[i % len(self.copies)]
@@ -249,6 +256,8 @@ def main():
     ap.add_argument("--m", type=int, default=1, help="window rows")
     ap.add_argument("--all", action="store_true", help="also time the other workloads and windows")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--arith", default="auto", choices=["auto", "dot", "mfma"],
+                    help="arithmetic of the handles (the fused stack always uses the library's choice)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (known bytes) for counter scaling")
     args = ap.parse_args()
@@ -274,7 +283,8 @@ def main():
 
     qgemv.load()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    wl = Workload(args.workload, args.m, torch, qgemv, synth)
+    arith = {"auto": 0, "dot": 1, "mfma": 2}[args.arith]
+    wl = Workload(args.workload, args.m, torch, qgemv, synth, arith)
     ms, batches = time_workload(wl, args.steps, args.warmup, torch)
     gbs = wl.bytes / (ms * 1e-3) / 1e9
     traffic = read_traffic(f"{args.workload}_m{wl.m}")
@@ -293,7 +303,7 @@ def main():
         "data": "synthetic (seeded uniform codes, bf16 scales/biases/activations)",
         "config": {"workload": wl.desc, "m": wl.m, "k": wl.k, "algorithmic_bytes": wl.bytes,
                    "weight_copies": len(wl.copies), "parallelism": "single GPU",
-                   "arithmetic": "exact codes as bf16, bf16 activations, fp32 sums"},
+                   "arithmetic": f"exact codes as bf16, bf16 activations, fp32 sums ({wl.arith_used} form)"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_GBS, 4), "traffic": traffic},
         "batch_ms": [round(b, 6) for b in batches],
@@ -301,15 +311,21 @@ def main():
     }
     if args.all:
         extra = {}
-        for name, m in [("lmhead", 1), ("lmhead", 8), ("lmhead", 16), ("stack", 1), ("stack", 16),
-                        ("stack3", 1), ("stack3", 16), ("experts", 16)]:
-            if name == args.workload and m == wl.m:
+        for name, m, ar in [("lmhead", 1, arith), ("lmhead", 8, arith), ("lmhead", 16, arith),
+                            ("lmhead", 1, 1), ("lmhead", 8, 1), ("lmhead", 16, 1),
+                            ("lmhead", 1, 2), ("lmhead", 8, 2), ("lmhead", 16, 2),
+                            ("stack", 1, arith), ("stack", 16, arith), ("stack3", 1, arith), ("stack3", 16, arith),
+                            ("experts", 16, arith), ("experts", 16, 1), ("experts", 16, 2)]:
+            w2 = Workload(name, m, torch, qgemv, synth, ar)
+            key = f"{name}_m{w2.m}_{w2.arith_used}"
+            if key in extra or (name == args.workload and m == wl.m and w2.arith_used == wl.arith_used):
+                del w2
                 continue
-            w2 = Workload(name, m, torch, qgemv, synth)
             ms2, _ = time_workload(w2, max(50, args.steps // 2), args.warmup, torch)
             g2 = w2.bytes / (ms2 * 1e-3) / 1e9
-            extra[f"{name}_m{w2.m}"] = {"us_per_call": round(ms2 * 1e3, 3), "GB/s": round(g2, 1),
-                                        "frac": round(g2 / PEAK_GBS, 4), "bytes": w2.bytes}
+            extra[key] = {"us_per_call": round(ms2 * 1e3, 3), "GB/s": round(g2, 1),
+                          "frac": round(g2 / PEAK_GBS, 4), "bytes": w2.bytes}
+            print(f"# {key}: {ms2 * 1e3:.3f} us, {g2:.1f} GB/s", file=sys.stderr, flush=True)
             del w2
             torch.cuda.empty_cache()
         out["workloads"] = extra

@@ -70,6 +70,7 @@ struct qgemv_handle {
   int lpr, cpl, nchunks; // lanes per column, chunks per lane, chunks per row
   int vec_groups;        // scales/biases aligned for packed loads
   int64_t wpr, gpr;
+  int arith;             // QGEMV_ARITH_DOT or QGEMV_ARITH_MFMA
   const qg::Entry* entry;
   // resident blocks per CU of each (window variant, staging) kernel, 0 =
   // not yet known; a benign cache: every thread that fills it writes the
@@ -99,7 +100,7 @@ void init_device(DeviceInfo* info) {
     for (int gi = 0; gi < 3; ++gi) {
       const qg::Entry& e = qg::entry(bi, gi);
       for (int v = 0; v < 5; ++v)
-        for (qg::KernelFn fn : {e.fast[v][0], e.fast[v][1], e.generic[v]})
+        for (qg::KernelFn fn : {e.fast[v][0], e.fast[v][1], e.generic[v], e.mfma[v]})
           if (fn && hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                         hipFuncAttributeMaxDynamicSharedMemorySize,
                                         static_cast<int>(qg::kMaxDynamicLds)) != hipSuccess)
@@ -147,6 +148,29 @@ size_t lds_bytes(const qgemv_handle* h, int var, int stage) {
   return b;
 }
 
+// The matrix-core kernels' LDS: the staged window (rows of k/32 units x 64
+// bytes + 16 padding, a zero line, unit sums), the routed list of an indexed
+// call, and a ring of D load-group slots per wave (2 <= D <= 8).  D is the
+// deepest ring that fits half the CU (two blocks per CU) for windows up to
+// 4 rows, else the whole CU.  Returns false when not even two slots fit.
+bool mfma_plan(const qgemv_handle* h, int var, bool indexed, int* depth, size_t* lds) {
+  const size_t mb = static_cast<size_t>(qg::kWindows[var]);
+  const size_t units = static_cast<size_t>(h->d.k) / 32;
+  const size_t fixed = mb * (units * 64 + 16) + 64 + mb * units * 4 + (indexed ? qg::kMaxList * 4 : 0);
+  const size_t per_slot = static_cast<size_t>(qg::kMWaves) * h->entry->mfma_slot;
+  size_t dmax = static_cast<size_t>(h->entry->mfma_dmax);
+  if (dmax > 8) dmax = 8;
+  for (size_t budget : {var <= 2 ? size_t{76 * 1024} : qg::kMaxDynamicLds, qg::kMaxDynamicLds}) {
+    if (fixed + 2 * per_slot > budget) continue;
+    size_t d = (budget - fixed) / per_slot;
+    if (d > dmax) d = dmax;
+    *depth = static_cast<int>(d);
+    *lds = fixed + d * per_slot;
+    return true;
+  }
+  return false;
+}
+
 int check_y_alias(const qgemv_handle* h, const void* y, size_t ybytes, const void* x, size_t xbytes,
                   const void* idx, size_t idxbytes) {
   const size_t E = static_cast<size_t>(h->d.n_experts);
@@ -163,17 +187,40 @@ int launch(const qgemv_handle* h, const uint16_t* x, int32_t m, float* y, int64_
   const DeviceInfo* dev = current_device();
   if (!dev) return QGEMV_E_HIP;
   const int indexed = idx != nullptr;
-  const int var = indexed ? window_variant(qg::kIndexedWindow) : window_variant(m);
+  int var = indexed ? window_variant(qg::kIndexedWindow) : window_variant(m);
   // hand-off staging for 3/5/6 bits when it fits; the direct mode gives the
   // same bits with more scattered loads
   int stage = (h->fast && h->ppc > 1) ? 1 : 0;
   if (stage && lds_bytes(h, var, 1) > qg::kMaxDynamicLds) stage = 0;
-  const size_t lds = lds_bytes(h, var, stage);
+  const bool mfma = h->arith == QGEMV_ARITH_MFMA;
+  int depth = 0;
+  size_t lds = 0;
+  if (mfma) {
+    stage = 0;
+    // A window too wide for one block's LDS runs as passes of a narrower
+    // variant over the same tiles: each output of the matrix-core form
+    // depends only on its own window row, so the bits are the same.
+    while (!mfma_plan(h, var, indexed, &depth, &lds)) {
+      if (var == 0) return QGEMV_E_WINDOW;
+      --var;
+    }
+  } else {
+    lds = lds_bytes(h, var, stage);
+  }
   if (lds > qg::kMaxDynamicLds) return QGEMV_E_WINDOW;
-  const qg::KernelFn fn = h->fast ? h->entry->fast[var][stage] : h->entry->generic[var];
-  const int R = h->fast ? h->entry->fast_rows[var] : h->entry->generic_rows[var];
-  const int slots_per_wave = qg::kWave / h->lpr;
-  const int64_t tile_rows = static_cast<int64_t>(qg::kWaves) * slots_per_wave * R;
+  qg::KernelFn fn = h->fast ? h->entry->fast[var][stage] : h->entry->generic[var];
+  int threads = qg::kThreads;
+  int64_t tile_rows = 0;
+  if (mfma) {
+    // one wave per 16 output columns
+    fn = h->entry->mfma[var];
+    threads = qg::kMThreads;
+    tile_rows = static_cast<int64_t>(qg::kMWaves) * 16;
+  } else {
+    const int R = h->fast ? h->entry->fast_rows[var] : h->entry->generic_rows[var];
+    const int slots_per_wave = qg::kWave / h->lpr;
+    tile_rows = static_cast<int64_t>(qg::kWaves) * slots_per_wave * R;
+  }
   const int64_t tiles = (h->d.n + tile_rows - 1) / tile_rows;
 
   qg::Params p{};
@@ -193,7 +240,7 @@ int launch(const qgemv_handle* h, const uint16_t* x, int32_t m, float* y, int64_
   p.n_experts = h->d.n_experts;
   p.epi = epi;
   p.lpr = h->lpr;
-  p.cpl = h->cpl;
+  p.cpl = mfma ? depth : h->cpl;   // the matrix-core kernels read their ring depth here
   p.nchunks = h->nchunks;
   p.tiles = static_cast<int32_t>(tiles);
   p.indexed = indexed;
@@ -209,7 +256,7 @@ int launch(const qgemv_handle* h, const uint16_t* x, int32_t m, float* y, int64_
   int occ = h->occupancy[var][stage].load(std::memory_order_relaxed);
   if (occ == 0) {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(fn), qg::kThreads,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(fn), threads,
                                                      lds) != hipSuccess || nb < 1)
       nb = 1;
     occ = nb;
@@ -226,7 +273,7 @@ int launch(const qgemv_handle* h, const uint16_t* x, int32_t m, float* y, int64_
     grid.x = static_cast<unsigned>(per);
     grid.y = static_cast<unsigned>(h->d.n_experts);
   }
-  hipLaunchKernelGGL(fn, grid, dim3(qg::kThreads), lds, static_cast<hipStream_t>(stream), p);
+  hipLaunchKernelGGL(fn, grid, dim3(threads), lds, static_cast<hipStream_t>(stream), p);
   return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_E_HIP;
 }
 
@@ -251,8 +298,23 @@ const char* qgemv_strerror(int status) {
   return "QGEMV_E_UNKNOWN";
 }
 
-int qgemv_create(const qgemv_desc* d, qgemv_t* out) {
+int qgemv_create(const qgemv_desc* d, qgemv_t* out) { return qgemv_create_arith(d, QGEMV_ARITH_AUTO, out); }
+
+int64_t qgemv_mfma_codes(int32_t bits, int32_t group) {
+  const int bi = qg::bits_index(bits), gi = qg::group_index(group);
+  if (bi < 0 || gi < 0) return 0;
+  // one load group of 128-code rounds per step; with one round per group at
+  // group 128 the scale loads take the aligned dword of two groups, so a row
+  // holds an even number of groups
+  const int64_t codes = 128 * static_cast<int64_t>(qg::entry(bi, gi).mfma_group);
+  return (group == 128 && codes == 128) ? 256 : codes;
+}
+
+int qgemv_arith(qgemv_t h) { return h ? h->arith : QGEMV_E_ARG; }
+
+int qgemv_create_arith(const qgemv_desc* d, int32_t arith, qgemv_t* out) {
   if (!d || !out) return QGEMV_E_ARG;
+  if (arith != QGEMV_ARITH_AUTO && arith != QGEMV_ARITH_DOT && arith != QGEMV_ARITH_MFMA) return QGEMV_E_ARG;
   const int bi = qg::bits_index(d->bits);
   if (bi < 0) return QGEMV_E_BITS;
   const int gi = qg::group_index(d->group);
@@ -297,15 +359,32 @@ int qgemv_create(const qgemv_desc* d, qgemv_t* out) {
   while (lpr < 64 && h.nchunks % (lpr * 2) == 0) lpr *= 2;
   h.lpr = lpr;
   h.cpl = h.nchunks / lpr;
+  // arithmetic: the dot form unless the matrix cores are asked for
+  const uintptr_t sb = reinterpret_cast<uintptr_t>(d->scales) | reinterpret_cast<uintptr_t>(d->biases);
+  const bool mfma_ok = d->k % qgemv_mfma_codes(d->bits, d->group) == 0 &&
+                       sb % static_cast<uintptr_t>(h.entry->mfma_salign) == 0;
+  if (arith == QGEMV_ARITH_MFMA && !mfma_ok) return QGEMV_E_NOKERNEL;
+  h.arith = arith == QGEMV_ARITH_MFMA ? QGEMV_ARITH_MFMA : QGEMV_ARITH_DOT;
   {
-    const int cpc_eff = h.cpc;
-    const int gspan = cpc_eff >= d->group ? cpc_eff / d->group : 1;
+    // groups one packed scale load spans: a lane chunk's, or a 128-code
+    // macro step's for the matrix-core form
+    const int span_codes = h.arith == QGEMV_ARITH_MFMA ? 128 : h.cpc;
+    const int gspan = span_codes >= d->group ? span_codes / d->group : 1;
     const uintptr_t a = reinterpret_cast<uintptr_t>(d->scales) | reinterpret_cast<uintptr_t>(d->biases);
     h.vec_groups = (a % (2 * gspan) == 0) && (h.gpr % gspan == 0);
   }
   // The one-row window must fit in LDS; wider windows are refused at run
-  // time when theirs does not (QGEMV_E_WINDOW).
-  if (lds_bytes(&h, 0, 0) > qg::kMaxDynamicLds) return QGEMV_E_SHAPE;
+  // time when theirs does not (QGEMV_E_WINDOW), or, in the matrix-core
+  // form, run as passes of fewer rows.
+  if (h.arith == QGEMV_ARITH_MFMA) {
+    int depth = 0;
+    size_t lds = 0;
+    if (!mfma_plan(&h, 0, false, &depth, &lds)) {
+      if (arith == QGEMV_ARITH_MFMA) return QGEMV_E_NOKERNEL;
+      h.arith = QGEMV_ARITH_DOT;
+    }
+  }
+  if (h.arith == QGEMV_ARITH_DOT && lds_bytes(&h, 0, 0) > qg::kMaxDynamicLds) return QGEMV_E_SHAPE;
   *out = hp.release();
   return QGEMV_OK;
 }
@@ -540,12 +619,21 @@ int qgemv_stack_run(qgemv_stack_t s, const uint16_t* x, int32_t m, float* y, int
 
 int qgemv_query(qgemv_t h, int64_t out[6]) {
   if (!h || !out) return QGEMV_E_ARG;
-  const int R = h->fast ? h->entry->fast_rows[0] : h->entry->generic_rows[0];
-  out[0] = h->lpr;
-  out[1] = (qg::kWave / h->lpr) * R;
-  out[2] = h->cpc;
-  out[3] = qg::kThreads;
-  out[4] = static_cast<int64_t>(qg::kWaves) * (qg::kWave / h->lpr) * R;
+  if (h->arith == QGEMV_ARITH_MFMA) {
+    // four lanes per column (one 32-code unit each), 16 columns per wave
+    out[0] = 4;
+    out[1] = 16;
+    out[2] = 32;
+    out[3] = qg::kMThreads;
+    out[4] = static_cast<int64_t>(qg::kMWaves) * 16;
+  } else {
+    const int R = h->fast ? h->entry->fast_rows[0] : h->entry->generic_rows[0];
+    out[0] = h->lpr;
+    out[1] = (qg::kWave / h->lpr) * R;
+    out[2] = h->cpc;
+    out[3] = qg::kThreads;
+    out[4] = static_cast<int64_t>(qg::kWaves) * (qg::kWave / h->lpr) * R;
+  }
   const DeviceInfo* dev = current_device();
   out[5] = dev ? dev->cus : 0;
   return QGEMV_OK;

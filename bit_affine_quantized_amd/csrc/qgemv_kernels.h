@@ -240,11 +240,12 @@ __device__ __forceinline__ float apply_epi(float v, int epi) {
 
 // Block-wide list of the (row, slot) pairs routed to `expert`, in index
 // order.  Returns the count.
+template <int NT = kThreads>
 __device__ inline int build_route_list(const int32_t* __restrict__ idx, int total, int expert,
                                 int* list, int* wave_cnt) {
   const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
   int base_count = 0;
-  for (int base = 0; base < total; base += kThreads) {
+  for (int base = 0; base < total; base += NT) {
     const int t = base + tid;
     const bool hit = t < total && idx[t] == expert;
     const uint64_t mask = __ballot(hit);
@@ -257,7 +258,7 @@ __device__ inline int build_route_list(const int32_t* __restrict__ idx, int tota
       list[before + __popcll(lower)] = t;
     }
     int all = 0;
-    for (int i = 0; i < kWaves; ++i) all += wave_cnt[i];
+    for (int i = 0; i < NT / kWave; ++i) all += wave_cnt[i];
     __syncthreads();
     base_count += all;
   }
@@ -932,6 +933,403 @@ __global__ __launch_bounds__(kThreads) void qrow_fast(const Params p) {
 }
 
 // ---------------------------------------------------------------------------
+// MFMA kernel: v_mfma_f32_16x16x32_bf16 with a block-diagonal activation
+// operand.
+//
+// A wave owns 16 output columns and walks K in rounds of 128 codes per
+// column.  In a round, lane l (column j = l % 16, quarter q = l / 16) holds
+// the 32-code unit q of its column as exact bf16 pairs in the unpack's slot
+// order.  MFMA step s (0..3) feeds slots 8s..8s+7 of every lane's unit as
+// the B operand (k-index 8q + e of column j).  Row i = 4m + q' of the A
+// operand holds window row m's activations of unit q' in k-indices
+// 8q'..8q'+7 and zeros elsewhere, so after the four steps D[4m + q'][j] is
+// the fp32 dot of unit q' of column j with window row m, every product
+// exact.  Lane l holds D[4(l/16) + q'][l % 16] for q' = 0..3 (one window
+// row, one column, four units) and folds them in unit order:
+// P = fma(s, D, P); P = fma(bias, X, P).  No lane reduction follows, and
+// each output depends only on its own window row's activations, wherever the
+// row sits in the window.
+//
+// Weights, scales and biases reach LDS straight from HBM: buffer loads with
+// the LDS bit put lane L's bytes at the wave's slot + L * size.  A slot holds
+// one group of R rounds, R chosen so that a column's share of a group is L
+// whole 128-byte lines; each group of 8 lanes of a load fetches one whole
+// line, because a streaming line asked for by two different loads is read
+// from HBM twice.  Lines sit in the slot line-major ([line][column]) with
+// the 8 pieces of column c's line rotated by c / 2, so the 16 lanes that
+// read the same piece of 16 columns hit 16 different bank groups.  The slots
+// form a ring of D groups private to the wave, loaded D - 1 groups ahead;
+// every group issues the same number of loads, so an s_waitcnt on the
+// vector-memory counter that leaves the later groups in flight marks a
+// group ready.
+// ---------------------------------------------------------------------------
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+template <int B, int G> struct MGroup {
+  static constexpr int R = B == 8 ? 1 : (B == 4 ? 2 : ((B == 2 || B == 6) ? 4 : 8));  // rounds per group
+  static constexpr int L = R * B / 8;              // 128-byte lines per column per group
+  static constexpr int WDMA = 2 * L;               // weight loads per group (8 lines each)
+  static constexpr int SB = 256 * R / G;           // scale bytes per column per group
+  static constexpr bool S16 = SB % 16 == 0;        // scales as 16-byte pieces, else dwords
+  static constexpr int SBP = SB < 4 ? 4 : SB;      // bytes kept per column (the aligned dword when 2)
+  static constexpr int SLANES = 16 * SBP / (S16 ? 16 : 4);   // lanes of one scale load
+  static constexpr int NDMA = WDMA + 2;            // loads per group
+  static constexpr int WBYTES = 16 * L * 128;
+  static constexpr int SLOT = WBYTES + 2 * 16 * SBP;
+  static constexpr int DMAX = 63 / NDMA + 1;       // ring depth the load counter can track
+  static constexpr int CH = (B % 4 == 0) ? 4 : ((B % 2 == 0) ? 2 : 1);   // words per LDS read
+  static_assert(R * B % 8 == 0 && SLANES <= 64, "group geometry");
+};
+
+constexpr int kMWaves = 4;                       // waves per block of the MFMA kernels
+constexpr int kMThreads = kMWaves * kWave;
+
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Wait until at most `ahead` groups of NDMA loads are still in flight.
+template <int NDMA>
+__device__ __forceinline__ void wait_groups(int ahead) {
+  switch (ahead) {
+#define QG_W(A)                                   \
+  case A:                                         \
+    if constexpr ((A) * NDMA <= 63) {             \
+      vm_wait<(A) * NDMA>();                      \
+    } else {                                      \
+      vm_wait<0>();                               \
+    }                                             \
+    break;
+    QG_W(0) QG_W(1) QG_W(2) QG_W(3) QG_W(4) QG_W(5) QG_W(6) QG_W(7)
+#undef QG_W
+    default: vm_wait<0>(); break;
+  }
+}
+
+template <int SIZE>
+__device__ __forceinline__ void lds_dma(__amdgpu_buffer_rsrc_t r, unsigned char* lds, int voff, int soff) {
+  if constexpr (SIZE == 16) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, soff, 0, kNt);
+  } else {
+    static_assert(SIZE == 4, "load size");
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 4, voff, soff, 0, kNt);
+  }
+}
+
+// p.cpl carries the ring depth D (groups per wave, at least 2) chosen by the host.
+template <int B, int G, int MB>
+__device__ __forceinline__ void mfma_body(const Params& p, const int bx, const int gx, unsigned char* smem,
+                                          int* s_wave_cnt, int* s_xrow, int64_t* s_yoff) {
+  using MG = MGroup<B, G>;
+  constexpr int R = MG::R, CH = MG::CH;
+  constexpr int NMB = (MB + 3) / 4;         // 4-row blocks of the window
+
+  const int units = static_cast<int>(p.k / 32);
+  const int groups = units / (4 * R);       // groups per tile
+  const int mrows = p.indexed ? MB : min(p.m, MB);       // window rows staged
+  const int xstride = units * 64 + 16;                     // bytes per staged row
+  const int D = p.cpl;
+  // LDS: activations [mrows][units][32 slots] bf16 (rows padded by 16 bytes
+  // so a 4 x 4 block of reads hits distinct banks), a 64-byte zero line
+  // (the A operand of lanes outside the block diagonal), unit sums
+  // [mrows][units] fp32, the routed list (indexed calls), then the rings.
+  unsigned char* xs = smem;
+  unsigned char* zero_line = smem + static_cast<size_t>(mrows) * xstride;
+  float* xsum = reinterpret_cast<float*>(zero_line + 64);
+  int* s_list = reinterpret_cast<int*>(xsum + static_cast<size_t>(mrows) * units);
+  unsigned char* rings = reinterpret_cast<unsigned char*>(s_list + (p.indexed ? kMaxList : 0));
+
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int j = lane % 16, qd = lane / 16;
+  unsigned char* ring = rings + static_cast<size_t>(wv) * D * MG::SLOT;
+
+  int expert = 0;
+  int total = p.m;
+  if (p.indexed) {
+    expert = blockIdx.y;
+    total = build_route_list<kMThreads>(p.idx, p.m * p.slots, expert, s_list, s_wave_cnt);
+    if (total == 0) return;
+  }
+  const int n = static_cast<int>(p.n);
+  const int64_t row_bytes = p.wpr * 4;
+  const int gpr2 = static_cast<int>(p.gpr) * 2;
+  const unsigned char* wexp = reinterpret_cast<const unsigned char*>(p.w) + static_cast<int64_t>(expert) * p.n * row_bytes;
+  const unsigned char* sexp = reinterpret_cast<const unsigned char*>(p.scales) + static_cast<int64_t>(expert) * p.n * gpr2;
+  const unsigned char* bexp = reinterpret_cast<const unsigned char*>(p.biases) + static_cast<int64_t>(expert) * p.n * gpr2;
+  const int my_tiles = bx < p.tiles ? (p.tiles - 1 - bx) / gx + 1 : 0;
+  const int steps = my_tiles * groups;
+  const __amdgpu_buffer_rsrc_t yres = make_rsrc(p.y, p.y_bytes);
+
+  // ---- per-lane constants of the loads and reads (the same for every group) ----
+  // weight load t: lanes 8a..8a+7 fetch line lam = 8t + a of the slot, which
+  // is line lam / 16 of column lam % 16's share; lane 8a + e brings piece
+  // (e - c/2) mod 8 of it, so piece pp of column c's line sits at e = (pp + c/2) mod 8
+  int w_voff[MG::WDMA];
+#pragma unroll
+  for (int t = 0; t < MG::WDMA; ++t) {
+    const int lam = 8 * t + lane / 8, c = lam % 16, ln = lam / 16;
+    const int pp = (lane % 8 - c / 2) & 7;
+    w_voff[t] = static_cast<int>(c * row_bytes) + ln * 128 + pp * 16;
+  }
+  // scale (bias) load: lane L < SLANES brings piece (or dword) L % per of
+  // column L / per, per = SBP / size
+  constexpr int SSZ = MG::S16 ? 16 : 4;
+  constexpr int SPER = MG::SBP / SSZ;
+  const bool s_live = lane < MG::SLANES;
+  const int s_voff = (lane / SPER) * gpr2 + (lane % SPER) * SSZ;
+  // this lane's unit words in round r: word w = r*4B + qd*B + h of column
+  // j's share sits at piece w / 4 -> line (w/4) / 8, piece (w/4) % 8
+  auto word_off = [&](int w) {
+    const int pc = w / 4, ln = pc / 8, pp = pc % 8;
+    return ((ln * 16 + j) * 8 + ((pp + j / 2) & 7)) * 16 + (w % 4) * 4;
+  };
+  int r_off[R][B / CH];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int h = 0; h < B / CH; ++h) r_off[r][h] = word_off(r * 4 * B + qd * B + h * CH);
+  const int s_off = MG::WBYTES + j * MG::SBP;
+  const int b_off = s_off + 16 * MG::SBP;
+
+  // A step is one group of one tile; both cursors walk the steps in order:
+  // (tile index i, group gr, ring slot sl).
+  struct Cursor {
+    int st, i, gr, sl;
+  };
+  auto advance = [&](Cursor& c) {
+    ++c.st;
+    if (++c.gr == groups) {
+      c.gr = 0;
+      ++c.i;
+    }
+    if (++c.sl == D) c.sl = 0;
+  };
+  // issue every load of a step (or, past the last step, loads that read
+  // nothing, so each group still counts NDMA loads) into its ring slot
+  auto issue = [&](const Cursor& c) {
+    const bool real = c.st < steps;
+    const int c0 = ((bx + c.i * gx) * kMWaves + wv) * 16;
+    const int ncols = real ? n - c0 : 0;
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(wexp + static_cast<int64_t>(c0) * row_bytes,
+                                                static_cast<int64_t>(ncols) * row_bytes);
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(sexp + static_cast<int64_t>(c0) * gpr2,
+                                                static_cast<int64_t>(ncols) * gpr2);
+    const __amdgpu_buffer_rsrc_t br = make_rsrc(bexp + static_cast<int64_t>(c0) * gpr2,
+                                                static_cast<int64_t>(ncols) * gpr2);
+    unsigned char* slot = ring + c.sl * MG::SLOT;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the slot's last reads are done
+    const int wsoff = c.gr * (MG::L * 128);
+#pragma unroll
+    for (int t = 0; t < MG::WDMA; ++t) lds_dma<16>(wr, slot + t * 1024, w_voff[t], wsoff);
+    // this group's scales: SB bytes per column from byte gr*SB of the row
+    // (at SB = 2, the aligned dword that holds them)
+    const int ssoff = MG::SB < 4 ? ((c.gr * MG::SB) & ~3) : c.gr * MG::SB;
+    if (s_live) {
+      lds_dma<SSZ>(sr, slot + MG::WBYTES, s_voff, ssoff);
+      lds_dma<SSZ>(br, slot + MG::WBYTES + 16 * MG::SBP, s_voff, ssoff);
+    }
+  };
+
+  float acc[NMB];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) acc[mb] = 0.0f;
+  int mcount = 0;
+
+  auto compute = [&](const Cursor& c) {
+    const unsigned char* slot = ring + c.sl * MG::SLOT;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      uint32_t wu[B];
+#pragma unroll
+      for (int h = 0; h < B / CH; ++h) {
+        if constexpr (CH == 4) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(slot + r_off[r][h]);
+          wu[4 * h] = v.x;
+          wu[4 * h + 1] = v.y;
+          wu[4 * h + 2] = v.z;
+          wu[4 * h + 3] = v.w;
+        } else if constexpr (CH == 2) {
+          const u32x2 v = *reinterpret_cast<const u32x2*>(slot + r_off[r][h]);
+          wu[2 * h] = v.x;
+          wu[2 * h + 1] = v.y;
+        } else {
+          wu[h] = *reinterpret_cast<const uint32_t*>(slot + r_off[r][h]);
+        }
+      }
+      // scales and biases of the round's four units
+      float sv[4], bv[4];
+      if constexpr (G == 32) {
+        const u32x2 sg = *reinterpret_cast<const u32x2*>(slot + s_off + r * 8);
+        const u32x2 bg = *reinterpret_cast<const u32x2*>(slot + b_off + r * 8);
+        const uint32_t sw[2] = {sg.x, sg.y}, bw[2] = {bg.x, bg.y};
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) {
+          sv[q2] = group_value<4>(sw, q2);
+          bv[q2] = group_value<4>(bw, q2);
+        }
+      } else if constexpr (G == 64) {
+        const uint32_t sw = *reinterpret_cast<const uint32_t*>(slot + s_off + r * 4);
+        const uint32_t bw = *reinterpret_cast<const uint32_t*>(slot + b_off + r * 4);
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) {
+          sv[q2] = q2 >= 2 ? __uint_as_float(sw & 0xffff0000u) : __uint_as_float(sw << 16);
+          bv[q2] = q2 >= 2 ? __uint_as_float(bw & 0xffff0000u) : __uint_as_float(bw << 16);
+        }
+      } else {
+        // group index of this round within the kept bytes: r, or at SB = 2
+        // the half of the aligned dword
+        const int gi = MG::SB < 4 ? ((c.gr * R + r) & 1) : r;
+        const uint32_t sw = *reinterpret_cast<const uint32_t*>(slot + s_off + (gi / 2) * 4);
+        const uint32_t bw = *reinterpret_cast<const uint32_t*>(slot + b_off + (gi / 2) * 4);
+        const float s1 = (gi & 1) ? __uint_as_float(sw & 0xffff0000u) : __uint_as_float(sw << 16);
+        const float b1 = (gi & 1) ? __uint_as_float(bw & 0xffff0000u) : __uint_as_float(bw << 16);
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) {
+          sv[q2] = s1;
+          bv[q2] = b1;
+        }
+      }
+      const int unit0 = (c.gr * R + r) * 4;
+      // A operand of every 4-row block: lane (row ai = lane % 16, k-quarter
+      // qd) reads its row's activations when its quarter is its row's unit
+      // and the window row exists, else the zero line
+      u32x4 av[NMB][4];
+      f32x4_t xsv[NMB];
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+        if (4 * mb < mcount) {
+          const int ai = lane % 16, am = 4 * mb + ai / 4;
+          const bool live = (qd == ai % 4) && (am < mcount);
+          const unsigned char* abase = live ? xs + am * xstride + (unit0 + qd) * 64 : zero_line;
+#pragma unroll
+          for (int sidx = 0; sidx < 4; ++sidx)
+            av[mb][sidx] = *reinterpret_cast<const u32x4*>(abase + (live ? sidx * 16 : 0));
+          const int em = 4 * mb + qd;
+          xsv[mb] = *reinterpret_cast<const f32x4_t*>(xsum + static_cast<size_t>(em < mcount ? em : 0) * units + unit0);
+        }
+      }
+      // B operand: this lane's unit as 16 exact bf16 pairs
+      uint32_t qp[16];
+      unpack_codes<B, 32>(wu, qp);
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+        if (4 * mb < mcount) {
+          f32x4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int sidx = 0; sidx < 4; ++sidx) {
+            u32x4 bq;
+            bq.x = qp[4 * sidx];
+            bq.y = qp[4 * sidx + 1];
+            bq.z = qp[4 * sidx + 2];
+            bq.w = qp[4 * sidx + 3];
+            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[mb][sidx]),
+                                                        __builtin_bit_cast(bf16x8_t, bq), d, 0, 0, 0);
+          }
+          // lane = (window row 4mb + qd, column j): units q2 = 0..3 in order
+#pragma unroll
+          for (int q2 = 0; q2 < 4; ++q2) {
+            acc[mb] = __builtin_fmaf(sv[q2], d[q2], acc[mb]);
+            acc[mb] = __builtin_fmaf(bv[q2], xsv[mb][q2], acc[mb]);
+          }
+        }
+      }
+    }
+    if (c.gr == groups - 1) {
+      const int col = ((bx + c.i * gx) * kMWaves + wv) * 16 + j;
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+        const int em = 4 * mb + qd;
+        const bool ok = em < mcount && col < n;
+        const int off = ok ? static_cast<int>((s_yoff[ok ? em : 0] + mapped_column(p, col)) * 4) : 0x7ffffff0;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(apply_epi(acc[mb], p.epi)), yres, off, 0, 0);
+        acc[mb] = 0.0f;
+      }
+    }
+  };
+
+  for (int c0 = 0; c0 < total; c0 += MB) {
+    mcount = min(MB, total - c0);
+    // the first D-1 groups are in flight while the window is staged
+    Cursor ci = {0, 0, 0, 0}, cc = {0, 0, 0, 0};
+    for (int st = 0; st < D - 1; ++st) {
+      issue(ci);
+      advance(ci);
+    }
+    if (tid < mcount) {
+      const int e = c0 + tid;
+      if (p.indexed) {
+        const int t = s_list[e];
+        const int row = t / p.slots, sl = t % p.slots;
+        s_xrow[tid] = row;
+        s_yoff[tid] = (static_cast<int64_t>(row) * p.slots + sl) * p.n;
+      } else {
+        s_xrow[tid] = e;
+        s_yoff[tid] = static_cast<int64_t>(e) * p.ldy;
+      }
+    }
+    if (tid < 16) reinterpret_cast<uint32_t*>(zero_line)[tid] = 0u;
+    __syncthreads();
+    // ---- stage the window: each unit's activations in slot order, and its sum ----
+    for (int t = tid; t < mcount * units; t += kMThreads) {
+      const int mi = t / units, un = t - (t / units) * units;
+      const u32x4* src = reinterpret_cast<const u32x4*>(p.x + static_cast<int64_t>(s_xrow[mi]) * p.k +
+                                                        static_cast<int64_t>(un) * 32);
+      uint32_t xin[16];
+#pragma unroll
+      for (int pc = 0; pc < 4; ++pc) {
+        const u32x4 v = src[pc];
+        xin[4 * pc] = v.x;
+        xin[4 * pc + 1] = v.y;
+        xin[4 * pc + 2] = v.z;
+        xin[4 * pc + 3] = v.w;
+      }
+      float X = 0.0f;
+      const uint32_t ones = 0x3f803f80u;  // bf16 pair {1, 1}
+      u32x4* dst = reinterpret_cast<u32x4*>(xs + mi * xstride + un * 64);
+#pragma unroll
+      for (int pc = 0; pc < 4; ++pc) {
+        u32x4 o;
+        o.x = slot_pair<B>(xin, 4 * pc);
+        o.y = slot_pair<B>(xin, 4 * pc + 1);
+        o.z = slot_pair<B>(xin, 4 * pc + 2);
+        o.w = slot_pair<B>(xin, 4 * pc + 3);
+        X = dot2(o.x, ones, X);
+        X = dot2(o.y, ones, X);
+        X = dot2(o.z, ones, X);
+        X = dot2(o.w, ones, X);
+        dst[pc] = o;
+      }
+      xsum[mi * units + un] = X;
+    }
+    __syncthreads();
+    for (; cc.st < steps; advance(cc)) {
+      issue(ci);
+      advance(ci);
+      wait_groups<MG::NDMA>(D - 1);   // the group at cc has landed
+      compute(cc);
+    }
+    vm_wait<0>();       // no load may still be writing this wave's ring
+    __syncthreads();    // LDS window reused by the next pass of routed rows
+  }
+}
+
+template <int B, int G, int MB>
+__global__ __launch_bounds__(kMThreads) void qrow_mfma(const Params p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int s_wave_cnt[kMWaves];
+  __shared__ int s_xrow[QGEMV_MAX_WINDOW];
+  __shared__ int64_t s_yoff[QGEMV_MAX_WINDOW];
+  mfma_body<B, G, MB>(p, blockIdx.x, gridDim.x, smem, s_wave_cnt, s_xrow, s_yoff);
+}
+
+// ---------------------------------------------------------------------------
 // Fused stack: the runs of a fused projection (each a matrix of one width and
 // group whose members write their own output columns) in one dispatch.  The
 // blocks are split among the runs; each run executes exactly the body of its
@@ -1048,6 +1446,11 @@ struct Entry {
   KernelFn generic[5];  // by window variant: one-unit chunks, any lane count
   int fast_rows[5];     // columns per lane of the fast kernels
   int generic_rows[5];
+  KernelFn mfma[5];     // matrix-core kernels by window variant (kMThreads threads)
+  int mfma_slot;        // bytes of one ring slot (one load group of a wave)
+  int mfma_dmax;        // deepest ring the load counter can track
+  int mfma_group;       // 128-code rounds per load group (k is a multiple of 128 * this)
+  int mfma_salign;      // alignment the scale and bias arrays need (bytes)
 };
 
 template <int B, int G>
@@ -1080,6 +1483,15 @@ Entry make_entry() {
   e.generic_rows[2] = RowsPerLane<B, 4>::v;
   e.generic_rows[3] = RowsPerLane<B, 8>::v;
   e.generic_rows[4] = RowsPerLane<B, 16>::v;
+  e.mfma[0] = qrow_mfma<B, G, 1>;
+  e.mfma[1] = qrow_mfma<B, G, 2>;
+  e.mfma[2] = qrow_mfma<B, G, 4>;
+  e.mfma[3] = qrow_mfma<B, G, 8>;
+  e.mfma[4] = qrow_mfma<B, G, 16>;
+  e.mfma_slot = MGroup<B, G>::SLOT;
+  e.mfma_dmax = MGroup<B, G>::DMAX;
+  e.mfma_group = MGroup<B, G>::R;
+  e.mfma_salign = MGroup<B, G>::S16 ? 16 : 4;
   return e;
 }
 

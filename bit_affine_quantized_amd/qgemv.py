@@ -19,6 +19,7 @@ QGEMV_OK = 0
 QGEMV_E_ARG, QGEMV_E_BITS, QGEMV_E_GROUP, QGEMV_E_SHAPE, QGEMV_E_STRIDE = -1, -2, -3, -4, -5
 QGEMV_E_ALIGN, QGEMV_E_WINDOW, QGEMV_E_ALIAS, QGEMV_E_NOKERNEL, QGEMV_E_HIP = -6, -7, -8, -9, -10
 QGEMV_EPI_NONE, QGEMV_EPI_RELU2 = 0, 1
+QGEMV_ARITH_AUTO, QGEMV_ARITH_DOT, QGEMV_ARITH_MFMA = 0, 1, 2
 QGEMV_MAX_WINDOW = 16
 
 _lib = None
@@ -59,6 +60,12 @@ def load(path: str | None = None):
             p, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
             lib.qgemv_create.argtypes = [ctypes.POINTER(qgemv_desc), ctypes.POINTER(p)]
             lib.qgemv_create.restype = ctypes.c_int
+            lib.qgemv_create_arith.argtypes = [ctypes.POINTER(qgemv_desc), i32, ctypes.POINTER(p)]
+            lib.qgemv_create_arith.restype = ctypes.c_int
+            lib.qgemv_arith.argtypes = [p]
+            lib.qgemv_arith.restype = ctypes.c_int
+            lib.qgemv_mfma_codes.argtypes = [i32, i32]
+            lib.qgemv_mfma_codes.restype = ctypes.c_int64
             lib.qgemv_destroy.argtypes = [p]
             lib.qgemv_destroy.restype = None
             lib.qgemv_run.argtypes = [p, p, i32, p, i32, p]
@@ -112,6 +119,22 @@ def qgemv_create(bits, group, n, k, w, scales, biases, n_experts=1):
     h = ctypes.c_void_p()
     rc = load().qgemv_create(ctypes.byref(d), ctypes.byref(h))
     return rc, (h.value if rc == QGEMV_OK else None)
+
+
+def qgemv_create_arith(bits, group, n, k, w, scales, biases, arith, n_experts=1):
+    """As qgemv_create with the arithmetic chosen (QGEMV_ARITH_*)."""
+    d = qgemv_desc(bits, group, n, k, n_experts, _addr(w), _addr(scales), _addr(biases))
+    h = ctypes.c_void_p()
+    rc = load().qgemv_create_arith(ctypes.byref(d), arith, ctypes.byref(h))
+    return rc, (h.value if rc == QGEMV_OK else None)
+
+
+def qgemv_arith(h) -> int:
+    return load().qgemv_arith(h)
+
+
+def qgemv_mfma_codes(bits, group) -> int:
+    return load().qgemv_mfma_codes(bits, group)
 
 
 def qgemv_destroy(h) -> None:
@@ -174,13 +197,14 @@ class Matrix:
     x: bf16 (or int16 bits) [M][K]; y: float32.  Statuses other than
     QGEMV_OK raise QgemvError."""
 
-    def __init__(self, bits, group, n, k, w, scales, biases, n_experts=1):
+    def __init__(self, bits, group, n, k, w, scales, biases, n_experts=1, arith=QGEMV_ARITH_AUTO):
         self.bits, self.group, self.n, self.k, self.n_experts = bits, group, n, k, n_experts
         self._keep = (w, scales, biases)
-        rc, h = qgemv_create(bits, group, n, k, w, scales, biases, n_experts)
+        rc, h = qgemv_create_arith(bits, group, n, k, w, scales, biases, arith, n_experts)
         if rc != QGEMV_OK:
-            raise QgemvError("qgemv_create", rc)
+            raise QgemvError("qgemv_create_arith", rc)
         self.h = h
+        self.arith = qgemv_arith(h)
 
     def _chk(self, rc, what):
         if rc != QGEMV_OK:

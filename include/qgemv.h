@@ -98,14 +98,53 @@ typedef struct qgemv_handle* qgemv_t;
  * Returns QGEMV_OK and *out, or a refusal (then *out is untouched). */
 int qgemv_create(const qgemv_desc* d, qgemv_t* out);
 
+/* ---- arithmetic of a handle --------------------------------------------
+ * Both forms compute, per output, the sum over the row's 32-code units u of
+ *   scale(u) * A(u) + bias(u) * X(u),
+ * A(u) the fp32 dot of the unit's exact bf16 codes with its activations and
+ * X(u) the fp32 sum of its activations ("Exactness", item "Precision", on
+ * "...support for oQ..." #774: bf16 activations, fp32 group sums).  They
+ * differ in how A(u) is summed and in the order of the folds, so their bits
+ * differ (each stays within the fp64 bound).  The form is fixed at create
+ * for every window, strided and indexed call of the handle, which is what
+ * keeps a row's bits the same alone and inside any window.
+ *   QGEMV_ARITH_DOT   lanes own slices of a row's K; v_dot2 chains, then one
+ *                     fixed butterfly over the lanes of the row.
+ *   QGEMV_ARITH_MFMA  matrix cores: 16x16x32 bf16 products with one window
+ *                     row per 4 operand rows; each lane folds its own four
+ *                     units in order, no butterfly.  Needs k a multiple of
+ *                     qgemv_mfma_codes(bits, group) and aligned scales
+ *                     and biases (QGEMV_E_NOKERNEL otherwise).
+ *   QGEMV_ARITH_AUTO  the library's choice (what qgemv_create uses).      */
+#define QGEMV_ARITH_AUTO 0
+#define QGEMV_ARITH_DOT 1
+#define QGEMV_ARITH_MFMA 2
+
+/* As qgemv_create, with the arithmetic chosen by the caller. */
+int qgemv_create_arith(const qgemv_desc* d, int32_t arith, qgemv_t* out);
+
+/* The arithmetic a handle was created with (QGEMV_ARITH_DOT or _MFMA), or
+ * QGEMV_E_ARG for a NULL handle. */
+int qgemv_arith(qgemv_t h);
+
+/* The multiple of k that the MFMA form needs, its load group of 128-code
+ * rounds (a whole number of 128-byte lines of a row): 512 codes for 2 and 6
+ * bits, 1024 for 3 and 5, 256 for 4, 128 for 8 (256 at group 128); 0 for a
+ * bad bits or group.  The MFMA form also needs scales and biases 16-byte
+ * aligned where a row's scales of one load group fill whole 16-byte pieces,
+ * else 4-byte aligned. */
+int64_t qgemv_mfma_codes(int32_t bits, int32_t group);
+
 /* Free the host-side handle (never touches device memory). NULL is a no-op. */
 void qgemv_destroy(qgemv_t h);
 
 /* y[i][j] for i < m, j < n, contiguous (row stride n).
  *   x  bf16 bits [m][k] device, 16-byte aligned.
  *   m  window rows, 0..16; m == 0 launches nothing and returns QGEMV_OK.
- *      A window whose staged activations exceed the LDS of one block
- *      (m*k*2.125 bytes > 152 KiB) is refused with QGEMV_E_WINDOW.
+ *      QGEMV_ARITH_DOT: a window whose staged activations exceed the LDS
+ *      of one block (m*k*2.125 bytes > 152 KiB) is refused with
+ *      QGEMV_E_WINDOW.  QGEMV_ARITH_MFMA: such a window runs as passes of
+ *      fewer rows (the weights are read once per pass), same bits.
  *   y  fp32 [m][n] device, 4-byte aligned, must not overlap x or weights.
  *   epi QGEMV_EPI_NONE or QGEMV_EPI_RELU2.
  *   stream  hipStream_t (NULL = the null stream).

@@ -165,3 +165,37 @@ def test_stack_create_rules():
     for runs, ldy, want in bad:
         rc, h = qgemv.qgemv_stack_create(runs, ldy)
         assert rc == want and h is None, (runs[:1], qgemv.qgemv_strerror(rc))
+
+
+def test_arith_choice_fixed_at_create():
+    steps = {2: 512, 3: 1024, 4: 256, 5: 1024, 6: 512, 8: 128}
+    for bits in (2, 3, 4, 5, 6, 8):
+        for group in (32, 64, 128):
+            want = 256 if (bits == 8 and group == 128) else steps[bits]
+            assert qgemv.qgemv_mfma_codes(bits, group) == want
+    assert qgemv.qgemv_mfma_codes(7, 64) == 0 and qgemv.qgemv_mfma_codes(4, 16) == 0
+    for bits in (2, 3, 4, 5, 6, 8):
+        for group in (32, 64, 128):
+            k = 4 * qgemv.qgemv_mfma_codes(bits, group)
+            for arith in (qgemv.QGEMV_ARITH_DOT, qgemv.QGEMV_ARITH_MFMA):
+                rc, h = qgemv.qgemv_create_arith(bits, group, 48, k, W, S, B, arith)
+                assert rc == 0, (bits, group, arith, qgemv.qgemv_strerror(rc))
+                assert qgemv.qgemv_arith(h) == arith
+                rc, geo = qgemv.qgemv_query(h)
+                assert rc == 0
+                if arith == qgemv.QGEMV_ARITH_MFMA:
+                    assert geo[:5] == [4, 16, 32, 256, 64]
+                qgemv.qgemv_destroy(h)
+            rc, h = qgemv.qgemv_create(bits, group, 48, k, W, S, B)
+            assert rc == 0 and qgemv.qgemv_arith(h) in (qgemv.QGEMV_ARITH_DOT, qgemv.QGEMV_ARITH_MFMA)
+            qgemv.qgemv_destroy(h)
+    # refused for that form only: k not a multiple of the step, scales
+    # only 2-byte aligned
+    for k, s in ((4096 + 512, S), (4096, S + 4)):
+        rc, h = qgemv.qgemv_create_arith(3, 128, 48, k, W, s, B, qgemv.QGEMV_ARITH_MFMA)
+        assert rc == qgemv.QGEMV_E_NOKERNEL and h is None
+        rc, h = qgemv.qgemv_create_arith(3, 128, 48, k, W, s, B, qgemv.QGEMV_ARITH_AUTO)
+        assert rc == 0 and qgemv.qgemv_arith(h) == qgemv.QGEMV_ARITH_DOT
+        qgemv.qgemv_destroy(h)
+    assert qgemv.qgemv_create_arith(4, 64, 48, 2048, W, S, B, 3)[0] == qgemv.QGEMV_E_ARG
+    assert qgemv.qgemv_arith(None) == qgemv.QGEMV_E_ARG

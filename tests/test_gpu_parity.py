@@ -37,12 +37,18 @@ def dev(a: np.ndarray):
     return torch.from_numpy(a.view(view)).to(DEV)
 
 
-def matrix_of(d, expert=None):
+# both arithmetic forms of a handle, each held to the same bars
+ARITHS = [qgemv.QGEMV_ARITH_DOT, qgemv.QGEMV_ARITH_MFMA]
+ARITH_IDS = ["dot", "mfma"]
+arith_param = pytest.mark.parametrize("arith", ARITHS, ids=ARITH_IDS)
+
+
+def matrix_of(d, expert=None, arith=qgemv.QGEMV_ARITH_AUTO):
     w, s, b = d["words"], d["scales"], d["biases"]
     if expert is not None:
         w, s, b = w[expert], s[expert], b[expert]
     tw, ts, tb = dev(w), dev(s), dev(b)
-    return qgemv.Matrix(d["bits"], d["group"], d["n"], d["k"], tw, ts, tb)
+    return qgemv.Matrix(d["bits"], d["group"], d["n"], d["k"], tw, ts, tb, arith=arith)
 
 
 def run(mat, xt, m=None, epi=0):
@@ -101,12 +107,14 @@ def test_unpacked_codes_bit_exact(bits, group):
 # the width sweep: N = K = 4096 at every pair, a 16-row window
 # ---------------------------------------------------------------------------
 
+@arith_param
 @pytest.mark.parametrize("bits,group", PAIRS)
-def test_sweep_within_bound(bits, group):
-    print_case("sweep", bits, group)
+def test_sweep_within_bound(bits, group, arith):
+    print_case("sweep", bits, group, arith)
     d = synth.sweep(bits, group, m=16)
     n, k = d["n"], d["k"]
-    mat = matrix_of(d)
+    mat = matrix_of(d, arith=arith)
+    assert mat.arith == arith
     xt = dev(d["x"])
     y16 = run(mat, xt).cpu().numpy()
     y64, a64, t64 = oracle.gemv(d["words"], d["scales"], d["biases"], d["x"], bits, group, n, k,
@@ -121,15 +129,16 @@ def test_sweep_within_bound(bits, group):
     assert ctrl > 1.0, f"negative control only {ctrl:.3f} of the bound"
 
 
+@arith_param
 @pytest.mark.parametrize("bits,group", PAIRS)
-def test_window_invariance(bits, group):
+def test_window_invariance(bits, group, arith):
     """Every row of a 64-row pool alone equals itself at every position of
     every 2-, 3-, 8- and 16-row window, bit for bit."""
-    print_case("windows", bits, group)
+    print_case("windows", bits, group, arith)
     d = synth.sweep(bits, group, m=0)
     rng = np.random.default_rng(synth.sweep_seed(bits, group) + 7)
     pool = dev(synth.draw_x(rng, 64, d["k"]))
-    mat = matrix_of(d)
+    mat = matrix_of(d, arith=arith)
     alone = torch.empty((64, d["n"]), dtype=torch.float32, device=DEV)
     for r in range(64):
         mat.run(pool[r:r + 1], alone[r:r + 1], m=1)
@@ -140,13 +149,14 @@ def test_window_invariance(bits, group):
             assert bits_equal(y, alone[s0:s0 + m]), f"window {m} at {s0}"
 
 
+@arith_param
 @pytest.mark.parametrize("bits,group", PAIRS)
-def test_exact_representable_inputs(bits, group):
+def test_exact_representable_inputs(bits, group, arith):
     """s in {2^-8, 2^-7, 2^-6}, bias a multiple of 2^-8, x in {-1, 0, 1}: every
     summation order is exact, so y must equal y64 exactly."""
     n, k = 72, 4096
     d = synth.exact_case(9000 + bits * 10 + group, bits, group, n, k, 16)
-    mat = matrix_of(d)
+    mat = matrix_of(d, arith=arith)
     xt = dev(d["x"])
     y64, _, _ = oracle.gemv(d["words"], d["scales"], d["biases"], d["x"], bits, group, n, k)
     for m in (1, 16):
@@ -158,12 +168,13 @@ def test_exact_representable_inputs(bits, group):
 # epilogue, stride, repeat, NaN
 # ---------------------------------------------------------------------------
 
+@arith_param
 @pytest.mark.parametrize("bits,group", [(2, 32), (3, 64), (4, 64), (5, 128), (6, 32), (8, 128)])
-def test_relu2_and_strided(bits, group):
-    print_case("relu2/strided", bits, group)
+def test_relu2_and_strided(bits, group, arith):
+    print_case("relu2/strided", bits, group, arith)
     n, k = 1000, 2048      # ragged against every tile size
     d = synth.matrix(6000 + bits * 10 + group, bits, group, n, k, 8)
-    mat = matrix_of(d)
+    mat = matrix_of(d, arith=arith)
     xt = dev(d["x"])
     y = run(mat, xt)
     r = run(mat, xt, epi=qgemv.QGEMV_EPI_RELU2)
@@ -191,12 +202,13 @@ def test_relu2_and_strided(bits, group):
     assert bits_equal(y, y2)
 
 
-def test_nan_row_stays_in_its_row():
+@arith_param
+def test_nan_row_stays_in_its_row(arith):
     bits, group, n, k = 4, 64, 512, 2048
     d = synth.matrix(77, bits, group, n, k, 3)
     x = d["x"].copy()
     x[1, 100] = 0x7FC0  # bf16 NaN
-    mat = matrix_of(d)
+    mat = matrix_of(d, arith=arith)
     y = run(mat, dev(x)).cpu().numpy()
     yc = run(mat, dev(d["x"])).cpu().numpy()
     assert np.all(np.isnan(y[1]))
@@ -223,14 +235,22 @@ def test_refusals_leave_output_untouched():
 # ---------------------------------------------------------------------------
 
 EDGE = [(6, 64, 48, 2048), (5, 128, 6192, 2048), (4, 32, 1, 2048), (3, 32, 33, 32),
-        (5, 32, 65, 96), (6, 64, 17, 192), (2, 128, 129, 384), (8, 32, 3, 32), (3, 128, 40, 4096 + 128)]
+        (5, 32, 65, 96), (6, 64, 17, 192), (2, 128, 129, 384), (8, 32, 3, 32), (3, 128, 40, 4096 + 128),
+        # the shortest rows of the matrix-core form, N ragged against 16-column waves
+        (4, 128, 1, 128), (8, 32, 17, 128), (2, 64, 100, 256), (6, 32, 1, 256), (3, 64, 33, 512),
+        (5, 128, 31, 1024), (4, 32, 1000, 384)]
 
 
+@arith_param
 @pytest.mark.parametrize("bits,group,n,k", EDGE)
-def test_edge_shapes(bits, group, n, k):
-    print_case("edge", bits, group, n, k)
+def test_edge_shapes(bits, group, n, k, arith):
+    print_case("edge", bits, group, n, k, arith)
     d = synth.matrix(8000 + n + k, bits, group, n, k, 3)
-    mat = matrix_of(d)
+    if arith == qgemv.QGEMV_ARITH_MFMA and k % qgemv.qgemv_mfma_codes(bits, group):
+        with pytest.raises(qgemv.QgemvError, match="QGEMV_E_NOKERNEL"):
+            matrix_of(d, arith=arith)
+        return
+    mat = matrix_of(d, arith=arith)
     xt = dev(d["x"])
     y3 = run(mat, xt)
     y64, a64, _ = oracle.gemv(d["words"], d["scales"], d["biases"], d["x"], bits, group, n, k)
@@ -287,16 +307,19 @@ def test_stack_config(m):
 @pytest.fixture(scope="module")
 def lmhead():
     d = synth.lmhead(m=16)
-    d["mat"] = matrix_of(d)
+    tw, ts, tb = dev(d["words"]), dev(d["scales"]), dev(d["biases"])
+    d["mats"] = {a: qgemv.Matrix(d["bits"], d["group"], d["n"], d["k"], tw, ts, tb, arith=a) for a in ARITHS}
     d["xt"] = dev(d["x"])
     return d
 
 
+@arith_param
 @pytest.mark.parametrize("m", [1, 8, 16])
-def test_lmhead_sampled(lmhead, m):
+def test_lmhead_sampled(lmhead, m, arith):
     d = lmhead
     n, k, bits, group = d["n"], d["k"], d["bits"], d["group"]
-    y = run(d["mat"], d["xt"], m)
+    mat = d["mats"][arith]
+    y = run(mat, d["xt"], m)
     rng = np.random.default_rng(m)
     cols = np.unique(np.concatenate([np.arange(64), np.arange(n - 64, n),
                                      rng.integers(0, n, 384)]))
@@ -305,26 +328,27 @@ def test_lmhead_sampled(lmhead, m):
     check_bound(y[:, cols].cpu().numpy(), y64, a64, k, f"lmhead m={m}")
     # the same rows alone, at full size
     for r in sorted({0, m - 1, m // 2}):
-        assert bits_equal(run(d["mat"], d["xt"][r:r + 1])[0], y[r])
+        assert bits_equal(run(mat, d["xt"][r:r + 1])[0], y[r])
 
 
 @pytest.fixture(scope="module")
 def experts():
     d = synth.experts()
     d["tw"], d["ts"], d["tb"] = dev(d["words"]), dev(d["scales"]), dev(d["biases"])
-    d["mat"] = qgemv.Matrix(d["bits"], d["group"], d["n"], d["k"], d["tw"], d["ts"], d["tb"],
-                            n_experts=d["n_experts"])
     return d
 
 
+@arith_param
 @pytest.mark.parametrize("epi", [0, 1])
-def test_indexed_experts_config(experts, epi):
+def test_indexed_experts_config(experts, epi, arith):
     d = experts
     n, k, m, slots = d["n"], d["k"], d["idx"].shape[0], d["idx"].shape[1]
     xt = dev(d["x"])
     it = dev(d["idx"])
     y = torch.empty((m, slots, n), dtype=torch.float32, device=DEV)
-    d["mat"].run_indexed(xt, it, y.view(-1), epi=epi)
+    mat = qgemv.Matrix(d["bits"], d["group"], n, k, d["tw"], d["ts"], d["tb"], n_experts=d["n_experts"],
+                       arith=arith)
+    mat.run_indexed(xt, it, y.view(-1), epi=epi)
     # each (row, slot) equals the plain call on the expert's own handle
     wpr = d["words"].shape[-1]
     gpr = d["scales"].shape[-1]
@@ -333,7 +357,8 @@ def test_indexed_experts_config(experts, epi):
         for s in range(slots):
             e = int(d["idx"][i, s])
             if e not in views:
-                views[e] = qgemv.Matrix(d["bits"], d["group"], n, k, d["tw"][e], d["ts"][e], d["tb"][e])
+                views[e] = qgemv.Matrix(d["bits"], d["group"], n, k, d["tw"][e], d["ts"][e], d["tb"][e],
+                                        arith=arith)
             yp = run(views[e], xt[i:i + 1], epi=epi)
             assert bits_equal(yp[0], y[i, s]), (i, s, e)
     assert wpr and gpr
@@ -347,7 +372,8 @@ def test_indexed_experts_config(experts, epi):
     assert np.all(np.abs(got - y64) <= tol)
 
 
-def test_indexed_small_stack_repeats_and_duplicates():
+@arith_param
+def test_indexed_small_stack_repeats_and_duplicates(arith):
     """A routing table that names one expert twice in a row and gives one
     expert more rows than one staging pass holds."""
     bits, group, n, k, e = 3, 64, 300, 1024, 6
@@ -355,14 +381,14 @@ def test_indexed_small_stack_repeats_and_duplicates():
     idx = np.array([[1, 1, 2], [1, 0, 5], [1, 3, 3], [1, 2, 0], [1, 4, 4],
                     [1, 5, 1], [0, 0, 0], [2, 1, 4], [3, 3, 1]], dtype=np.int32)
     tw, ts, tb = dev(d["words"]), dev(d["scales"]), dev(d["biases"])
-    mat = qgemv.Matrix(bits, group, n, k, tw, ts, tb, n_experts=e)
+    mat = qgemv.Matrix(bits, group, n, k, tw, ts, tb, n_experts=e, arith=arith)
     xt = dev(d["x"])
     y = torch.empty((9, 3, n), dtype=torch.float32, device=DEV)
     mat.run_indexed(xt, dev(idx), y.view(-1))
     for i in range(9):
         for s in range(3):
             ex = int(idx[i, s])
-            v = qgemv.Matrix(bits, group, n, k, tw[ex], ts[ex], tb[ex])
+            v = qgemv.Matrix(bits, group, n, k, tw[ex], ts[ex], tb[ex], arith=arith)
             assert bits_equal(run(v, xt[i:i + 1])[0], y[i, s]), (i, s)
 
 
