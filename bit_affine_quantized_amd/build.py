@@ -3,8 +3,9 @@
 The kernels are instantiated per code width in csrc/qgemv_b<bits>.hip and
 compiled in parallel with the host code (csrc/qgemv.hip), then linked.
 Flags: -ffp-contract=off (every fused operation in the kernels is an explicit
-builtin, so no instantiation contracts differently from another), and the
-packed-fp32 feature switched off for device code.
+builtin, so no instantiation contracts differently from another), the
+packed-fp32 feature switched off for device code, and MFMA results kept in
+ordinary VGPRs (the epilogue reads them with plain VALU operands).
 """
 
 from __future__ import annotations
@@ -26,6 +27,7 @@ ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 

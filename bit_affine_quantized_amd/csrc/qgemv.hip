@@ -99,12 +99,16 @@ void init_device(DeviceInfo* info) {
   for (int bi = 0; bi < 6; ++bi)
     for (int gi = 0; gi < 3; ++gi) {
       const qg::Entry& e = qg::entry(bi, gi);
-      for (int v = 0; v < 5; ++v)
-        for (qg::KernelFn fn : {e.fast[v][0], e.fast[v][1], e.generic[v], e.mfma[v]})
+      for (int v = 0; v < 5; ++v) {
+        for (qg::KernelFn fn : {e.fast[v][0], e.fast[v][1], e.generic[v]})
           if (fn && hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                         hipFuncAttributeMaxDynamicSharedMemorySize,
                                         static_cast<int>(qg::kMaxDynamicLds)) != hipSuccess)
             return;
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(e.mfma[v]), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                static_cast<int>(qg::kMaxMfmaLds)) != hipSuccess)
+          return;
+      }
     }
   for (qg::StackFn fn : {qg::stack_kernel_m1(), qg::stack_kernel_m2(), qg::stack_kernel_m4(),
                          qg::stack_kernel_m8(), qg::stack_kernel_m16()})
@@ -149,26 +153,18 @@ size_t lds_bytes(const qgemv_handle* h, int var, int stage) {
 }
 
 // The matrix-core kernels' LDS: the staged window (rows of k/32 units x 64
-// bytes + 16 padding, a zero line, unit sums), the routed list of an indexed
-// call, and a ring of D load-group slots per wave (2 <= D <= 8).  D is the
-// deepest ring that fits half the CU (two blocks per CU) for windows up to
-// 4 rows, else the whole CU.  Returns false when not even two slots fit.
-bool mfma_plan(const qgemv_handle* h, int var, bool indexed, int* depth, size_t* lds) {
+// bytes + 16 padding, a zero area of R * 256 bytes, unit sums), the routed
+// list of an indexed call, and one load-group slot per wave.  Returns false
+// when it exceeds one block's LDS.
+bool mfma_plan(const qgemv_handle* h, int var, bool indexed, size_t* lds) {
   const size_t mb = static_cast<size_t>(qg::kWindows[var]);
   const size_t units = static_cast<size_t>(h->d.k) / 32;
-  const size_t fixed = mb * (units * 64 + 16) + 64 + mb * units * 4 + (indexed ? qg::kMaxList * 4 : 0);
-  const size_t per_slot = static_cast<size_t>(qg::kMWaves) * h->entry->mfma_slot;
-  size_t dmax = static_cast<size_t>(h->entry->mfma_dmax);
-  if (dmax > 8) dmax = 8;
-  for (size_t budget : {var <= 2 ? size_t{76 * 1024} : qg::kMaxDynamicLds, qg::kMaxDynamicLds}) {
-    if (fixed + 2 * per_slot > budget) continue;
-    size_t d = (budget - fixed) / per_slot;
-    if (d > dmax) d = dmax;
-    *depth = static_cast<int>(d);
-    *lds = fixed + d * per_slot;
-    return true;
-  }
-  return false;
+  const size_t b = mb * (units * 64 + 16) + 256 * static_cast<size_t>(h->entry->mfma_group) + mb * units * 4 +
+                   (indexed ? qg::kMaxList * 4 : 0) +
+                   static_cast<size_t>(h->entry->mfma_waves[var]) * h->entry->mfma_slot;
+  if (b > qg::kMaxMfmaLds) return false;
+  *lds = b;
+  return true;
 }
 
 int check_y_alias(const qgemv_handle* h, const void* y, size_t ybytes, const void* x, size_t xbytes,
@@ -193,29 +189,28 @@ int launch(const qgemv_handle* h, const uint16_t* x, int32_t m, float* y, int64_
   int stage = (h->fast && h->ppc > 1) ? 1 : 0;
   if (stage && lds_bytes(h, var, 1) > qg::kMaxDynamicLds) stage = 0;
   const bool mfma = h->arith == QGEMV_ARITH_MFMA;
-  int depth = 0;
   size_t lds = 0;
   if (mfma) {
     stage = 0;
     // A window too wide for one block's LDS runs as passes of a narrower
     // variant over the same tiles: each output of the matrix-core form
     // depends only on its own window row, so the bits are the same.
-    while (!mfma_plan(h, var, indexed, &depth, &lds)) {
+    while (!mfma_plan(h, var, indexed, &lds)) {
       if (var == 0) return QGEMV_E_WINDOW;
       --var;
     }
   } else {
     lds = lds_bytes(h, var, stage);
   }
-  if (lds > qg::kMaxDynamicLds) return QGEMV_E_WINDOW;
+  if (lds > (mfma ? qg::kMaxMfmaLds : qg::kMaxDynamicLds)) return QGEMV_E_WINDOW;
   qg::KernelFn fn = h->fast ? h->entry->fast[var][stage] : h->entry->generic[var];
   int threads = qg::kThreads;
   int64_t tile_rows = 0;
   if (mfma) {
     // one wave per 16 output columns
     fn = h->entry->mfma[var];
-    threads = qg::kMThreads;
-    tile_rows = static_cast<int64_t>(qg::kMWaves) * 16;
+    threads = h->entry->mfma_waves[var] * qg::kWave;
+    tile_rows = static_cast<int64_t>(h->entry->mfma_waves[var]) * 16;
   } else {
     const int R = h->fast ? h->entry->fast_rows[var] : h->entry->generic_rows[var];
     const int slots_per_wave = qg::kWave / h->lpr;
@@ -240,7 +235,7 @@ int launch(const qgemv_handle* h, const uint16_t* x, int32_t m, float* y, int64_
   p.n_experts = h->d.n_experts;
   p.epi = epi;
   p.lpr = h->lpr;
-  p.cpl = mfma ? depth : h->cpl;   // the matrix-core kernels read their ring depth here
+  p.cpl = h->cpl;
   p.nchunks = h->nchunks;
   p.tiles = static_cast<int32_t>(tiles);
   p.indexed = indexed;
@@ -377,9 +372,8 @@ int qgemv_create_arith(const qgemv_desc* d, int32_t arith, qgemv_t* out) {
   // time when theirs does not (QGEMV_E_WINDOW), or, in the matrix-core
   // form, run as passes of fewer rows.
   if (h.arith == QGEMV_ARITH_MFMA) {
-    int depth = 0;
     size_t lds = 0;
-    if (!mfma_plan(&h, 0, false, &depth, &lds)) {
+    if (!mfma_plan(&h, 0, false, &lds)) {
       if (arith == QGEMV_ARITH_MFMA) return QGEMV_E_NOKERNEL;
       h.arith = QGEMV_ARITH_DOT;
     }
@@ -624,8 +618,8 @@ int qgemv_query(qgemv_t h, int64_t out[6]) {
     out[0] = 4;
     out[1] = 16;
     out[2] = 32;
-    out[3] = qg::kMThreads;
-    out[4] = static_cast<int64_t>(qg::kMWaves) * 16;
+    out[3] = h->entry->mfma_waves[0] * qg::kWave;
+    out[4] = static_cast<int64_t>(h->entry->mfma_waves[0]) * 16;
   } else {
     const int R = h->fast ? h->entry->fast_rows[0] : h->entry->generic_rows[0];
     out[0] = h->lpr;

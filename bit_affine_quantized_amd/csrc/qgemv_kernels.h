@@ -58,6 +58,7 @@ constexpr int kMaxSeg = 4;    // members per run of a fused stack
 constexpr int kMaxRuns = 8;   // runs per fused stack
 // 160 KiB of LDS per CU on gfx950, less the kernels' static arrays.
 constexpr size_t kMaxDynamicLds = 160 * 1024 - 8 * 1024;
+constexpr size_t kMaxMfmaLds = 160 * 1024 - 1024;   // the MFMA kernels' static LDS is a few hundred bytes
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -950,111 +951,74 @@ __global__ __launch_bounds__(kThreads) void qrow_fast(const Params p) {
 // each output depends only on its own window row's activations, wherever the
 // row sits in the window.
 //
-// Weights, scales and biases reach LDS straight from HBM: buffer loads with
-// the LDS bit put lane L's bytes at the wave's slot + L * size.  A slot holds
-// one group of R rounds, R chosen so that a column's share of a group is L
-// whole 128-byte lines; each group of 8 lanes of a load fetches one whole
-// line, because a streaming line asked for by two different loads is read
-// from HBM twice.  Lines sit in the slot line-major ([line][column]) with
-// the 8 pieces of column c's line rotated by c / 2, so the 16 lanes that
-// read the same piece of 16 columns hit 16 different bank groups.  The slots
-// form a ring of D groups private to the wave, loaded D - 1 groups ahead;
-// every group issues the same number of loads, so an s_waitcnt on the
-// vector-memory counter that leaves the later groups in flight marks a
-// group ready.
+// Loads: a group of R rounds, R chosen so that a column's share of a group
+// is L whole 128-byte lines, comes in as 16-byte pieces, each group of 8
+// lanes of one load fetching one whole line (a streaming line asked for by
+// two different loads is read from HBM twice).  The pieces go to registers
+// one group ahead, then to a per-wave LDS slot laid out line-major
+// ([line][column]) with the 8 pieces of column c's line rotated by c / 2,
+// so the 16 lanes that read the same piece of 16 columns hit 16 different
+// bank groups.
 // ---------------------------------------------------------------------------
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 template <int B, int G> struct MGroup {
   static constexpr int R = B == 8 ? 1 : (B == 4 ? 2 : ((B == 2 || B == 6) ? 4 : 8));  // rounds per group
   static constexpr int L = R * B / 8;              // 128-byte lines per column per group
-  static constexpr int WDMA = 2 * L;               // weight loads per group (8 lines each)
+  static constexpr int WLD = 2 * L;                // 16-byte weight loads per lane per group
   static constexpr int SB = 256 * R / G;           // scale bytes per column per group
   static constexpr bool S16 = SB % 16 == 0;        // scales as 16-byte pieces, else dwords
   static constexpr int SBP = SB < 4 ? 4 : SB;      // bytes kept per column (the aligned dword when 2)
-  static constexpr int SLANES = 16 * SBP / (S16 ? 16 : 4);   // lanes of one scale load
-  static constexpr int NDMA = WDMA + 2;            // loads per group
+  static constexpr int SSZ = S16 ? 16 : 4;         // bytes of one scale load
+  static constexpr int SLANES = 16 * SBP / SSZ;    // lanes of one scale load
   static constexpr int WBYTES = 16 * L * 128;
   static constexpr int SLOT = WBYTES + 2 * 16 * SBP;
-  static constexpr int DMAX = 63 / NDMA + 1;       // ring depth the load counter can track
   static constexpr int CH = (B % 4 == 0) ? 4 : ((B % 2 == 0) ? 2 : 1);   // words per LDS read
   static_assert(R * B % 8 == 0 && SLANES <= 64, "group geometry");
 };
 
-constexpr int kMWaves = 4;                       // waves per block of the MFMA kernels
-constexpr int kMThreads = kMWaves * kWave;
+// Waves per block: a wide window's activations are staged once for 8 waves.
+template <int MB> struct MWaves {
+  static constexpr int v = MB >= 8 ? 8 : 4;
+};
 
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// Wait until at most `ahead` groups of NDMA loads are still in flight.
-template <int NDMA>
-__device__ __forceinline__ void wait_groups(int ahead) {
-  switch (ahead) {
-#define QG_W(A)                                   \
-  case A:                                         \
-    if constexpr ((A) * NDMA <= 63) {             \
-      vm_wait<(A) * NDMA>();                      \
-    } else {                                      \
-      vm_wait<0>();                               \
-    }                                             \
-    break;
-    QG_W(0) QG_W(1) QG_W(2) QG_W(3) QG_W(4) QG_W(5) QG_W(6) QG_W(7)
-#undef QG_W
-    default: vm_wait<0>(); break;
-  }
-}
-
-template <int SIZE>
-__device__ __forceinline__ void lds_dma(__amdgpu_buffer_rsrc_t r, unsigned char* lds, int voff, int soff) {
-  if constexpr (SIZE == 16) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, soff, 0, kNt);
-  } else {
-    static_assert(SIZE == 4, "load size");
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 4, voff, soff, 0, kNt);
-  }
-}
-
-// p.cpl carries the ring depth D (groups per wave, at least 2) chosen by the host.
 template <int B, int G, int MB>
 __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const int gx, unsigned char* smem,
                                           int* s_wave_cnt, int* s_xrow, int64_t* s_yoff) {
   using MG = MGroup<B, G>;
-  constexpr int R = MG::R, CH = MG::CH;
+  constexpr int R = MG::R, CH = MG::CH, SSZ = MG::SSZ;
+  constexpr int NW = MWaves<MB>::v, NT = NW * kWave;
   constexpr int NMB = (MB + 3) / 4;         // 4-row blocks of the window
+  constexpr int ZB = R * 256;               // zero area: one group's activations
 
   const int units = static_cast<int>(p.k / 32);
   const int groups = units / (4 * R);       // groups per tile
   const int mrows = p.indexed ? MB : min(p.m, MB);       // window rows staged
   const int xstride = units * 64 + 16;                     // bytes per staged row
-  const int D = p.cpl;
   // LDS: activations [mrows][units][32 slots] bf16 (rows padded by 16 bytes
-  // so a 4 x 4 block of reads hits distinct banks), a 64-byte zero line
-  // (the A operand of lanes outside the block diagonal), unit sums
-  // [mrows][units] fp32, the routed list (indexed calls), then the rings.
-  unsigned char* xs = smem;
-  unsigned char* zero_line = smem + static_cast<size_t>(mrows) * xstride;
-  float* xsum = reinterpret_cast<float*>(zero_line + 64);
+  // so a 4 x 4 block of reads hits distinct banks), a zero area of one
+  // group's activations (the A operand of lanes outside the block diagonal,
+  // read at the same offsets as a live lane's), unit sums [mrows][units]
+  // fp32, the routed list (indexed calls), then one slot per wave.
+  unsigned char* zero_area = smem + static_cast<size_t>(mrows) * xstride;
+  float* xsum = reinterpret_cast<float*>(zero_area + ZB);
   int* s_list = reinterpret_cast<int*>(xsum + static_cast<size_t>(mrows) * units);
-  unsigned char* rings = reinterpret_cast<unsigned char*>(s_list + (p.indexed ? kMaxList : 0));
+  unsigned char* slots = reinterpret_cast<unsigned char*>(s_list + (p.indexed ? kMaxList : 0));
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int j = lane % 16, qd = lane / 16;
-  unsigned char* ring = rings + static_cast<size_t>(wv) * D * MG::SLOT;
+  unsigned char* slot = slots + static_cast<size_t>(wv) * MG::SLOT;
 
   int expert = 0;
   int total = p.m;
   if (p.indexed) {
     expert = blockIdx.y;
-    total = build_route_list<kMThreads>(p.idx, p.m * p.slots, expert, s_list, s_wave_cnt);
+    total = build_route_list<NT>(p.idx, p.m * p.slots, expert, s_list, s_wave_cnt);
     if (total == 0) return;
   }
   const int n = static_cast<int>(p.n);
@@ -1071,16 +1035,15 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
   // weight load t: lanes 8a..8a+7 fetch line lam = 8t + a of the slot, which
   // is line lam / 16 of column lam % 16's share; lane 8a + e brings piece
   // (e - c/2) mod 8 of it, so piece pp of column c's line sits at e = (pp + c/2) mod 8
-  int w_voff[MG::WDMA];
+  int w_voff[MG::WLD];
 #pragma unroll
-  for (int t = 0; t < MG::WDMA; ++t) {
+  for (int t = 0; t < MG::WLD; ++t) {
     const int lam = 8 * t + lane / 8, c = lam % 16, ln = lam / 16;
     const int pp = (lane % 8 - c / 2) & 7;
     w_voff[t] = static_cast<int>(c * row_bytes) + ln * 128 + pp * 16;
   }
   // scale (bias) load: lane L < SLANES brings piece (or dword) L % per of
-  // column L / per, per = SBP / size
-  constexpr int SSZ = MG::S16 ? 16 : 4;
+  // column L / per, per = SBP / SSZ
   constexpr int SPER = MG::SBP / SSZ;
   const bool s_live = lane < MG::SLANES;
   const int s_voff = (lane / SPER) * gpr2 + (lane % SPER) * SSZ;
@@ -1098,10 +1061,9 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
   const int s_off = MG::WBYTES + j * MG::SBP;
   const int b_off = s_off + 16 * MG::SBP;
 
-  // A step is one group of one tile; both cursors walk the steps in order:
-  // (tile index i, group gr, ring slot sl).
+  // A step is one group of one tile; cursors walk the steps in order
   struct Cursor {
-    int st, i, gr, sl;
+    int st, i, gr;
   };
   auto advance = [&](Cursor& c) {
     ++c.st;
@@ -1109,13 +1071,16 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
       c.gr = 0;
       ++c.i;
     }
-    if (++c.sl == D) c.sl = 0;
   };
-  // issue every load of a step (or, past the last step, loads that read
-  // nothing, so each group still counts NDMA loads) into its ring slot
-  auto issue = [&](const Cursor& c) {
+  struct Stage {
+    u32x4 w[MG::WLD];
+    uint32_t s[SSZ / 4];
+    uint32_t b[SSZ / 4];
+  };
+  // a step's loads into registers (past the last step: loads that read nothing)
+  auto load_stage = [&](Stage& sg, const Cursor& c) {
     const bool real = c.st < steps;
-    const int c0 = ((bx + c.i * gx) * kMWaves + wv) * 16;
+    const int c0 = ((bx + c.i * gx) * NW + wv) * 16;
     const int ncols = real ? n - c0 : 0;
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(wexp + static_cast<int64_t>(c0) * row_bytes,
                                                 static_cast<int64_t>(ncols) * row_bytes);
@@ -1123,17 +1088,22 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
                                                 static_cast<int64_t>(ncols) * gpr2);
     const __amdgpu_buffer_rsrc_t br = make_rsrc(bexp + static_cast<int64_t>(c0) * gpr2,
                                                 static_cast<int64_t>(ncols) * gpr2);
-    unsigned char* slot = ring + c.sl * MG::SLOT;
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the slot's last reads are done
     const int wsoff = c.gr * (MG::L * 128);
 #pragma unroll
-    for (int t = 0; t < MG::WDMA; ++t) lds_dma<16>(wr, slot + t * 1024, w_voff[t], wsoff);
+    for (int t = 0; t < MG::WLD; ++t) sg.w[t] = __builtin_amdgcn_raw_buffer_load_b128(wr, w_voff[t], wsoff, kNt);
     // this group's scales: SB bytes per column from byte gr*SB of the row
-    // (at SB = 2, the aligned dword that holds them)
+    // (at SB = 2, the aligned dword that holds them); default cache policy,
+    // since a row's scale line serves several groups
     const int ssoff = MG::SB < 4 ? ((c.gr * MG::SB) & ~3) : c.gr * MG::SB;
-    if (s_live) {
-      lds_dma<SSZ>(sr, slot + MG::WBYTES, s_voff, ssoff);
-      lds_dma<SSZ>(br, slot + MG::WBYTES + 16 * MG::SBP, s_voff, ssoff);
+    const int sv = s_live ? s_voff : 0x7ffffff0;
+    if constexpr (SSZ == 16) {
+      const u32x4 a4 = __builtin_amdgcn_raw_buffer_load_b128(sr, sv, ssoff, 0);
+      const u32x4 b4 = __builtin_amdgcn_raw_buffer_load_b128(br, sv, ssoff, 0);
+      sg.s[0] = a4.x; sg.s[1] = a4.y; sg.s[2] = a4.z; sg.s[3] = a4.w;
+      sg.b[0] = b4.x; sg.b[1] = b4.y; sg.b[2] = b4.z; sg.b[3] = b4.w;
+    } else {
+      sg.s[0] = __builtin_amdgcn_raw_buffer_load_b32(sr, sv, ssoff, 0);
+      sg.b[0] = __builtin_amdgcn_raw_buffer_load_b32(br, sv, ssoff, 0);
     }
   };
 
@@ -1142,8 +1112,46 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
   for (int mb = 0; mb < NMB; ++mb) acc[mb] = 0.0f;
   int mcount = 0;
 
-  auto compute = [&](const Cursor& c) {
-    const unsigned char* slot = ring + c.sl * MG::SLOT;
+  // per-lane LDS offsets (from smem) of the A operand and unit sums of each
+  // 4-row block, set for each pass of window rows and advanced per group
+  int a_base[NMB], x_base[NMB], a_live[NMB];
+  auto set_bases = [&]() {
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+      const int ai = lane % 16, am = 4 * mb + ai / 4;
+      // lane (row ai, k-quarter qd) is live when its quarter is its row's
+      // unit and the window row exists
+      const bool live = (qd == ai % 4) && (am < mcount);
+      a_live[mb] = live ? 1 : 0;
+      a_base[mb] = live ? am * xstride + qd * 64 : mrows * xstride;
+      const int em = 4 * mb + qd;
+      x_base[mb] = mrows * xstride + ZB + (em < mcount ? em : 0) * units * 4;
+    }
+  };
+
+  auto compute = [&](const Stage& sg, const Cursor& c) {
+    // hand the group over: lane order in, the slot layout out (the wave's
+    // previous reads of the slot precede these writes in its LDS queue)
+#pragma unroll
+    for (int t = 0; t < MG::WLD; ++t) reinterpret_cast<u32x4*>(slot)[t * kWave + lane] = sg.w[t];
+    if (s_live) {
+      if constexpr (SSZ == 16) {
+        u32x4 a4, b4;
+        a4.x = sg.s[0]; a4.y = sg.s[1]; a4.z = sg.s[2]; a4.w = sg.s[3];
+        b4.x = sg.b[0]; b4.y = sg.b[1]; b4.z = sg.b[2]; b4.w = sg.b[3];
+        reinterpret_cast<u32x4*>(slot + MG::WBYTES)[lane] = a4;
+        reinterpret_cast<u32x4*>(slot + MG::WBYTES + 16 * MG::SBP)[lane] = b4;
+      } else {
+        reinterpret_cast<uint32_t*>(slot + MG::WBYTES)[lane] = sg.s[0];
+        reinterpret_cast<uint32_t*>(slot + MG::WBYTES + 16 * MG::SBP)[lane] = sg.b[0];
+      }
+    }
+    int a_grp[NMB], x_grp[NMB];
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+      a_grp[mb] = a_base[mb] + a_live[mb] * (c.gr * R * 256);
+      x_grp[mb] = x_base[mb] + c.gr * R * 16;
+    }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       uint32_t wu[B];
@@ -1166,9 +1174,9 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
       // scales and biases of the round's four units
       float sv[4], bv[4];
       if constexpr (G == 32) {
-        const u32x2 sg = *reinterpret_cast<const u32x2*>(slot + s_off + r * 8);
-        const u32x2 bg = *reinterpret_cast<const u32x2*>(slot + b_off + r * 8);
-        const uint32_t sw[2] = {sg.x, sg.y}, bw[2] = {bg.x, bg.y};
+        const u32x2 sgv = *reinterpret_cast<const u32x2*>(slot + s_off + r * 8);
+        const u32x2 bgv = *reinterpret_cast<const u32x2*>(slot + b_off + r * 8);
+        const uint32_t sw[2] = {sgv.x, sgv.y}, bw[2] = {bgv.x, bgv.y};
 #pragma unroll
         for (int q2 = 0; q2 < 4; ++q2) {
           sv[q2] = group_value<4>(sw, q2);
@@ -1196,53 +1204,46 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
           bv[q2] = b1;
         }
       }
-      const int unit0 = (c.gr * R + r) * 4;
-      // A operand of every 4-row block: lane (row ai = lane % 16, k-quarter
-      // qd) reads its row's activations when its quarter is its row's unit
-      // and the window row exists, else the zero line
+      // A operand and unit sums of every 4-row block (rows past the window
+      // read zeros and are never stored)
       u32x4 av[NMB][4];
       f32x4_t xsv[NMB];
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb) {
-        if (4 * mb < mcount) {
-          const int ai = lane % 16, am = 4 * mb + ai / 4;
-          const bool live = (qd == ai % 4) && (am < mcount);
-          const unsigned char* abase = live ? xs + am * xstride + (unit0 + qd) * 64 : zero_line;
 #pragma unroll
-          for (int sidx = 0; sidx < 4; ++sidx)
-            av[mb][sidx] = *reinterpret_cast<const u32x4*>(abase + (live ? sidx * 16 : 0));
-          const int em = 4 * mb + qd;
-          xsv[mb] = *reinterpret_cast<const f32x4_t*>(xsum + static_cast<size_t>(em < mcount ? em : 0) * units + unit0);
-        }
+        for (int sidx = 0; sidx < 4; ++sidx)
+          av[mb][sidx] = *reinterpret_cast<const u32x4*>(smem + a_grp[mb] + r * 256 + sidx * 16);
+        xsv[mb] = *reinterpret_cast<const f32x4_t*>(smem + x_grp[mb] + r * 16);
       }
       // B operand: this lane's unit as 16 exact bf16 pairs
       uint32_t qp[16];
       unpack_codes<B, 32>(wu, qp);
+      f32x4_t d[NMB];
 #pragma unroll
-      for (int mb = 0; mb < NMB; ++mb) {
-        if (4 * mb < mcount) {
-          f32x4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int mb = 0; mb < NMB; ++mb) d[mb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-          for (int sidx = 0; sidx < 4; ++sidx) {
-            u32x4 bq;
-            bq.x = qp[4 * sidx];
-            bq.y = qp[4 * sidx + 1];
-            bq.z = qp[4 * sidx + 2];
-            bq.w = qp[4 * sidx + 3];
-            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[mb][sidx]),
-                                                        __builtin_bit_cast(bf16x8_t, bq), d, 0, 0, 0);
-          }
-          // lane = (window row 4mb + qd, column j): units q2 = 0..3 in order
+      for (int sidx = 0; sidx < 4; ++sidx) {
+        u32x4 bq;
+        bq.x = qp[4 * sidx];
+        bq.y = qp[4 * sidx + 1];
+        bq.z = qp[4 * sidx + 2];
+        bq.w = qp[4 * sidx + 3];
 #pragma unroll
-          for (int q2 = 0; q2 < 4; ++q2) {
-            acc[mb] = __builtin_fmaf(sv[q2], d[q2], acc[mb]);
-            acc[mb] = __builtin_fmaf(bv[q2], xsv[mb][q2], acc[mb]);
-          }
-        }
+        for (int mb = 0; mb < NMB; ++mb)
+          d[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[mb][sidx]),
+                                                          __builtin_bit_cast(bf16x8_t, bq), d[mb], 0, 0, 0);
       }
+      // lane = (window row 4mb + qd, column j): units q2 = 0..3 in order
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) {
+          acc[mb] = __builtin_fmaf(sv[q2], d[mb][q2], acc[mb]);
+          acc[mb] = __builtin_fmaf(bv[q2], xsv[mb][q2], acc[mb]);
+        }
     }
     if (c.gr == groups - 1) {
-      const int col = ((bx + c.i * gx) * kMWaves + wv) * 16 + j;
+      const int col = ((bx + c.i * gx) * NW + wv) * 16 + j;
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb) {
         const int em = 4 * mb + qd;
@@ -1256,12 +1257,11 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
 
   for (int c0 = 0; c0 < total; c0 += MB) {
     mcount = min(MB, total - c0);
-    // the first D-1 groups are in flight while the window is staged
-    Cursor ci = {0, 0, 0, 0}, cc = {0, 0, 0, 0};
-    for (int st = 0; st < D - 1; ++st) {
-      issue(ci);
-      advance(ci);
-    }
+    // the first group's loads are in flight while the window is staged
+    Cursor cl = {0, 0, 0}, cc = {0, 0, 0};
+    Stage sa, sb;
+    load_stage(sa, cl);
+    advance(cl);
     if (tid < mcount) {
       const int e = c0 + tid;
       if (p.indexed) {
@@ -1274,10 +1274,11 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
         s_yoff[tid] = static_cast<int64_t>(e) * p.ldy;
       }
     }
-    if (tid < 16) reinterpret_cast<uint32_t*>(zero_line)[tid] = 0u;
+    for (int t = tid; t < ZB / 4; t += NT) reinterpret_cast<uint32_t*>(zero_area)[t] = 0u;
+    set_bases();
     __syncthreads();
     // ---- stage the window: each unit's activations in slot order, and its sum ----
-    for (int t = tid; t < mcount * units; t += kMThreads) {
+    for (int t = tid; t < mcount * units; t += NT) {
       const int mi = t / units, un = t - (t / units) * units;
       const u32x4* src = reinterpret_cast<const u32x4*>(p.x + static_cast<int64_t>(s_xrow[mi]) * p.k +
                                                         static_cast<int64_t>(un) * 32);
@@ -1292,7 +1293,7 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
       }
       float X = 0.0f;
       const uint32_t ones = 0x3f803f80u;  // bf16 pair {1, 1}
-      u32x4* dst = reinterpret_cast<u32x4*>(xs + mi * xstride + un * 64);
+      u32x4* dst = reinterpret_cast<u32x4*>(smem + mi * xstride + un * 64);
 #pragma unroll
       for (int pc = 0; pc < 4; ++pc) {
         u32x4 o;
@@ -1309,21 +1310,27 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
       xsum[mi * units + un] = X;
     }
     __syncthreads();
-    for (; cc.st < steps; advance(cc)) {
-      issue(ci);
-      advance(ci);
-      wait_groups<MG::NDMA>(D - 1);   // the group at cc has landed
-      compute(cc);
+    // double-buffered: a group's loads are in flight while the previous one
+    // is computed
+    while (cc.st < steps) {
+      load_stage(sb, cl);
+      advance(cl);
+      compute(sa, cc);
+      advance(cc);
+      if (cc.st >= steps) break;
+      load_stage(sa, cl);
+      advance(cl);
+      compute(sb, cc);
+      advance(cc);
     }
-    vm_wait<0>();       // no load may still be writing this wave's ring
     __syncthreads();    // LDS window reused by the next pass of routed rows
   }
 }
 
 template <int B, int G, int MB>
-__global__ __launch_bounds__(kMThreads) void qrow_mfma(const Params p) {
+__global__ __launch_bounds__(MWaves<MB>::v * kWave) void qrow_mfma(const Params p) {
   extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ int s_wave_cnt[kMWaves];
+  __shared__ int s_wave_cnt[MWaves<MB>::v];
   __shared__ int s_xrow[QGEMV_MAX_WINDOW];
   __shared__ int64_t s_yoff[QGEMV_MAX_WINDOW];
   mfma_body<B, G, MB>(p, blockIdx.x, gridDim.x, smem, s_wave_cnt, s_xrow, s_yoff);
@@ -1446,9 +1453,9 @@ struct Entry {
   KernelFn generic[5];  // by window variant: one-unit chunks, any lane count
   int fast_rows[5];     // columns per lane of the fast kernels
   int generic_rows[5];
-  KernelFn mfma[5];     // matrix-core kernels by window variant (kMThreads threads)
-  int mfma_slot;        // bytes of one ring slot (one load group of a wave)
-  int mfma_dmax;        // deepest ring the load counter can track
+  KernelFn mfma[5];     // matrix-core kernels by window variant
+  int mfma_slot;        // bytes of one wave's LDS slot (one load group)
+  int mfma_waves[5];    // waves per block of the matrix-core kernels by window variant
   int mfma_group;       // 128-code rounds per load group (k is a multiple of 128 * this)
   int mfma_salign;      // alignment the scale and bias arrays need (bytes)
 };
@@ -1489,8 +1496,12 @@ Entry make_entry() {
   e.mfma[3] = qrow_mfma<B, G, 8>;
   e.mfma[4] = qrow_mfma<B, G, 16>;
   e.mfma_slot = MGroup<B, G>::SLOT;
-  e.mfma_dmax = MGroup<B, G>::DMAX;
   e.mfma_group = MGroup<B, G>::R;
+  e.mfma_waves[0] = MWaves<1>::v;
+  e.mfma_waves[1] = MWaves<2>::v;
+  e.mfma_waves[2] = MWaves<4>::v;
+  e.mfma_waves[3] = MWaves<8>::v;
+  e.mfma_waves[4] = MWaves<16>::v;
   e.mfma_salign = MGroup<B, G>::S16 ? 16 : 4;
   return e;
 }
