@@ -167,7 +167,7 @@ class Workload:
             self.copies.append((trip_list, mats))
         self.flat = self.y.view(-1)
         first = self.copies[0][1][0]
-        self.arith_used = "dot" if self.kind == "fused" else ARITH_NAMES[first.arith]
+        self.arith_used = "auto" if self.kind == "fused" else ARITH_NAMES[first.arith]
 
     def step(self, i: int, stream: int):
         _, mats = self.copies[i % len(self.copies)]

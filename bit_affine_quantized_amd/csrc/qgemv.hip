@@ -90,6 +90,16 @@ struct DeviceInfo {
 constexpr int kMaxDevices = 64;
 DeviceInfo g_devices[kMaxDevices];
 
+qg::StackKernels stack_kernels(int var) {
+  switch (var) {
+    case 0: return qg::stack_kernels_m1();
+    case 1: return qg::stack_kernels_m2();
+    case 2: return qg::stack_kernels_m4();
+    case 3: return qg::stack_kernels_m8();
+    default: return qg::stack_kernels_m16();
+  }
+}
+
 void init_device(DeviceInfo* info) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return;
@@ -110,11 +120,14 @@ void init_device(DeviceInfo* info) {
           return;
       }
     }
-  for (qg::StackFn fn : {qg::stack_kernel_m1(), qg::stack_kernel_m2(), qg::stack_kernel_m4(),
-                         qg::stack_kernel_m8(), qg::stack_kernel_m16()})
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            static_cast<int>(qg::kMaxDynamicLds)) != hipSuccess)
+  for (int v = 0; v < 5; ++v) {
+    const qg::StackKernels sk = stack_kernels(v);
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(sk.dot), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(qg::kMaxDynamicLds)) != hipSuccess ||
+        hipFuncSetAttribute(reinterpret_cast<const void*>(sk.mfma), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(qg::kMaxMfmaLds)) != hipSuccess)
       return;
+  }
   info->cus = cus;
   info->status = QGEMV_OK;
 }
@@ -354,12 +367,14 @@ int qgemv_create_arith(const qgemv_desc* d, int32_t arith, qgemv_t* out) {
   while (lpr < 64 && h.nchunks % (lpr * 2) == 0) lpr *= 2;
   h.lpr = lpr;
   h.cpl = h.nchunks / lpr;
-  // arithmetic: the dot form unless the matrix cores are asked for
+  // arithmetic: the matrix cores when asked for or when left to the library
+  // and the shape allows them, else the dot form
   const uintptr_t sb = reinterpret_cast<uintptr_t>(d->scales) | reinterpret_cast<uintptr_t>(d->biases);
   const bool mfma_ok = d->k % qgemv_mfma_codes(d->bits, d->group) == 0 &&
                        sb % static_cast<uintptr_t>(h.entry->mfma_salign) == 0;
   if (arith == QGEMV_ARITH_MFMA && !mfma_ok) return QGEMV_E_NOKERNEL;
-  h.arith = arith == QGEMV_ARITH_MFMA ? QGEMV_ARITH_MFMA : QGEMV_ARITH_DOT;
+  h.arith = (arith == QGEMV_ARITH_MFMA || (arith == QGEMV_ARITH_AUTO && mfma_ok)) ? QGEMV_ARITH_MFMA
+                                                                               : QGEMV_ARITH_DOT;
   {
     // groups one packed scale load spans: a lane chunk's, or a 128-code
     // macro step's for the matrix-core form
@@ -456,7 +471,7 @@ struct qgemv_stack {
   int n_members[qg::kMaxRuns];
   int64_t member_rows[qg::kMaxRuns][qg::kMaxSeg];
   int64_t member_cols[qg::kMaxRuns][qg::kMaxSeg];
-  mutable std::atomic<int> occupancy[5];
+  mutable std::atomic<int> occupancy[5][2];   // by window variant and form (0 dot, 1 matrix-core)
   ~qgemv_stack() {
     for (int r = 0; r < n_runs; ++r) delete run[r];
   }
@@ -468,7 +483,8 @@ int qgemv_stack_create(const qgemv_run_spec* runs, int32_t n_runs, int64_t ldy, 
   if (ldy < 1) return QGEMV_E_STRIDE;
   std::unique_ptr<qgemv_stack> st(new (std::nothrow) qgemv_stack());
   if (!st) return QGEMV_E_ARG;
-  for (auto& o : st->occupancy) o.store(0);
+  for (auto& row : st->occupancy)
+    for (auto& o : row) o.store(0);
   st->ldy = ldy;
   st->n_runs = 0;
   int64_t ranges[qg::kMaxRuns * qg::kMaxSeg][2];
@@ -481,7 +497,7 @@ int qgemv_stack_create(const qgemv_run_spec* runs, int32_t n_runs, int64_t ldy, 
     st->run[st->n_runs++] = h;
     if (rr.w.n_experts != 1) return QGEMV_E_ARG;
     if (rr.w.k != runs[0].w.k) return QGEMV_E_SHAPE;
-    if (!h->fast) return QGEMV_E_NOKERNEL;
+    if (h->arith == QGEMV_ARITH_DOT && !h->fast) return QGEMV_E_NOKERNEL;
     if (rr.n_members < 1 || rr.n_members > qg::kMaxSeg) return QGEMV_E_ARG;
     int64_t rows = 0;
     for (int mbr = 0; mbr < rr.n_members; ++mbr) {
@@ -507,43 +523,62 @@ int qgemv_stack_create(const qgemv_run_spec* runs, int32_t n_runs, int64_t ldy, 
 
 void qgemv_stack_destroy(qgemv_stack_t s) { delete s; }
 
-int qgemv_stack_run(qgemv_stack_t s, const uint16_t* x, int32_t m, float* y, int32_t epi, void* stream) {
-  if (!s) return QGEMV_E_ARG;
-  if (m < 0 || m > QGEMV_MAX_WINDOW) return QGEMV_E_WINDOW;
-  if (epi != QGEMV_EPI_NONE && epi != QGEMV_EPI_RELU2) return QGEMV_E_ARG;
-  if (m == 0) return QGEMV_OK;
-  if (!x || !y) return QGEMV_E_ARG;
-  if ((reinterpret_cast<uintptr_t>(x) & 15) || (reinterpret_cast<uintptr_t>(y) & 3)) return QGEMV_E_ALIGN;
-  const int64_t k = s->run[0]->d.k;
-  const size_t xbytes = static_cast<size_t>(m) * k * 2;
-  const size_t ybytes = (static_cast<size_t>(m - 1) * s->ldy + s->col_end) * 4;
-  if (ybytes > 0x7fffffffu) return QGEMV_E_STRIDE;
-  for (int r = 0; r < s->n_runs; ++r) {
-    const int rc = check_y_alias(s->run[r], y, ybytes, x, xbytes, nullptr, 0);
-    if (rc != QGEMV_OK) return rc;
-  }
-  const DeviceInfo* dev = current_device();
-  if (!dev) return QGEMV_E_HIP;
-  const int var = window_variant(m);
-  qg::StackParams sp{};
-  sp.nruns = s->n_runs;
+}  // extern "C"
+
+namespace {
+
+// One dispatch over the runs of a stack that share an arithmetic form.
+int launch_stack(const qgemv_stack* s, bool mfma, const uint16_t* x, int32_t m, float* y, int32_t epi,
+                 void* stream, size_t ybytes, const DeviceInfo* dev) {
+  int idx[qg::kMaxRuns];
+  int nr = 0;
+  for (int r = 0; r < s->n_runs; ++r)
+    if ((s->run[r]->arith == QGEMV_ARITH_MFMA) == mfma) idx[nr++] = r;
+  if (nr == 0) return QGEMV_OK;
+  int var = window_variant(m);
   size_t lds = 0;
+  if (mfma) {
+    // the widest variant whose LDS every run fits (narrower ones run the
+    // window as passes, same bits)
+    for (;; --var) {
+      lds = 0;
+      bool fits = true;
+      for (int q = 0; q < nr && fits; ++q) {
+        size_t l = 0;
+        fits = mfma_plan(s->run[idx[q]], var, false, &l);
+        if (l > lds) lds = l;
+      }
+      if (fits) break;
+      if (var == 0) return QGEMV_E_WINDOW;
+    }
+  }
+  qg::StackParams sp{};
+  sp.nruns = nr;
   int64_t tiles[qg::kMaxRuns];
   int64_t total_tiles = 0;
-  for (int r = 0; r < s->n_runs; ++r) {
+  int threads = qg::kThreads;
+  for (int q = 0; q < nr; ++q) {
+    const int r = idx[q];
     const qgemv_handle* h = s->run[r];
-    int stage = h->ppc > 1 ? 1 : 0;
-    if (stage && lds_bytes(h, var, 1) > qg::kMaxDynamicLds) stage = 0;
-    const size_t l = lds_bytes(h, var, stage);
-    if (l > qg::kMaxDynamicLds) return QGEMV_E_WINDOW;
-    if (l > lds) lds = l;
-    const int R = h->entry->fast_rows[var];
-    const int64_t tile_rows = static_cast<int64_t>(qg::kWaves) * (qg::kWave / h->lpr) * R;
-    tiles[r] = (h->d.n + tile_rows - 1) / tile_rows;
-    total_tiles += tiles[r];
     const int bi = qg::bits_index(h->d.bits), gi = qg::group_index(h->d.group);
-    sp.kind[r] = (bi * 3 + gi) * 2 + stage;
-    qg::Params& p = sp.run[r];
+    int64_t tile_rows = 0;
+    if (mfma) {
+      threads = h->entry->mfma_waves[var] * qg::kWave;
+      tile_rows = static_cast<int64_t>(h->entry->mfma_waves[var]) * 16;
+      sp.kind[q] = bi * 3 + gi;
+    } else {
+      int stage = h->ppc > 1 ? 1 : 0;
+      if (stage && lds_bytes(h, var, 1) > qg::kMaxDynamicLds) stage = 0;
+      const size_t l = lds_bytes(h, var, stage);
+      if (l > qg::kMaxDynamicLds) return QGEMV_E_WINDOW;
+      if (l > lds) lds = l;
+      const int R = h->entry->fast_rows[var];
+      tile_rows = static_cast<int64_t>(qg::kWaves) * (qg::kWave / h->lpr) * R;
+      sp.kind[q] = (bi * 3 + gi) * 2 + stage;
+    }
+    tiles[q] = (h->d.n + tile_rows - 1) / tile_rows;
+    total_tiles += tiles[q];
+    qg::Params& p = sp.run[q];
     p.w = h->d.w;
     p.scales = h->d.scales;
     p.biases = h->d.biases;
@@ -562,7 +597,7 @@ int qgemv_stack_run(qgemv_stack_t s, const uint16_t* x, int32_t m, float* y, int
     p.lpr = h->lpr;
     p.cpl = h->cpl;
     p.nchunks = h->nchunks;
-    p.tiles = static_cast<int32_t>(tiles[r]);
+    p.tiles = static_cast<int32_t>(tiles[q]);
     p.indexed = 0;
     p.vec_groups = h->vec_groups;
     p.y_bytes = static_cast<int64_t>(ybytes);
@@ -574,41 +609,62 @@ int qgemv_stack_run(qgemv_stack_t s, const uint16_t* x, int32_t m, float* y, int
       row0 += s->member_rows[r][mbr];
     }
   }
-  qg::StackFn fn = nullptr;
-  switch (var) {
-    case 0: fn = qg::stack_kernel_m1(); break;
-    case 1: fn = qg::stack_kernel_m2(); break;
-    case 2: fn = qg::stack_kernel_m4(); break;
-    case 3: fn = qg::stack_kernel_m8(); break;
-    default: fn = qg::stack_kernel_m16(); break;
-  }
-  int occ = s->occupancy[var].load(std::memory_order_relaxed);
+  const qg::StackKernels sk = stack_kernels(var);
+  const qg::StackFn fn = mfma ? sk.mfma : sk.dot;
+  int occ = s->occupancy[var][mfma].load(std::memory_order_relaxed);
   if (occ == 0) {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(fn), qg::kThreads,
-                                                     lds) != hipSuccess || nb < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(fn), threads, lds) !=
+            hipSuccess || nb < 1)
       nb = 1;
     occ = nb;
-    s->occupancy[var].store(occ, std::memory_order_relaxed);
+    s->occupancy[var][mfma].store(occ, std::memory_order_relaxed);
   }
   // blocks per run: every tile its own block when the CUs hold them all,
   // else a share of the resident blocks in proportion to the run's tiles
   const int64_t cap = static_cast<int64_t>(dev->cus) * occ;
   int64_t b0 = 0;
-  for (int r = 0; r < s->n_runs; ++r) {
-    int64_t nb = tiles[r];
+  for (int q = 0; q < nr; ++q) {
+    int64_t nb = tiles[q];
     if (total_tiles > cap) {
-      nb = cap * tiles[r] / total_tiles;
+      nb = cap * tiles[q] / total_tiles;
       if (nb < 1) nb = 1;
-      if (nb > tiles[r]) nb = tiles[r];
+      if (nb > tiles[q]) nb = tiles[q];
     }
-    sp.block0[r] = static_cast<int32_t>(b0);
+    sp.block0[q] = static_cast<int32_t>(b0);
     b0 += nb;
   }
-  sp.block0[s->n_runs] = static_cast<int32_t>(b0);
-  hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(b0)), dim3(qg::kThreads), lds,
-                     static_cast<hipStream_t>(stream), sp);
+  sp.block0[nr] = static_cast<int32_t>(b0);
+  hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(b0)), dim3(threads), lds, static_cast<hipStream_t>(stream), sp);
   return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_E_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qgemv_stack_run(qgemv_stack_t s, const uint16_t* x, int32_t m, float* y, int32_t epi, void* stream) {
+  if (!s) return QGEMV_E_ARG;
+  if (m < 0 || m > QGEMV_MAX_WINDOW) return QGEMV_E_WINDOW;
+  if (epi != QGEMV_EPI_NONE && epi != QGEMV_EPI_RELU2) return QGEMV_E_ARG;
+  if (m == 0) return QGEMV_OK;
+  if (!x || !y) return QGEMV_E_ARG;
+  if ((reinterpret_cast<uintptr_t>(x) & 15) || (reinterpret_cast<uintptr_t>(y) & 3)) return QGEMV_E_ALIGN;
+  const int64_t k = s->run[0]->d.k;
+  const size_t xbytes = static_cast<size_t>(m) * k * 2;
+  const size_t ybytes = (static_cast<size_t>(m - 1) * s->ldy + s->col_end) * 4;
+  if (ybytes > 0x7fffffffu) return QGEMV_E_STRIDE;
+  for (int r = 0; r < s->n_runs; ++r) {
+    const int rc = check_y_alias(s->run[r], y, ybytes, x, xbytes, nullptr, 0);
+    if (rc != QGEMV_OK) return rc;
+  }
+  const DeviceInfo* dev = current_device();
+  if (!dev) return QGEMV_E_HIP;
+  // one dispatch per arithmetic form present (one, unless some run's shape
+  // rules out the matrix cores)
+  int rc = launch_stack(s, true, x, m, y, epi, stream, ybytes, dev);
+  if (rc != QGEMV_OK) return rc;
+  return launch_stack(s, false, x, m, y, epi, stream, ybytes, dev);
 }
 
 int qgemv_query(qgemv_t h, int64_t out[6]) {

@@ -1350,6 +1350,38 @@ struct StackParams {
   int32_t nruns;
 };
 
+// The block's run (blocks [block0[r], block0[r+1]) belong to run r), its
+// place among that run's blocks, its parameters and its kernel kind.  Written
+// out in each kernel (a macro, not a function taking the argument struct by
+// reference), and with constant indices only: either of the other forms
+// copies the whole argument struct to scratch.
+#define QG_SELECT_RUN(sp, p, bx, gx, kind)                                   \
+  do {                                                                       \
+    int r_ = 0, lo_ = (sp).block0[0], hi_ = (sp).block0[1];                  \
+    _Pragma("unroll") for (int q_ = 1; q_ < kMaxRuns; ++q_) if (             \
+        q_ < (sp).nruns && static_cast<int>(blockIdx.x) >= (sp).block0[q_]) { \
+      r_ = q_;                                                               \
+      lo_ = (sp).block0[q_];                                                 \
+      hi_ = (sp).block0[q_ + 1];                                             \
+    }                                                                        \
+    bx = static_cast<int>(blockIdx.x) - lo_;                                 \
+    gx = hi_ - lo_;                                                          \
+    switch (r_) {                                                            \
+      case 0: p = (sp).run[0]; break;                                        \
+      case 1: p = (sp).run[1]; break;                                        \
+      case 2: p = (sp).run[2]; break;                                        \
+      case 3: p = (sp).run[3]; break;                                        \
+      case 4: p = (sp).run[4]; break;                                        \
+      case 5: p = (sp).run[5]; break;                                        \
+      case 6: p = (sp).run[6]; break;                                        \
+      default: p = (sp).run[7]; break;                                       \
+    }                                                                        \
+    kind = (sp).kind[0];                                                     \
+    _Pragma("unroll") for (int q_ = 1; q_ < kMaxRuns; ++q_) if (q_ == r_) kind = (sp).kind[q_]; \
+  } while (0)
+static_assert(kMaxRuns == 8, "one case per run");
+
+// Dot-form runs: kind = (bits index * 3 + group index) * 2 + staging.
 template <int MB>
 __global__ __launch_bounds__(kThreads) void qrow_stack(const StackParams sp) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -1357,30 +1389,9 @@ __global__ __launch_bounds__(kThreads) void qrow_stack(const StackParams sp) {
   __shared__ int s_wave_cnt[kWaves];
   __shared__ int s_xrow[QGEMV_MAX_WINDOW];
   __shared__ int64_t s_yoff[QGEMV_MAX_WINDOW];
-  int r = 0, lo = sp.block0[0], hi = sp.block0[1];
-#pragma unroll
-  for (int q = 1; q < kMaxRuns; ++q)
-    if (q < sp.nruns && static_cast<int>(blockIdx.x) >= sp.block0[q]) {
-      r = q;
-      lo = sp.block0[q];
-      hi = sp.block0[q + 1];
-    }
-  const int bx = static_cast<int>(blockIdx.x) - lo;
-  const int gx = hi - lo;
-  // the run's parameters, selected with constant indices (a run-time index
-  // into the argument struct would copy all of it to scratch)
   Params p;
-  switch (r) {
-    case 0: p = sp.run[0]; break;
-    case 1: p = sp.run[1]; break;
-    case 2: p = sp.run[2]; break;
-    case 3: p = sp.run[3]; break;
-    case 4: p = sp.run[4]; break;
-    case 5: p = sp.run[5]; break;
-    case 6: p = sp.run[6]; break;
-    default: p = sp.run[7]; break;
-  }
-  static_assert(kMaxRuns == 8, "one case per run");
+  int bx, gx, kind;
+  QG_SELECT_RUN(sp, p, bx, gx, kind);
 // (the empty asm keeps each case's parameter loads inside the case, so no
 // value is live across the switch)
 #define QG_BODY(B, G, STG)               \
@@ -1396,10 +1407,41 @@ __global__ __launch_bounds__(kThreads) void qrow_stack(const StackParams sp) {
     if constexpr (Geo<B>::PPC > 1) QG_BODY(B, G, true); \
     break;
 #define QG_WIDTH(BI, B) QG_PAIR(BI, B, 0, 32) QG_PAIR(BI, B, 1, 64) QG_PAIR(BI, B, 2, 128)
-  int kind = sp.kind[0];
-#pragma unroll
-  for (int q = 1; q < kMaxRuns; ++q)
-    if (q == r) kind = sp.kind[q];
+  switch (kind) {
+    QG_WIDTH(0, 2)
+    QG_WIDTH(1, 3)
+    QG_WIDTH(2, 4)
+    QG_WIDTH(3, 5)
+    QG_WIDTH(4, 6)
+    QG_WIDTH(5, 8)
+    default:
+      break;
+  }
+#undef QG_WIDTH
+#undef QG_PAIR
+#undef QG_BODY
+}
+
+// Matrix-core runs: kind = bits index * 3 + group index.
+template <int MB>
+__global__ __launch_bounds__(MWaves<MB>::v * kWave) void qrow_stack_mfma(const StackParams sp) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int s_wave_cnt[MWaves<MB>::v];
+  __shared__ int s_xrow[QGEMV_MAX_WINDOW];
+  __shared__ int64_t s_yoff[QGEMV_MAX_WINDOW];
+  Params p;
+  int bx, gx, kind;
+  QG_SELECT_RUN(sp, p, bx, gx, kind);
+#define QG_BODY(B, G)                    \
+  do {                                   \
+    asm volatile("" ::: "memory");       \
+    mfma_body<B, G, MB>(p, bx, gx, smem, s_wave_cnt, s_xrow, s_yoff); \
+  } while (0)
+#define QG_PAIR(BI, B, GI, G) \
+  case (BI) * 3 + (GI):       \
+    QG_BODY(B, G);            \
+    break;
+#define QG_WIDTH(BI, B) QG_PAIR(BI, B, 0, 32) QG_PAIR(BI, B, 1, 64) QG_PAIR(BI, B, 2, 128)
   switch (kind) {
     QG_WIDTH(0, 2)
     QG_WIDTH(1, 3)
@@ -1515,13 +1557,17 @@ const Entry* entries_b5();
 const Entry* entries_b6();
 const Entry* entries_b8();
 
-// Fused-stack kernels by window variant (1, 2, 4, 8, 16 rows), one
-// translation unit each.
+// Fused-stack kernels (both arithmetic forms) by window variant (1, 2, 4,
+// 8, 16 rows), one translation unit each.
 typedef void (*StackFn)(const StackParams);
-StackFn stack_kernel_m1();
-StackFn stack_kernel_m2();
-StackFn stack_kernel_m4();
-StackFn stack_kernel_m8();
-StackFn stack_kernel_m16();
+struct StackKernels {
+  StackFn dot;    // qrow_stack<MB>
+  StackFn mfma;   // qrow_stack_mfma<MB>
+};
+StackKernels stack_kernels_m1();
+StackKernels stack_kernels_m2();
+StackKernels stack_kernels_m4();
+StackKernels stack_kernels_m8();
+StackKernels stack_kernels_m16();
 
 }  // namespace qg

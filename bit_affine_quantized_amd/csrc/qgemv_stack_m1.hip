@@ -1,8 +1,8 @@
-// Fused-stack kernel for windows of up to 1 row.
+// Fused-stack kernels (dot and matrix-core forms) for one-row windows.
 #include "qgemv_kernels.h"
 
 namespace qg {
 
-StackFn stack_kernel_m1() { return qrow_stack<1>; }
+StackKernels stack_kernels_m1() { return {qrow_stack<1>, qrow_stack_mfma<1>}; }
 
 }  // namespace qg

@@ -1,8 +1,8 @@
-// Fused-stack kernel for windows of up to 16 rows.
+// Fused-stack kernels (dot and matrix-core forms) for windows of up to 16 rows.
 #include "qgemv_kernels.h"
 
 namespace qg {
 
-StackFn stack_kernel_m16() { return qrow_stack<16>; }
+StackKernels stack_kernels_m16() { return {qrow_stack<16>, qrow_stack_mfma<16>}; }
 
 }  // namespace qg

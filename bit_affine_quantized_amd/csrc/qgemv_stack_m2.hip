@@ -1,8 +1,8 @@
-// Fused-stack kernel for windows of up to 2 rows.
+// Fused-stack kernels (dot and matrix-core forms) for windows of up to 2 rows.
 #include "qgemv_kernels.h"
 
 namespace qg {
 
-StackFn stack_kernel_m2() { return qrow_stack<2>; }
+StackKernels stack_kernels_m2() { return {qrow_stack<2>, qrow_stack_mfma<2>}; }
 
 }  // namespace qg

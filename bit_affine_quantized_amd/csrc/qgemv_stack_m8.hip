@@ -1,8 +1,8 @@
-// Fused-stack kernel for windows of up to 8 rows.
+// Fused-stack kernels (dot and matrix-core forms) for windows of up to 8 rows.
 #include "qgemv_kernels.h"
 
 namespace qg {
 
-StackFn stack_kernel_m8() { return qrow_stack<8>; }
+StackKernels stack_kernels_m8() { return {qrow_stack<8>, qrow_stack_mfma<8>}; }
 
 }  // namespace qg

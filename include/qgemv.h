@@ -115,7 +115,9 @@ int qgemv_create(const qgemv_desc* d, qgemv_t* out);
  *                     units in order, no butterfly.  Needs k a multiple of
  *                     qgemv_mfma_codes(bits, group) and aligned scales
  *                     and biases (QGEMV_E_NOKERNEL otherwise).
- *   QGEMV_ARITH_AUTO  the library's choice (what qgemv_create uses).      */
+ *   QGEMV_ARITH_AUTO  the library's choice (what qgemv_create uses): the
+ *                     MFMA form when the shape and alignment allow it,
+ *                     else the dot form.                                  */
 #define QGEMV_ARITH_AUTO 0
 #define QGEMV_ARITH_DOT 1
 #define QGEMV_ARITH_MFMA 2
@@ -183,7 +185,9 @@ const char* qgemv_strerror(int status);
  * A fused projection is a set of runs sharing one input: each run is one
  * matrix of one width and group, and its members (consecutive row ranges of
  * the run) write their own columns of one output row of ldy columns, with no
- * scratch copy.  qgemv_stack_run computes every run in ONE dispatch; each
+ * scratch copy.  qgemv_stack_run computes every run in ONE dispatch per
+ * arithmetic form present (each run takes qgemv_create's choice, so one
+ * dispatch unless some run's shape rules out the matrix cores); each
  * member's columns are bit for bit what qgemv_run_strided of that run's own
  * handle writes there (same kernels, same arithmetic).  Columns outside every
  * member are left untouched.
@@ -209,9 +213,9 @@ typedef struct qgemv_stack* qgemv_stack_t;
  * then: 1 <= n_runs <= QGEMV_MAX_RUNS, every run has the same k (else
  * QGEMV_E_SHAPE), member rows are >= 1 and sum to the run's n (QGEMV_E_SHAPE),
  * every member's columns lie in [0, ldy) (QGEMV_E_STRIDE), no two members
- * share a column (QGEMV_E_ALIAS), and every run has k a whole number of
- * 16-lane chunks (QGEMV_E_NOKERNEL otherwise).  Borrows the weight pointers;
- * makes no HIP call. */
+ * share a column (QGEMV_E_ALIAS), and every dot-form run has k a whole
+ * number of 16-lane chunks (QGEMV_E_NOKERNEL otherwise).  Borrows the weight
+ * pointers; makes no HIP call. */
 int qgemv_stack_create(const qgemv_run_spec* runs, int32_t n_runs, int64_t ldy, qgemv_stack_t* out);
 
 /* y[i*ldy + c] for every member column c and window row i < m, in one
