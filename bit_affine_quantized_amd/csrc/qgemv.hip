@@ -71,6 +71,7 @@ struct qgemv_handle {
   int vec_groups;        // scales/biases aligned for packed loads
   int64_t wpr, gpr;
   int arith;             // QGEMV_ARITH_DOT or QGEMV_ARITH_MFMA
+  int ksplit;            // matrix-core form: K-parts per column (1, 2 or 4)
   const qg::Entry* entry;
   // resident blocks per CU of each (window variant, staging) kernel, 0 =
   // not yet known; a benign cache: every thread that fills it writes the
@@ -167,14 +168,15 @@ size_t lds_bytes(const qgemv_handle* h, int var, int stage) {
 
 // The matrix-core kernels' LDS: the staged window (rows of k/32 units x 64
 // bytes + 16 padding, a zero area of R * 256 bytes, unit sums), the routed
-// list of an indexed call, and one load-group slot per wave.  Returns false
-// when it exceeds one block's LDS.
+// list of an indexed call, one load-group slot per wave, and with a K split
+// the waves' partial sums.  Returns false when it exceeds one block's LDS.
 bool mfma_plan(const qgemv_handle* h, int var, bool indexed, size_t* lds) {
   const size_t mb = static_cast<size_t>(qg::kWindows[var]);
   const size_t units = static_cast<size_t>(h->d.k) / 32;
+  const size_t waves = static_cast<size_t>(h->entry->mfma_waves[var]);
   const size_t b = mb * (units * 64 + 16) + 256 * static_cast<size_t>(h->entry->mfma_group) + mb * units * 4 +
-                   (indexed ? qg::kMaxList * 4 : 0) +
-                   static_cast<size_t>(h->entry->mfma_waves[var]) * h->entry->mfma_slot;
+                   (indexed ? qg::kMaxList * 4 : 0) + waves * h->entry->mfma_slot +
+                   (h->ksplit > 1 ? waves * ((mb + 3) / 4) * qg::kWave * 4 : 0);
   if (b > qg::kMaxMfmaLds) return false;
   *lds = b;
   return true;
@@ -223,7 +225,7 @@ int launch(const qgemv_handle* h, const uint16_t* x, int32_t m, float* y, int64_
     // one wave per 16 output columns
     fn = h->entry->mfma[var];
     threads = h->entry->mfma_waves[var] * qg::kWave;
-    tile_rows = static_cast<int64_t>(h->entry->mfma_waves[var]) * 16;
+    tile_rows = static_cast<int64_t>(h->entry->mfma_waves[var] / h->ksplit) * 16;
   } else {
     const int R = h->fast ? h->entry->fast_rows[var] : h->entry->generic_rows[var];
     const int slots_per_wave = qg::kWave / h->lpr;
@@ -253,6 +255,7 @@ int launch(const qgemv_handle* h, const uint16_t* x, int32_t m, float* y, int64_
   p.tiles = static_cast<int32_t>(tiles);
   p.indexed = indexed;
   p.vec_groups = h->vec_groups;
+  p.ksplit = h->ksplit;
   p.y_bytes = static_cast<int64_t>(ybytes);
   p.nseg = 1;
   p.seg_row0[0] = 0;
@@ -375,6 +378,16 @@ int qgemv_create_arith(const qgemv_desc* d, int32_t arith, qgemv_t* out) {
   if (arith == QGEMV_ARITH_MFMA && !mfma_ok) return QGEMV_E_NOKERNEL;
   h.arith = (arith == QGEMV_ARITH_MFMA || (arith == QGEMV_ARITH_AUTO && mfma_ok)) ? QGEMV_ARITH_MFMA
                                                                                : QGEMV_ARITH_DOT;
+  // matrix-core K split, from one expert's shape only (an indexed call must
+  // give each expert the bits of that expert's own single-expert handle):
+  // small matrices split K in 2 or 4 parts so that enough waves stream at
+  // once (about 2048, two per SIMD), when the row's load groups divide evenly
+  h.ksplit = 1;
+  if (h.arith == QGEMV_ARITH_MFMA) {
+    const int64_t groups = d->k / (128 * static_cast<int64_t>(h.entry->mfma_group));
+    const int64_t col_tiles = (d->n + 15) / 16;
+    while (h.ksplit < 4 && col_tiles * h.ksplit < 2048 && groups % (2 * h.ksplit) == 0) h.ksplit *= 2;
+  }
   {
     // groups one packed scale load spans: a lane chunk's, or a 128-code
     // macro step's for the matrix-core form
@@ -391,6 +404,7 @@ int qgemv_create_arith(const qgemv_desc* d, int32_t arith, qgemv_t* out) {
     if (!mfma_plan(&h, 0, false, &lds)) {
       if (arith == QGEMV_ARITH_MFMA) return QGEMV_E_NOKERNEL;
       h.arith = QGEMV_ARITH_DOT;
+      h.ksplit = 1;
     }
   }
   if (h.arith == QGEMV_ARITH_DOT && lds_bytes(&h, 0, 0) > qg::kMaxDynamicLds) return QGEMV_E_SHAPE;
@@ -564,7 +578,7 @@ int launch_stack(const qgemv_stack* s, bool mfma, const uint16_t* x, int32_t m, 
     int64_t tile_rows = 0;
     if (mfma) {
       threads = h->entry->mfma_waves[var] * qg::kWave;
-      tile_rows = static_cast<int64_t>(h->entry->mfma_waves[var]) * 16;
+      tile_rows = static_cast<int64_t>(h->entry->mfma_waves[var] / h->ksplit) * 16;
       sp.kind[q] = bi * 3 + gi;
     } else {
       int stage = h->ppc > 1 ? 1 : 0;
@@ -600,6 +614,7 @@ int launch_stack(const qgemv_stack* s, bool mfma, const uint16_t* x, int32_t m, 
     p.tiles = static_cast<int32_t>(tiles[q]);
     p.indexed = 0;
     p.vec_groups = h->vec_groups;
+    p.ksplit = h->ksplit;
     p.y_bytes = static_cast<int64_t>(ybytes);
     p.nseg = s->n_members[r];
     int64_t row0 = 0;

@@ -226,6 +226,7 @@ struct Params {
   int32_t tiles;            // column tiles per expert
   int32_t indexed;          // 0: plain/strided, 1: indexed
   int32_t vec_groups;       // scales/biases aligned for packed loads
+  int32_t ksplit;           // matrix-core form: K-parts per column (1, 2 or 4)
   int64_t y_bytes;          // extent of y written by this call (fast kernel stores)
   // column map: rows [seg_row0[s], seg_row0[s+1]) are written at column
   // row + seg_delta[s] (one segment {0, 0} for plain, strided and indexed calls)
@@ -959,6 +960,11 @@ __global__ __launch_bounds__(kThreads) void qrow_fast(const Params p) {
 // ([line][column]) with the 8 pieces of column c's line rotated by c / 2,
 // so the 16 lanes that read the same piece of 16 columns hit 16 different
 // bank groups.
+//
+// K split: a handle may split K into S = 1, 2 or 4 consecutive parts (fixed
+// at create from its shape, never from the window).  The S waves of a
+// column group each fold their part's units in order from zero, and the
+// parts are then added in order, P = ((P0 + P1) + P2) + P3, through LDS.
 // ---------------------------------------------------------------------------
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -995,14 +1001,17 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
   constexpr int ZB = R * 256;               // zero area: one group's activations
 
   const int units = static_cast<int>(p.k / 32);
-  const int groups = units / (4 * R);       // groups per tile
+  const int S = p.ksplit;                   // K-parts per column
+  const int gpp = units / (4 * R) / S;      // groups per K-part
+  const int ncg = NW / S;                   // column groups (of 16 columns) per block
   const int mrows = p.indexed ? MB : min(p.m, MB);       // window rows staged
   const int xstride = units * 64 + 16;                     // bytes per staged row
   // LDS: activations [mrows][units][32 slots] bf16 (rows padded by 16 bytes
   // so a 4 x 4 block of reads hits distinct banks), a zero area of one
   // group's activations (the A operand of lanes outside the block diagonal,
   // read at the same offsets as a live lane's), unit sums [mrows][units]
-  // fp32, the routed list (indexed calls), then one slot per wave.
+  // fp32, the routed list (indexed calls), one slot per wave, then (K
+  // split) the partial sums [waves][NMB][64 lanes] fp32.
   unsigned char* zero_area = smem + static_cast<size_t>(mrows) * xstride;
   float* xsum = reinterpret_cast<float*>(zero_area + ZB);
   int* s_list = reinterpret_cast<int*>(xsum + static_cast<size_t>(mrows) * units);
@@ -1012,7 +1021,9 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
   const int lane = tid % kWave;
   const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int j = lane % 16, qd = lane / 16;
+  const int cg = wv / S, ks = wv - (wv / S) * S;   // column group, K-part
   unsigned char* slot = slots + static_cast<size_t>(wv) * MG::SLOT;
+  float* partial = reinterpret_cast<float*>(slots + static_cast<size_t>(NW) * MG::SLOT);
 
   int expert = 0;
   int total = p.m;
@@ -1028,7 +1039,7 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
   const unsigned char* sexp = reinterpret_cast<const unsigned char*>(p.scales) + static_cast<int64_t>(expert) * p.n * gpr2;
   const unsigned char* bexp = reinterpret_cast<const unsigned char*>(p.biases) + static_cast<int64_t>(expert) * p.n * gpr2;
   const int my_tiles = bx < p.tiles ? (p.tiles - 1 - bx) / gx + 1 : 0;
-  const int steps = my_tiles * groups;
+  const int steps = my_tiles * gpp;
   const __amdgpu_buffer_rsrc_t yres = make_rsrc(p.y, p.y_bytes);
 
   // ---- per-lane constants of the loads and reads (the same for every group) ----
@@ -1061,14 +1072,16 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
   const int s_off = MG::WBYTES + j * MG::SBP;
   const int b_off = s_off + 16 * MG::SBP;
 
-  // A step is one group of one tile; cursors walk the steps in order
+  // A step is one group of this wave's K-part of one tile; cursors walk the
+  // steps in order (gr counts groups from the start of the row)
   struct Cursor {
     int st, i, gr;
   };
+  const int gr0 = ks * gpp;
   auto advance = [&](Cursor& c) {
     ++c.st;
-    if (++c.gr == groups) {
-      c.gr = 0;
+    if (++c.gr == gr0 + gpp) {
+      c.gr = gr0;
       ++c.i;
     }
   };
@@ -1080,7 +1093,7 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
   // a step's loads into registers (past the last step: loads that read nothing)
   auto load_stage = [&](Stage& sg, const Cursor& c) {
     const bool real = c.st < steps;
-    const int c0 = ((bx + c.i * gx) * NW + wv) * 16;
+    const int c0 = ((bx + c.i * gx) * ncg + cg) * 16;
     const int ncols = real ? n - c0 : 0;
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(wexp + static_cast<int64_t>(c0) * row_bytes,
                                                 static_cast<int64_t>(ncols) * row_bytes);
@@ -1242,23 +1255,47 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
           acc[mb] = __builtin_fmaf(bv[q2], xsv[mb][q2], acc[mb]);
         }
     }
-    if (c.gr == groups - 1) {
-      const int col = ((bx + c.i * gx) * NW + wv) * 16 + j;
+    if (c.gr == gr0 + gpp - 1) {
+      const int col = ((bx + c.i * gx) * ncg + cg) * 16 + j;
+      float out[NMB];
+      bool store = true;
+      if (S == 1) {
 #pragma unroll
-      for (int mb = 0; mb < NMB; ++mb) {
-        const int em = 4 * mb + qd;
-        const bool ok = em < mcount && col < n;
-        const int off = ok ? static_cast<int>((s_yoff[ok ? em : 0] + mapped_column(p, col)) * 4) : 0x7ffffff0;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(apply_epi(acc[mb], p.epi)), yres, off, 0, 0);
-        acc[mb] = 0.0f;
+        for (int mb = 0; mb < NMB; ++mb) out[mb] = acc[mb];
+      } else {
+        // the column group's parts meet in LDS and are added in part order
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) partial[(wv * NMB + mb) * kWave + lane] = acc[mb];
+        __syncthreads();
+        store = ks == 0;
+        if (store) {
+#pragma unroll
+          for (int mb = 0; mb < NMB; ++mb) {
+            float v = partial[((cg * S) * NMB + mb) * kWave + lane];
+            for (int q = 1; q < S; ++q) v += partial[((cg * S + q) * NMB + mb) * kWave + lane];
+            out[mb] = v;
+          }
+        }
+        __syncthreads();
       }
+      if (store) {
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+          const int em = 4 * mb + qd;
+          const bool ok = em < mcount && col < n;
+          const int off = ok ? static_cast<int>((s_yoff[ok ? em : 0] + mapped_column(p, col)) * 4) : 0x7ffffff0;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(apply_epi(out[mb], p.epi)), yres, off, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) acc[mb] = 0.0f;
     }
   };
 
   for (int c0 = 0; c0 < total; c0 += MB) {
     mcount = min(MB, total - c0);
     // the first group's loads are in flight while the window is staged
-    Cursor cl = {0, 0, 0}, cc = {0, 0, 0};
+    Cursor cl = {0, 0, gr0}, cc = {0, 0, gr0};
     Stage sa, sb;
     load_stage(sa, cl);
     advance(cl);

@@ -112,7 +112,11 @@ int qgemv_create(const qgemv_desc* d, qgemv_t* out);
  *                     fixed butterfly over the lanes of the row.
  *   QGEMV_ARITH_MFMA  matrix cores: 16x16x32 bf16 products with one window
  *                     row per 4 operand rows; each lane folds its own four
- *                     units in order, no butterfly.  Needs k a multiple of
+ *                     units in order, no butterfly.  A matrix of few
+ *                     columns (n under 32768) splits k
+ *                     into 2 or 4 consecutive parts, fixed at create from
+ *                     its shape: each part folds from zero and the parts are
+ *                     added in order.  Needs k a multiple of
  *                     qgemv_mfma_codes(bits, group) and aligned scales
  *                     and biases (QGEMV_E_NOKERNEL otherwise).
  *   QGEMV_ARITH_AUTO  the library's choice (what qgemv_create uses): the
