@@ -167,14 +167,15 @@ size_t lds_bytes(const qgemv_handle* h, int var, int stage) {
 }
 
 // The matrix-core kernels' LDS: the staged window (rows of k/32 units x 64
-// bytes + 16 padding, a zero area of R * 256 bytes, unit sums), the routed
-// list of an indexed call, one load-group slot per wave, and with a K split
-// the waves' partial sums.  Returns false when it exceeds one block's LDS.
+// bytes, a zero area of R * 256 bytes, unit sums; rows padded by 16 bytes),
+// the routed list of an indexed call, one load-group slot per wave, and with
+// a K split the waves' partial sums.  Returns false when it exceeds one
+// block's LDS.
 bool mfma_plan(const qgemv_handle* h, int var, bool indexed, size_t* lds) {
   const size_t mb = static_cast<size_t>(qg::kWindows[var]);
   const size_t units = static_cast<size_t>(h->d.k) / 32;
   const size_t waves = static_cast<size_t>(h->entry->mfma_waves[var]);
-  const size_t b = mb * (units * 64 + 16) + 256 * static_cast<size_t>(h->entry->mfma_group) + mb * units * 4 +
+  const size_t b = mb * (units * 64 + 16) + 256 * static_cast<size_t>(h->entry->mfma_group) + mb * (units + 4) * 4 +
                    (indexed ? qg::kMaxList * 4 : 0) + waves * h->entry->mfma_slot +
                    (h->ksplit > 1 ? waves * ((mb + 3) / 4) * qg::kWave * 4 : 0);
   if (b > qg::kMaxMfmaLds) return false;

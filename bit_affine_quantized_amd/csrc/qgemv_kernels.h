@@ -980,8 +980,9 @@ template <int B, int G> struct MGroup {
   static constexpr int SBP = SB < 4 ? 4 : SB;      // bytes kept per column (the aligned dword when 2)
   static constexpr int SSZ = S16 ? 16 : 4;         // bytes of one scale load
   static constexpr int SLANES = 16 * SBP / SSZ;    // lanes of one scale load
+  static constexpr int SSTR = SBP % 32 == 0 ? SBP + 16 : SBP;   // LDS bytes per column of scales
   static constexpr int WBYTES = 16 * L * 128;
-  static constexpr int SLOT = WBYTES + 2 * 16 * SBP;
+  static constexpr int SLOT = WBYTES + 2 * 16 * SSTR;
   static constexpr int CH = (B % 4 == 0) ? 4 : ((B % 2 == 0) ? 2 : 1);   // words per LDS read
   static_assert(R * B % 8 == 0 && SLANES <= 64, "group geometry");
 };
@@ -1006,15 +1007,17 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
   const int ncg = NW / S;                   // column groups (of 16 columns) per block
   const int mrows = p.indexed ? MB : min(p.m, MB);       // window rows staged
   const int xstride = units * 64 + 16;                     // bytes per staged row
-  // LDS: activations [mrows][units][32 slots] bf16 (rows padded by 16 bytes
-  // so a 4 x 4 block of reads hits distinct banks), a zero area of one
+  const int sstride = units + 4;                           // floats per row of unit sums
+  // LDS: activations [mrows][units][32 slots] bf16, a zero area of one
   // group's activations (the A operand of lanes outside the block diagonal,
   // read at the same offsets as a live lane's), unit sums [mrows][units]
-  // fp32, the routed list (indexed calls), one slot per wave, then (K
-  // split) the partial sums [waves][NMB][64 lanes] fp32.
+  // fp32 (rows of activations and of sums padded by 16 bytes, so the rows a
+  // wave reads at once fall in different banks), the routed list (indexed
+  // calls), one slot per wave, then (K split) the partial sums
+  // [waves][NMB][64 lanes] fp32.
   unsigned char* zero_area = smem + static_cast<size_t>(mrows) * xstride;
   float* xsum = reinterpret_cast<float*>(zero_area + ZB);
-  int* s_list = reinterpret_cast<int*>(xsum + static_cast<size_t>(mrows) * units);
+  int* s_list = reinterpret_cast<int*>(xsum + static_cast<size_t>(mrows) * sstride);
   unsigned char* slots = reinterpret_cast<unsigned char*>(s_list + (p.indexed ? kMaxList : 0));
 
   const int tid = threadIdx.x;
@@ -1058,6 +1061,7 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
   constexpr int SPER = MG::SBP / SSZ;
   const bool s_live = lane < MG::SLANES;
   const int s_voff = (lane / SPER) * gpr2 + (lane % SPER) * SSZ;
+  const int s_woff = (lane / SPER) * MG::SSTR + (lane % SPER) * SSZ;   // its place in the slot
   // this lane's unit words in round r: word w = r*4B + qd*B + h of column
   // j's share sits at piece w / 4 -> line (w/4) / 8, piece (w/4) % 8
   auto word_off = [&](int w) {
@@ -1069,8 +1073,8 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
   for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int h = 0; h < B / CH; ++h) r_off[r][h] = word_off(r * 4 * B + qd * B + h * CH);
-  const int s_off = MG::WBYTES + j * MG::SBP;
-  const int b_off = s_off + 16 * MG::SBP;
+  const int s_off = MG::WBYTES + j * MG::SSTR;
+  const int b_off = s_off + 16 * MG::SSTR;
 
   // A step is one group of this wave's K-part of one tile; cursors walk the
   // steps in order (gr counts groups from the start of the row)
@@ -1138,7 +1142,7 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
       a_live[mb] = live ? 1 : 0;
       a_base[mb] = live ? am * xstride + qd * 64 : mrows * xstride;
       const int em = 4 * mb + qd;
-      x_base[mb] = mrows * xstride + ZB + (em < mcount ? em : 0) * units * 4;
+      x_base[mb] = mrows * xstride + ZB + (em < mcount ? em : 0) * sstride * 4;
     }
   };
 
@@ -1152,11 +1156,11 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
         u32x4 a4, b4;
         a4.x = sg.s[0]; a4.y = sg.s[1]; a4.z = sg.s[2]; a4.w = sg.s[3];
         b4.x = sg.b[0]; b4.y = sg.b[1]; b4.z = sg.b[2]; b4.w = sg.b[3];
-        reinterpret_cast<u32x4*>(slot + MG::WBYTES)[lane] = a4;
-        reinterpret_cast<u32x4*>(slot + MG::WBYTES + 16 * MG::SBP)[lane] = b4;
+        *reinterpret_cast<u32x4*>(slot + MG::WBYTES + s_woff) = a4;
+        *reinterpret_cast<u32x4*>(slot + MG::WBYTES + 16 * MG::SSTR + s_woff) = b4;
       } else {
-        reinterpret_cast<uint32_t*>(slot + MG::WBYTES)[lane] = sg.s[0];
-        reinterpret_cast<uint32_t*>(slot + MG::WBYTES + 16 * MG::SBP)[lane] = sg.b[0];
+        *reinterpret_cast<uint32_t*>(slot + MG::WBYTES + s_woff) = sg.s[0];
+        *reinterpret_cast<uint32_t*>(slot + MG::WBYTES + 16 * MG::SSTR + s_woff) = sg.b[0];
       }
     }
     int a_grp[NMB], x_grp[NMB];
@@ -1344,7 +1348,7 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
         X = dot2(o.w, ones, X);
         dst[pc] = o;
       }
-      xsum[mi * units + un] = X;
+      xsum[mi * sstride + un] = X;
     }
     __syncthreads();
     // double-buffered: a group's loads are in flight while the previous one
