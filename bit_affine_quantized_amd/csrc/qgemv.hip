@@ -148,10 +148,12 @@ bool overlaps(const void* a, size_t abytes, const void* b, size_t bbytes) {
   return a0 < b0 + bbytes && b0 < a0 + abytes;
 }
 
+// The window variant of m rows: the narrowest that holds them, the widest
+// (passes of 16 rows) beyond 16.
 int window_variant(int m) {
   for (int i = 0; i < 5; ++i)
     if (m <= qg::kWindows[i]) return i;
-  return -1;
+  return 4;
 }
 
 // Dynamic LDS of one block: the staged window (activations and unit sums)
@@ -415,9 +417,12 @@ int qgemv_create_arith(const qgemv_desc* d, int32_t arith, qgemv_t* out) {
 
 void qgemv_destroy(qgemv_t h) { delete h; }
 
-static int check_run_common(qgemv_t h, const uint16_t* x, int32_t m, const float* y, int32_t epi) {
+// max_m: QGEMV_MAX_WINDOW, or for plain and strided calls on a matrix-core
+// handle QGEMV_MAX_PROMPT (windows above 16 rows run as passes of 16)
+static int check_run_common(qgemv_t h, const uint16_t* x, int32_t m, const float* y, int32_t epi,
+                            int32_t max_m) {
   if (!h) return QGEMV_E_ARG;
-  if (m < 0 || m > QGEMV_MAX_WINDOW) return QGEMV_E_WINDOW;
+  if (m < 0 || m > max_m) return QGEMV_E_WINDOW;
   if (epi != QGEMV_EPI_NONE && epi != QGEMV_EPI_RELU2) return QGEMV_E_ARG;
   if (m == 0) return QGEMV_OK;
   if (!x || !y) return QGEMV_E_ARG;
@@ -427,7 +432,8 @@ static int check_run_common(qgemv_t h, const uint16_t* x, int32_t m, const float
 
 int qgemv_run_strided(qgemv_t h, const uint16_t* x, int32_t m, float* y, int64_t ldy, int32_t epi,
                       void* stream) {
-  int rc = check_run_common(h, x, m, y, epi);
+  int rc = check_run_common(h, x, m, y, epi,
+                            h && h->arith == QGEMV_ARITH_MFMA ? QGEMV_MAX_PROMPT : QGEMV_MAX_WINDOW);
   if (rc != QGEMV_OK) return rc;
   if (h->d.n_experts != 1) return QGEMV_E_ARG;
   if (ldy < h->d.n) return QGEMV_E_STRIDE;
@@ -447,7 +453,7 @@ int qgemv_run(qgemv_t h, const uint16_t* x, int32_t m, float* y, int32_t epi, vo
 
 int qgemv_run_indexed(qgemv_t h, const uint16_t* x, int32_t m, const int32_t* idx, int32_t slots,
                       float* y, int32_t epi, void* stream) {
-  int rc = check_run_common(h, x, m, y, epi);
+  int rc = check_run_common(h, x, m, y, epi, QGEMV_MAX_WINDOW);
   if (rc != QGEMV_OK) return rc;
   if (slots < 0 || slots > qg::kMaxSlots) return QGEMV_E_ARG;
   if (m == 0 || slots == 0) return QGEMV_OK;

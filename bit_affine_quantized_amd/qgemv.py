@@ -21,6 +21,7 @@ QGEMV_E_ALIGN, QGEMV_E_WINDOW, QGEMV_E_ALIAS, QGEMV_E_NOKERNEL, QGEMV_E_HIP = -6
 QGEMV_EPI_NONE, QGEMV_EPI_RELU2 = 0, 1
 QGEMV_ARITH_AUTO, QGEMV_ARITH_DOT, QGEMV_ARITH_MFMA = 0, 1, 2
 QGEMV_MAX_WINDOW = 16
+QGEMV_MAX_PROMPT = 65
 
 _lib = None
 _lock = threading.Lock()

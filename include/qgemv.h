@@ -67,6 +67,7 @@ extern "C" {
 #define QGEMV_EPI_RELU2 1     /* y > 0 ? y*y : (y is NaN ? y : +0), on fp32 y */
 
 #define QGEMV_MAX_WINDOW 16
+#define QGEMV_MAX_PROMPT 65   /* prompt windows: plain and strided calls, MFMA form */
 
 /* Weights of one handle.
  *   bits       code width: 2, 3, 4, 5, 6 or 8.
@@ -146,11 +147,15 @@ void qgemv_destroy(qgemv_t h);
 
 /* y[i][j] for i < m, j < n, contiguous (row stride n).
  *   x  bf16 bits [m][k] device, 16-byte aligned.
- *   m  window rows, 0..16; m == 0 launches nothing and returns QGEMV_OK.
- *      QGEMV_ARITH_DOT: a window whose staged activations exceed the LDS
- *      of one block (m*k*2.125 bytes > 152 KiB) is refused with
- *      QGEMV_E_WINDOW.  QGEMV_ARITH_MFMA: such a window runs as passes of
- *      fewer rows (the weights are read once per pass), same bits.
+ *   m  window rows: 0..16 (decode windows), and on a QGEMV_ARITH_MFMA
+ *      handle up to QGEMV_MAX_PROMPT = 65 (prompt windows: P788 keeps a
+ *      row's bits in every window of 1-65 rows in prompt).  m == 0 launches
+ *      nothing and returns QGEMV_OK.  QGEMV_ARITH_DOT: a window whose staged
+ *      activations exceed the LDS of one block (m*k*2.125 bytes > 152 KiB)
+ *      is refused with QGEMV_E_WINDOW.  QGEMV_ARITH_MFMA: a window above 16
+ *      rows, or one too wide for the LDS, runs as passes of fewer rows (the
+ *      weights are read once per pass); each row's bits are those of the
+ *      row alone.
  *   y  fp32 [m][n] device, 4-byte aligned, must not overlap x or weights.
  *   epi QGEMV_EPI_NONE or QGEMV_EPI_RELU2.
  *   stream  hipStream_t (NULL = the null stream).

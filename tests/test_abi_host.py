@@ -90,7 +90,7 @@ def test_run_refusals(handle):
     h = handle
     run, strided = qgemv.qgemv_run, qgemv.qgemv_run_strided
     assert run(None, X, 1, Y, 0, 0) == qgemv.QGEMV_E_ARG
-    assert run(h, X, 17, Y, 0, 0) == qgemv.QGEMV_E_WINDOW
+    assert run(h, X, 66, Y, 0, 0) == qgemv.QGEMV_E_WINDOW
     assert run(h, X, -1, Y, 0, 0) == qgemv.QGEMV_E_WINDOW
     assert run(h, X, 1, Y, 2, 0) == qgemv.QGEMV_E_ARG          # unknown epilogue
     assert run(h, 0, 1, Y, 0, 0) == qgemv.QGEMV_E_ARG
@@ -199,3 +199,20 @@ def test_arith_choice_fixed_at_create():
         qgemv.qgemv_destroy(h)
     assert qgemv.qgemv_create_arith(4, 64, 48, 2048, W, S, B, 3)[0] == qgemv.QGEMV_E_ARG
     assert qgemv.qgemv_arith(None) == qgemv.QGEMV_E_ARG
+
+
+def test_window_limits_by_form():
+    """Decode windows of 1-16 rows for every handle; prompt windows up to 65
+    rows for plain and strided calls in the MFMA form only."""
+    assert qgemv.QGEMV_MAX_WINDOW == 16 and qgemv.QGEMV_MAX_PROMPT == 65
+    rc, hd = qgemv.qgemv_create_arith(4, 64, 256, 2048, W, S, B, qgemv.QGEMV_ARITH_DOT)
+    rc2, hm = qgemv.qgemv_create_arith(4, 64, 256, 2048, W, S, B, qgemv.QGEMV_ARITH_MFMA)
+    rc3, he = qgemv.qgemv_create_arith(4, 64, 256, 2048, W, S, B, qgemv.QGEMV_ARITH_MFMA, n_experts=4)
+    assert rc == rc2 == rc3 == 0
+    assert qgemv.qgemv_run(hd, X, 17, Y, 0, 0) == qgemv.QGEMV_E_WINDOW
+    assert qgemv.qgemv_run_strided(hd, X, 17, Y, 512, 0, 0) == qgemv.QGEMV_E_WINDOW
+    assert qgemv.qgemv_run(hm, X, 66, Y, 0, 0) == qgemv.QGEMV_E_WINDOW
+    assert qgemv.qgemv_run_strided(hm, X, 66, Y, 512, 0, 0) == qgemv.QGEMV_E_WINDOW
+    assert qgemv.qgemv_run_indexed(he, X, 17, IDX, 8, Y, 0, 0) == qgemv.QGEMV_E_WINDOW
+    for h in (hd, hm, he):
+        qgemv.qgemv_destroy(h)

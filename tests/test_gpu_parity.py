@@ -149,6 +149,34 @@ def test_window_invariance(bits, group, arith):
             assert bits_equal(y, alone[s0:s0 + m]), f"window {m} at {s0}"
 
 
+@pytest.mark.parametrize("bits,group", [(6, 32), (4, 64), (3, 128), (8, 32), (2, 64), (5, 64)])
+def test_prompt_windows(bits, group):
+    """MFMA form: windows of 17-65 rows (passes of 16) give every row the bits
+    it has alone, and stay within the bound; the dot form refuses them."""
+    print_case("prompt", bits, group)
+    n, k = 1000, 2048
+    d = synth.matrix(7000 + bits * 10 + group, bits, group, n, k)
+    rng = np.random.default_rng(7100 + bits * 10 + group)
+    pool_np = synth.draw_x(rng, 80, k)
+    pool = dev(pool_np)
+    mat = matrix_of(d, arith=qgemv.QGEMV_ARITH_MFMA)
+    alone = torch.empty((80, n), dtype=torch.float32, device=DEV)
+    for r in range(80):
+        mat.run(pool[r:r + 1], alone[r:r + 1], m=1)
+    for m in (17, 33, 65):
+        y = torch.empty((m, n), dtype=torch.float32, device=DEV)
+        for s0 in (0, 15 if m < 65 else 7):
+            mat.run(pool[s0:s0 + m], y, m=m)
+            assert bits_equal(y, alone[s0:s0 + m]), f"window {m} at {s0}"
+    # y holds the last 65-row window, pool rows 7..71
+    y64, a64, _ = oracle.gemv(d["words"], d["scales"], d["biases"], pool_np[7:72], bits, group, n, k,
+                              threads=THREADS)
+    check_bound(y.cpu().numpy(), y64, a64, k, f"prompt {bits}/{group}")
+    dot = matrix_of(d, arith=qgemv.QGEMV_ARITH_DOT)
+    with pytest.raises(qgemv.QgemvError, match="QGEMV_E_WINDOW"):
+        dot.run(pool[:17], torch.empty((17, n), dtype=torch.float32, device=DEV), m=17)
+
+
 @arith_param
 @pytest.mark.parametrize("bits,group", PAIRS)
 def test_exact_representable_inputs(bits, group, arith):
@@ -223,7 +251,7 @@ def test_refusals_leave_output_untouched():
     xt = dev(d["x"])
     y = torch.full((2, n), 3.0, device=DEV)
     assert qgemv.qgemv_run(mat.h, xt, 0, y) == qgemv.QGEMV_OK
-    assert qgemv.qgemv_run(mat.h, xt, 17, y) == qgemv.QGEMV_E_WINDOW
+    assert qgemv.qgemv_run(mat.h, xt, qgemv.QGEMV_MAX_PROMPT + 1, y) == qgemv.QGEMV_E_WINDOW
     assert qgemv.qgemv_run_strided(mat.h, xt, 2, y, n - 1) == qgemv.QGEMV_E_STRIDE
     assert qgemv.qgemv_run(mat.h, xt, 2, xt) == qgemv.QGEMV_E_ALIAS
     torch.cuda.synchronize()
