@@ -196,8 +196,10 @@ int check_y_alias(const qgemv_handle* h, const void* y, size_t ybytes, const voi
   return QGEMV_OK;
 }
 
+// up: the up matrix of a gate/up pair (matrix-core form), else nullptr.
 int launch(const qgemv_handle* h, const uint16_t* x, int32_t m, float* y, int64_t ldy,
-           const int32_t* idx, int32_t slots, int32_t epi, void* stream, size_t ybytes) {
+           const int32_t* idx, int32_t slots, int32_t epi, void* stream, size_t ybytes,
+           const qgemv_handle* up = nullptr) {
   const DeviceInfo* dev = current_device();
   if (!dev) return QGEMV_E_HIP;
   const int indexed = idx != nullptr;
@@ -228,7 +230,7 @@ int launch(const qgemv_handle* h, const uint16_t* x, int32_t m, float* y, int64_
     // one wave per 16 output columns
     fn = h->entry->mfma[var];
     threads = h->entry->mfma_waves[var] * qg::kWave;
-    tile_rows = static_cast<int64_t>(h->entry->mfma_waves[var] / h->ksplit) * 16;
+    tile_rows = static_cast<int64_t>(h->entry->mfma_waves[var] / h->ksplit) * (up ? 8 : 16);
   } else {
     const int R = h->fast ? h->entry->fast_rows[var] : h->entry->generic_rows[var];
     const int slots_per_wave = qg::kWave / h->lpr;
@@ -259,6 +261,10 @@ int launch(const qgemv_handle* h, const uint16_t* x, int32_t m, float* y, int64_
   p.indexed = indexed;
   p.vec_groups = h->vec_groups;
   p.ksplit = h->ksplit;
+  p.gateup = up ? 1 : 0;
+  p.w2 = up ? up->d.w : nullptr;
+  p.scales2 = up ? up->d.scales : nullptr;
+  p.biases2 = up ? up->d.biases : nullptr;
   p.y_bytes = static_cast<int64_t>(ybytes);
   p.nseg = 1;
   p.seg_row0[0] = 0;
@@ -465,6 +471,53 @@ int qgemv_run_indexed(qgemv_t h, const uint16_t* x, int32_t m, const int32_t* id
   rc = check_y_alias(h, y, ybytes, x, xbytes, idx, static_cast<size_t>(m) * slots * 4);
   if (rc != QGEMV_OK) return rc;
   return launch(h, x, m, y, h->d.n, idx, slots, epi, stream, ybytes);
+}
+
+static int check_gateup_pair(qgemv_t gate, qgemv_t up) {
+  if (!gate || !up) return QGEMV_E_ARG;
+  if (gate->arith != QGEMV_ARITH_MFMA || up->arith != QGEMV_ARITH_MFMA) return QGEMV_E_NOKERNEL;
+  if (gate->d.bits != up->d.bits || gate->d.group != up->d.group || gate->d.n != up->d.n ||
+      gate->d.k != up->d.k || gate->d.n_experts != up->d.n_experts || gate->ksplit != up->ksplit)
+    return QGEMV_E_SHAPE;
+  return QGEMV_OK;
+}
+
+int qgemv_run_gateup(qgemv_t gate, qgemv_t up, const uint16_t* x, int32_t m, float* y, int64_t ldy,
+                     void* stream) {
+  int rc = check_gateup_pair(gate, up);
+  if (rc != QGEMV_OK) return rc;
+  rc = check_run_common(gate, x, m, y, QGEMV_EPI_NONE, QGEMV_MAX_PROMPT);
+  if (rc != QGEMV_OK) return rc;
+  if (gate->d.n_experts != 1) return QGEMV_E_ARG;
+  if (ldy < gate->d.n) return QGEMV_E_STRIDE;
+  if (m == 0) return QGEMV_OK;
+  const size_t xbytes = static_cast<size_t>(m) * gate->d.k * 2;
+  const size_t ybytes = (static_cast<size_t>(m - 1) * ldy + gate->d.n) * 4;
+  if (ybytes > 0x7fffffffu) return QGEMV_E_STRIDE;
+  rc = check_y_alias(gate, y, ybytes, x, xbytes, nullptr, 0);
+  if (rc == QGEMV_OK) rc = check_y_alias(up, y, ybytes, x, xbytes, nullptr, 0);
+  if (rc != QGEMV_OK) return rc;
+  return launch(gate, x, m, y, ldy, nullptr, 0, QGEMV_EPI_NONE, stream, ybytes, up);
+}
+
+int qgemv_run_gateup_indexed(qgemv_t gate, qgemv_t up, const uint16_t* x, int32_t m, const int32_t* idx,
+                             int32_t slots, float* y, void* stream) {
+  int rc = check_gateup_pair(gate, up);
+  if (rc != QGEMV_OK) return rc;
+  rc = check_run_common(gate, x, m, y, QGEMV_EPI_NONE, QGEMV_MAX_WINDOW);
+  if (rc != QGEMV_OK) return rc;
+  if (slots < 0 || slots > qg::kMaxSlots) return QGEMV_E_ARG;
+  if (m == 0 || slots == 0) return QGEMV_OK;
+  if (!idx) return QGEMV_E_ARG;
+  if (reinterpret_cast<uintptr_t>(idx) & 3) return QGEMV_E_ALIGN;
+  const size_t xbytes = static_cast<size_t>(m) * gate->d.k * 2;
+  const size_t ybytes = static_cast<size_t>(m) * slots * gate->d.n * 4;
+  if (ybytes > 0x7fffffffu) return QGEMV_E_SHAPE;
+  const size_t ib = static_cast<size_t>(m) * slots * 4;
+  rc = check_y_alias(gate, y, ybytes, x, xbytes, idx, ib);
+  if (rc == QGEMV_OK) rc = check_y_alias(up, y, ybytes, x, xbytes, idx, ib);
+  if (rc != QGEMV_OK) return rc;
+  return launch(gate, x, m, y, gate->d.n, idx, slots, QGEMV_EPI_NONE, stream, ybytes, up);
 }
 
 int qgemv_debug_unpack(qgemv_t h, int32_t expert, uint8_t* codes, void* stream) {

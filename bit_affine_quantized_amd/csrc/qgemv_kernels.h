@@ -227,6 +227,12 @@ struct Params {
   int32_t indexed;          // 0: plain/strided, 1: indexed
   int32_t vec_groups;       // scales/biases aligned for packed loads
   int32_t ksplit;           // matrix-core form: K-parts per column (1, 2 or 4)
+  // gate/up pair (matrix-core form): y = silu(gate row) * (up row), the up
+  // matrix at w2/scales2/biases2 with the gate's shape
+  int32_t gateup;
+  const uint32_t* w2;
+  const uint16_t* scales2;
+  const uint16_t* biases2;
   int64_t y_bytes;          // extent of y written by this call (fast kernel stores)
   // column map: rows [seg_row0[s], seg_row0[s+1]) are written at column
   // row + seg_delta[s] (one segment {0, 0} for plain, strided and indexed calls)
@@ -234,6 +240,9 @@ struct Params {
   int32_t seg_row0[kMaxSeg];
   int64_t seg_delta[kMaxSeg];
 };
+
+// silu(g) = g / (1 + exp(-g)), fp32, with the device library's expf
+__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
 
 __device__ __forceinline__ float apply_epi(float v, int epi) {
   if (epi == QGEMV_EPI_RELU2) return v > 0.0f ? v * v : (v != v ? v : 0.0f);
@@ -965,6 +974,13 @@ __global__ __launch_bounds__(kThreads) void qrow_fast(const Params p) {
 // at create from its shape, never from the window).  The S waves of a
 // column group each fold their part's units in order from zero, and the
 // parts are then added in order, P = ((P0 + P1) + P2) + P3, through LDS.
+//
+// Gate/up pairs: the 16 MFMA columns of a tile are rows f0..f0+7 of the gate
+// matrix (columns 0-7) and the same rows of the up matrix (columns 8-15).
+// Even loads of a group fetch only columns 0-7 and odd loads only 8-15, so
+// each load reads one matrix.  Every column keeps the arithmetic it has in
+// a plain call; at the tile's end lane j + 8 hands its up value to lane j
+// (DPP row rotate by 8), which stores silu(g) * u for output column f0 + j.
 // ---------------------------------------------------------------------------
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -1041,6 +1057,11 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
   const unsigned char* wexp = reinterpret_cast<const unsigned char*>(p.w) + static_cast<int64_t>(expert) * p.n * row_bytes;
   const unsigned char* sexp = reinterpret_cast<const unsigned char*>(p.scales) + static_cast<int64_t>(expert) * p.n * gpr2;
   const unsigned char* bexp = reinterpret_cast<const unsigned char*>(p.biases) + static_cast<int64_t>(expert) * p.n * gpr2;
+  const bool gu = p.gateup != 0;
+  const int cw = gu ? 8 : 16;                 // output columns per column group
+  const unsigned char* wexp2 = gu ? reinterpret_cast<const unsigned char*>(p.w2) + static_cast<int64_t>(expert) * p.n * row_bytes : wexp;
+  const unsigned char* sexp2 = gu ? reinterpret_cast<const unsigned char*>(p.scales2) + static_cast<int64_t>(expert) * p.n * gpr2 : sexp;
+  const unsigned char* bexp2 = gu ? reinterpret_cast<const unsigned char*>(p.biases2) + static_cast<int64_t>(expert) * p.n * gpr2 : bexp;
   const int my_tiles = bx < p.tiles ? (p.tiles - 1 - bx) / gx + 1 : 0;
   const int steps = my_tiles * gpp;
   const __amdgpu_buffer_rsrc_t yres = make_rsrc(p.y, p.y_bytes);
@@ -1054,13 +1075,15 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
   for (int t = 0; t < MG::WLD; ++t) {
     const int lam = 8 * t + lane / 8, c = lam % 16, ln = lam / 16;
     const int pp = (lane % 8 - c / 2) & 7;
-    w_voff[t] = static_cast<int>(c * row_bytes) + ln * 128 + pp * 16;
+    const int row = gu ? (c & 7) : c;         // row of its matrix within the tile
+    w_voff[t] = static_cast<int>(row * row_bytes) + ln * 128 + pp * 16;
   }
   // scale (bias) load: lane L < SLANES brings piece (or dword) L % per of
   // column L / per, per = SBP / SSZ
   constexpr int SPER = MG::SBP / SSZ;
   const bool s_live = lane < MG::SLANES;
-  const int s_voff = (lane / SPER) * gpr2 + (lane % SPER) * SSZ;
+  const int s_col = lane / SPER;
+  const int s_voff = (gu ? (s_col & 7) : s_col) * gpr2 + (lane % SPER) * SSZ;
   const int s_woff = (lane / SPER) * MG::SSTR + (lane % SPER) * SSZ;   // its place in the slot
   // this lane's unit words in round r: word w = r*4B + qd*B + h of column
   // j's share sits at piece w / 4 -> line (w/4) / 8, piece (w/4) % 8
@@ -1097,7 +1120,7 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
   // a step's loads into registers (past the last step: loads that read nothing)
   auto load_stage = [&](Stage& sg, const Cursor& c) {
     const bool real = c.st < steps;
-    const int c0 = ((bx + c.i * gx) * ncg + cg) * 16;
+    const int c0 = ((bx + c.i * gx) * ncg + cg) * cw;
     const int ncols = real ? n - c0 : 0;
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(wexp + static_cast<int64_t>(c0) * row_bytes,
                                                 static_cast<int64_t>(ncols) * row_bytes);
@@ -1105,22 +1128,46 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
                                                 static_cast<int64_t>(ncols) * gpr2);
     const __amdgpu_buffer_rsrc_t br = make_rsrc(bexp + static_cast<int64_t>(c0) * gpr2,
                                                 static_cast<int64_t>(ncols) * gpr2);
+    // the up matrix's rows of the same tile (gate/up pairs only)
+    const __amdgpu_buffer_rsrc_t wr2 = make_rsrc(wexp2 + static_cast<int64_t>(c0) * row_bytes,
+                                                 static_cast<int64_t>(gu ? ncols : 0) * row_bytes);
     const int wsoff = c.gr * (MG::L * 128);
 #pragma unroll
-    for (int t = 0; t < MG::WLD; ++t) sg.w[t] = __builtin_amdgcn_raw_buffer_load_b128(wr, w_voff[t], wsoff, kNt);
+    for (int t = 0; t < MG::WLD; ++t)
+      sg.w[t] = __builtin_amdgcn_raw_buffer_load_b128((t & 1) && gu ? wr2 : wr, w_voff[t], wsoff, kNt);
     // this group's scales: SB bytes per column from byte gr*SB of the row
     // (at SB = 2, the aligned dword that holds them); default cache policy,
-    // since a row's scale line serves several groups
+    // since a row's scale line serves several groups.  A gate/up tile loads
+    // its gate columns and its up columns separately (a lane outside a
+    // load's range reads zeros), and merges them.
     const int ssoff = MG::SB < 4 ? ((c.gr * MG::SB) & ~3) : c.gr * MG::SB;
-    const int sv = s_live ? s_voff : 0x7ffffff0;
+    const int sv = s_live && !(gu && s_col >= 8) ? s_voff : 0x7ffffff0;
     if constexpr (SSZ == 16) {
-      const u32x4 a4 = __builtin_amdgcn_raw_buffer_load_b128(sr, sv, ssoff, 0);
-      const u32x4 b4 = __builtin_amdgcn_raw_buffer_load_b128(br, sv, ssoff, 0);
+      u32x4 a4 = __builtin_amdgcn_raw_buffer_load_b128(sr, sv, ssoff, 0);
+      u32x4 b4 = __builtin_amdgcn_raw_buffer_load_b128(br, sv, ssoff, 0);
+      if (gu) {
+        const __amdgpu_buffer_rsrc_t sr2 = make_rsrc(sexp2 + static_cast<int64_t>(c0) * gpr2,
+                                                     static_cast<int64_t>(ncols) * gpr2);
+        const __amdgpu_buffer_rsrc_t br2 = make_rsrc(bexp2 + static_cast<int64_t>(c0) * gpr2,
+                                                     static_cast<int64_t>(ncols) * gpr2);
+        const int sv2 = s_live && s_col >= 8 ? s_voff : 0x7ffffff0;
+        a4 |= __builtin_amdgcn_raw_buffer_load_b128(sr2, sv2, ssoff, 0);
+        b4 |= __builtin_amdgcn_raw_buffer_load_b128(br2, sv2, ssoff, 0);
+      }
       sg.s[0] = a4.x; sg.s[1] = a4.y; sg.s[2] = a4.z; sg.s[3] = a4.w;
       sg.b[0] = b4.x; sg.b[1] = b4.y; sg.b[2] = b4.z; sg.b[3] = b4.w;
     } else {
       sg.s[0] = __builtin_amdgcn_raw_buffer_load_b32(sr, sv, ssoff, 0);
       sg.b[0] = __builtin_amdgcn_raw_buffer_load_b32(br, sv, ssoff, 0);
+      if (gu) {
+        const __amdgpu_buffer_rsrc_t sr2 = make_rsrc(sexp2 + static_cast<int64_t>(c0) * gpr2,
+                                                     static_cast<int64_t>(ncols) * gpr2);
+        const __amdgpu_buffer_rsrc_t br2 = make_rsrc(bexp2 + static_cast<int64_t>(c0) * gpr2,
+                                                     static_cast<int64_t>(ncols) * gpr2);
+        const int sv2 = s_live && s_col >= 8 ? s_voff : 0x7ffffff0;
+        sg.s[0] |= __builtin_amdgcn_raw_buffer_load_b32(sr2, sv2, ssoff, 0);
+        sg.b[0] |= __builtin_amdgcn_raw_buffer_load_b32(br2, sv2, ssoff, 0);
+      }
     }
   };
 
@@ -1260,7 +1307,7 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
         }
     }
     if (c.gr == gr0 + gpp - 1) {
-      const int col = ((bx + c.i * gx) * ncg + cg) * 16 + j;
+      const int col = ((bx + c.i * gx) * ncg + cg) * cw + j;
       float out[NMB];
       bool store = true;
       if (S == 1) {
@@ -1282,13 +1329,22 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
         }
         __syncthreads();
       }
+      if (gu) {
+        // lane j + 8 (up) hands its value to lane j (gate) in each 16-lane row
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+          const float u = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(out[mb]), 0x128, 0xf, 0xf, false));
+          out[mb] = silu_f32(out[mb]) * u;
+        }
+      }
       if (store) {
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) {
           const int em = 4 * mb + qd;
-          const bool ok = em < mcount && col < n;
+          const bool ok = em < mcount && col < n && j < cw;
           const int off = ok ? static_cast<int>((s_yoff[ok ? em : 0] + mapped_column(p, col)) * 4) : 0x7ffffff0;
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(apply_epi(out[mb], p.epi)), yres, off, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(gu ? out[mb] : apply_epi(out[mb], p.epi)), yres,
+                                                off, 0, 0);
         }
       }
 #pragma unroll

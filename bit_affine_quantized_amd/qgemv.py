@@ -75,6 +75,10 @@ def load(path: str | None = None):
             lib.qgemv_run_strided.restype = ctypes.c_int
             lib.qgemv_run_indexed.argtypes = [p, p, i32, p, i32, p, i32, p]
             lib.qgemv_run_indexed.restype = ctypes.c_int
+            lib.qgemv_run_gateup.argtypes = [p, p, p, i32, p, i64, p]
+            lib.qgemv_run_gateup.restype = ctypes.c_int
+            lib.qgemv_run_gateup_indexed.argtypes = [p, p, p, i32, p, i32, p, p]
+            lib.qgemv_run_gateup_indexed.restype = ctypes.c_int
             lib.qgemv_debug_unpack.argtypes = [p, i32, p, p]
             lib.qgemv_debug_unpack.restype = ctypes.c_int
             lib.qgemv_strerror.argtypes = [ctypes.c_int]
@@ -152,6 +156,14 @@ def qgemv_run_strided(h, x, m, y, ldy, epi=QGEMV_EPI_NONE, stream=None) -> int:
 
 def qgemv_run_indexed(h, x, m, idx, slots, y, epi=QGEMV_EPI_NONE, stream=None) -> int:
     return load().qgemv_run_indexed(h, _addr(x), m, _addr(idx), slots, _addr(y), epi, _stream(stream))
+
+
+def qgemv_run_gateup(gate, up, x, m, y, ldy, stream=None) -> int:
+    return load().qgemv_run_gateup(gate, up, _addr(x), m, _addr(y), ldy, _stream(stream))
+
+
+def qgemv_run_gateup_indexed(gate, up, x, m, idx, slots, y, stream=None) -> int:
+    return load().qgemv_run_gateup_indexed(gate, up, _addr(x), m, _addr(idx), slots, _addr(y), _stream(stream))
 
 
 def qgemv_debug_unpack(h, expert, codes, stream=None) -> int:

@@ -182,6 +182,24 @@ int qgemv_run_strided(qgemv_t h, const uint16_t* x, int32_t m, float* y, int64_t
 int qgemv_run_indexed(qgemv_t h, const uint16_t* x, int32_t m, const int32_t* idx,
                       int32_t slots, float* y, int32_t epi, void* stream);
 
+/* ---- gate/up pairs ------------------------------------------------------
+ * The fused gate/up of a gated MLP or expert ("experts gate/up (through
+ * silu)" and "the fused gate/up", P788 "tf-flashnext-widths"; one kernel
+ * reads both, so gate and up must share a width, P774 "What this changes"):
+ *   y[i][j] = silu(g) * u,   g = row j of `gate` times x[i],
+ *                            u = row j of `up`   times x[i],
+ *   silu(g) = g / (1 + exp(-g)) in fp32 (the device library's expf).
+ * g and u have exactly the bits qgemv_run gives each handle; one dispatch
+ * reads both matrices.  gate and up: QGEMV_ARITH_MFMA handles of equal bits,
+ * group, n, k and n_experts (QGEMV_E_NOKERNEL for another form,
+ * QGEMV_E_SHAPE for unequal shapes).  Windows, strides, alignment, aliasing
+ * and refusals as qgemv_run_strided (m up to QGEMV_MAX_PROMPT) and
+ * qgemv_run_indexed (the same expert of both stacks for each slot). */
+int qgemv_run_gateup(qgemv_t gate, qgemv_t up, const uint16_t* x, int32_t m, float* y, int64_t ldy,
+                     void* stream);
+int qgemv_run_gateup_indexed(qgemv_t gate, qgemv_t up, const uint16_t* x, int32_t m, const int32_t* idx,
+                             int32_t slots, float* y, void* stream);
+
 /* Test hook: the kernels' own unpack of expert `expert` into codes[n][k]
  * (uint8, device, n*k bytes): each code is cut and converted exactly as the
  * product kernels do it, then written back as an integer. */

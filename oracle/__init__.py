@@ -55,6 +55,8 @@ def _bind(lib):
     lib.oracle_gemv.restype = ctypes.c_int
     lib.oracle_relu2.argtypes = [p, i64, p]
     lib.oracle_relu2.restype = None
+    lib.oracle_silu_gateup.argtypes = [p, p, i64, p]
+    lib.oracle_silu_gateup.restype = None
     return lib
 
 
@@ -155,6 +157,19 @@ def relu2(y: np.ndarray, lib=None) -> np.ndarray:
     return out
 
 
+def silu_gateup(g: np.ndarray, u: np.ndarray, lib=None) -> np.ndarray:
+    """Gate/up pair in fp64: silu(g) * u, silu(g) = g / (1 + exp(-g)) (the
+    experts' "gate/up (through silu)" class, P788 "tf-flashnext-widths").
+    Pinned by tests/test_oracle_pins.py against g * (1 + tanh(g/2)) / 2."""
+    lib = lib or load()
+    gg = np.ascontiguousarray(g, dtype=np.float64)
+    uu = np.ascontiguousarray(u, dtype=np.float64)
+    assert gg.shape == uu.shape
+    out = np.empty_like(gg)
+    lib.oracle_silu_gateup(_ptr(gg), _ptr(uu), gg.size, _ptr(out))
+    return out
+
+
 def gemv_indexed(words, scales, biases, x, idx, bits, group, n, k, scale_mult=1.0,
                  threads: int = 1, lib=None):
     """Indexed slots: output (i, s) is row i times the expert idx[i, s]
@@ -199,6 +214,24 @@ def tol_relu2(y64: np.ndarray, tol: np.ndarray) -> np.ndarray:
     under |dy| <= E, plus one fp32 rounding of the product."""
     ay = np.abs(y64)
     return tol * (2.0 * ay + tol) + U32 * (ay + tol) ** 2
+
+
+SILU_SLOPE = 1.0999   # max |d silu / dg| (about 1.0998, at g = 2.3994)
+
+
+def tol_gateup(g64: np.ndarray, u64: np.ndarray, tol_g: np.ndarray, tol_u: np.ndarray) -> np.ndarray:
+    """Bound for fp32 silu(g) * u given the bounds E_g, E_u on g and u:
+    |silu(G) - silu(g)| <= SILU_SLOPE * E_g; the fp32 evaluation
+    g / (1 + exp(-g)) adds at most 4 roundings (exp within 2 ulp, the add,
+    the divide), E_s = 4u * A + SILU_SLOPE * E_g with A = |silu(g)| +
+    SILU_SLOPE * E_g; then the product: A' * E_u + |u| * E_s + u * A' *
+    (|u| + E_u), A' = |silu(g)| + E_s, u = 2^-24."""
+    s64 = np.abs(silu_gateup(g64, np.ones_like(g64)))
+    a = s64 + SILU_SLOPE * tol_g
+    e_s = 4.0 * U32 * a + SILU_SLOPE * tol_g
+    a2 = s64 + e_s
+    au = np.abs(u64)
+    return a2 * tol_u + au * e_s + U32 * a2 * (au + tol_u)
 
 
 def worst_fraction(err: np.ndarray, tol: np.ndarray) -> float:

@@ -151,3 +151,10 @@ void oracle_relu2(const double *y, int64_t count, double *out) {
     out[i] = v > 0.0 ? v * v : (v != v ? v : 0.0);
   }
 }
+
+/* Gate/up pair of a gated MLP, the experts' "gate/up (through silu)" class
+ * of P788 "tf-flashnext-widths": out = silu(g) * u with silu(g) = g / (1 +
+ * exp(-g)), in fp64. */
+void oracle_silu_gateup(const double *g, const double *u, int64_t count, double *out) {
+  for (int64_t i = 0; i < count; i++) out[i] = g[i] / (1.0 + exp(-g[i])) * u[i];
+}

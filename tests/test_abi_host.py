@@ -216,3 +216,28 @@ def test_window_limits_by_form():
     assert qgemv.qgemv_run_indexed(he, X, 17, IDX, 8, Y, 0, 0) == qgemv.QGEMV_E_WINDOW
     for h in (hd, hm, he):
         qgemv.qgemv_destroy(h)
+
+
+def test_gateup_refusals():
+    """Gate/up pairs: both handles in the MFMA form with equal shapes."""
+    mf, dt = qgemv.QGEMV_ARITH_MFMA, qgemv.QGEMV_ARITH_DOT
+    hs = {}
+    for name, n, arith, e in (("g", 256, mf, 1), ("u", 256, mf, 1), ("u255", 255, mf, 1),
+                              ("gd", 256, dt, 1), ("ud", 256, dt, 1), ("ge", 256, mf, 4), ("ue", 256, mf, 4)):
+        rc, hs[name] = qgemv.qgemv_create_arith(6, 32, n, 2048, W, S, B, arith, n_experts=e)
+        assert rc == 0
+    gu, gi = qgemv.qgemv_run_gateup, qgemv.qgemv_run_gateup_indexed
+    assert gu(None, hs["u"], X, 1, Y, 256) == qgemv.QGEMV_E_ARG
+    assert gu(hs["gd"], hs["ud"], X, 1, Y, 256) == qgemv.QGEMV_E_NOKERNEL
+    assert gu(hs["g"], hs["ud"], X, 1, Y, 256) == qgemv.QGEMV_E_NOKERNEL
+    assert gu(hs["g"], hs["u255"], X, 1, Y, 256) == qgemv.QGEMV_E_SHAPE
+    assert gu(hs["g"], hs["ue"], X, 1, Y, 256) == qgemv.QGEMV_E_SHAPE
+    assert gu(hs["g"], hs["u"], X, 66, Y, 256) == qgemv.QGEMV_E_WINDOW
+    assert gu(hs["g"], hs["u"], X, 1, Y, 255) == qgemv.QGEMV_E_STRIDE
+    assert gu(hs["ge"], hs["ue"], X, 1, Y, 256) == qgemv.QGEMV_E_ARG          # plain pair on expert stacks
+    assert gu(hs["g"], hs["u"], X, 0, Y, 256) == qgemv.QGEMV_OK               # nothing launched
+    assert gi(hs["ge"], hs["ue"], X, 17, IDX, 8, Y) == qgemv.QGEMV_E_WINDOW
+    assert gi(hs["ge"], hs["ue"], X, 2, IDX, 65, Y) == qgemv.QGEMV_E_ARG
+    assert gi(hs["ge"], hs["ue"], X, 2, IDX + 2, 8, Y) == qgemv.QGEMV_E_ALIGN
+    for h in hs.values():
+        qgemv.qgemv_destroy(h)

@@ -177,6 +177,97 @@ def test_prompt_windows(bits, group):
         dot.run(pool[:17], torch.empty((17, n), dtype=torch.float32, device=DEV), m=17)
 
 
+GATEUP = [(6, 32, 1003, 2048), (4, 64, 1024, 2048), (3, 128, 100, 1024), (8, 32, 48, 512),
+          (2, 64, 300, 2048), (5, 32, 17, 1024)]
+
+
+def _gateup_pair(bits, group, n, k, m, seed, n_experts=1):
+    dg = synth.matrix(seed, bits, group, n, k, m, n_experts=n_experts)
+    du = synth.matrix(seed + 1, bits, group, n, k, n_experts=n_experts)
+    return dg, du
+
+
+@pytest.mark.parametrize("bits,group,n,k", GATEUP)
+def test_gateup_pair(bits, group, n, k):
+    """y = silu(g) * u in one dispatch over the gate and up matrices: within
+    a few fp32 roundings of fp64 silu over the plain calls' own g and u, within
+    the bound against the oracle, and each row's bits the same in every
+    window and position."""
+    print_case("gateup", bits, group, n, k)
+    dg, du = _gateup_pair(bits, group, n, k, 16, 7500 + bits * 10 + group)
+    gate = matrix_of(dg, arith=qgemv.QGEMV_ARITH_MFMA)
+    up = matrix_of(du, arith=qgemv.QGEMV_ARITH_MFMA)
+    xt = dev(dg["x"])
+    rows = {}
+    for m in (1, 5, 16):
+        y = torch.empty((m, n), dtype=torch.float32, device=DEV)
+        assert qgemv.qgemv_run_gateup(gate.h, up.h, xt, m, y, n) == qgemv.QGEMV_OK
+        g = run(gate, xt, m).cpu().numpy().astype(np.float64)
+        u = run(up, xt, m).cpu().numpy().astype(np.float64)
+        yc = y.cpu().numpy()
+        ref = oracle.silu_gateup(g, u)
+        # a few fp32 roundings; below g = -88.7 exp(-g) overflows fp32 and
+        # silu(g) (under 1e-36 |g| there) evaluates to 0
+        floor = 1e-30 * (1.0 + np.abs(u))
+        assert np.all(np.abs(yc - ref) <= 8 * oracle.U32 * np.abs(ref) + floor), f"m={m}"
+        g64, ag, _ = oracle.gemv(dg["words"], dg["scales"], dg["biases"], dg["x"][:m], bits, group, n, k)
+        u64, au, _ = oracle.gemv(du["words"], du["scales"], du["biases"], dg["x"][:m], bits, group, n, k)
+        tol = oracle.tol_gateup(g64, u64, oracle.tol_y(ag, k), oracle.tol_y(au, k))
+        err = np.abs(yc - oracle.silu_gateup(g64, u64))
+        assert np.all(err <= tol), f"m={m}: worst err/bound {oracle.worst_fraction(err, tol):.3f}"
+        rows[m] = y
+    for m in (5, 16):
+        assert bits_equal(rows[m][:1], rows[1])
+    y1 = torch.empty((1, n), dtype=torch.float32, device=DEV)
+    for r in (3, 15):
+        assert qgemv.qgemv_run_gateup(gate.h, up.h, xt[r:r + 1], 1, y1, n) == qgemv.QGEMV_OK
+        assert bits_equal(y1[0], rows[16][r])
+    # strided: gaps keep their bytes
+    ldy = n + 5
+    sentinel = torch.full((5, ldy), 0x7FC0BEEF, dtype=torch.int32, device=DEV)
+    ys = sentinel.clone().view(torch.float32)
+    assert qgemv.qgemv_run_gateup(gate.h, up.h, xt, 5, ys.view(-1)[2:], ldy) == qgemv.QGEMV_OK
+    assert bits_equal(ys[:, 2:2 + n], rows[5])
+    gap = torch.ones((5, ldy), dtype=torch.bool, device=DEV)
+    gap[:, 2:2 + n] = False
+    assert torch.equal(ys.view(torch.int32)[gap], sentinel[gap])
+
+
+def test_gateup_indexed_and_refusals():
+    """Indexed gate/up: each (row, slot) equals the pair call on that expert's
+    own gate and up handles; unequal shapes and the dot form are refused."""
+    bits, group, n, k, e = 3, 64, 300, 1024, 6
+    dg, du = _gateup_pair(bits, group, n, k, 9, 7700, n_experts=e)
+    idx = np.array([[1, 1, 2], [1, 0, 5], [1, 3, 3], [1, 2, 0], [1, 4, 4],
+                    [1, 5, 1], [0, 0, 0], [2, 1, 4], [3, 3, 1]], dtype=np.int32)
+    tg = [dev(dg[key]) for key in ("words", "scales", "biases")]
+    tu = [dev(du[key]) for key in ("words", "scales", "biases")]
+    mf = qgemv.QGEMV_ARITH_MFMA
+    gate = qgemv.Matrix(bits, group, n, k, *tg, n_experts=e, arith=mf)
+    up = qgemv.Matrix(bits, group, n, k, *tu, n_experts=e, arith=mf)
+    xt = dev(dg["x"])
+    y = torch.empty((9, 3, n), dtype=torch.float32, device=DEV)
+    assert qgemv.qgemv_run_gateup_indexed(gate.h, up.h, xt, 9, dev(idx), 3, y.view(-1)) == qgemv.QGEMV_OK
+    y1 = torch.empty((1, n), dtype=torch.float32, device=DEV)
+    views = {}
+    for i in range(9):
+        for s_ in range(3):
+            ex = int(idx[i, s_])
+            if ex not in views:
+                views[ex] = (qgemv.Matrix(bits, group, n, k, tg[0][ex], tg[1][ex], tg[2][ex], arith=mf),
+                             qgemv.Matrix(bits, group, n, k, tu[0][ex], tu[1][ex], tu[2][ex], arith=mf))
+            vg, vu = views[ex]
+            assert qgemv.qgemv_run_gateup(vg.h, vu.h, xt[i:i + 1], 1, y1, n) == qgemv.QGEMV_OK
+            assert bits_equal(y1[0], y[i, s_]), (i, s_)
+    # refusals
+    dot_g = qgemv.Matrix(bits, group, n, k, tg[0][0], tg[1][0], tg[2][0], arith=qgemv.QGEMV_ARITH_DOT)
+    dot_u = qgemv.Matrix(bits, group, n, k, tu[0][0], tu[1][0], tu[2][0], arith=qgemv.QGEMV_ARITH_DOT)
+    assert qgemv.qgemv_run_gateup(dot_g.h, dot_u.h, xt, 1, y1, n) == qgemv.QGEMV_E_NOKERNEL
+    vg0, _ = views[0]
+    narrow = qgemv.Matrix(bits, group, n - 1, k, tu[0][0], tu[1][0], tu[2][0], arith=mf)
+    assert qgemv.qgemv_run_gateup(vg0.h, narrow.h, xt, 1, y1, n) == qgemv.QGEMV_E_SHAPE
+
+
 @arith_param
 @pytest.mark.parametrize("bits,group", PAIRS)
 def test_exact_representable_inputs(bits, group, arith):

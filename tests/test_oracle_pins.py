@@ -15,6 +15,8 @@ import sys
 import tempfile
 from fractions import Fraction
 
+import math
+
 import numpy as np
 import pytest
 
@@ -226,6 +228,36 @@ def test_relu2_rule():
     r = oracle.relu2(v)
     assert r[0] == 0 and r[1] == 0 and r[2] == 0 and not np.signbit(r[2])
     assert r[3] == 4.0 and np.isnan(r[4]) and r[5] == 1e-3 * 1e-3
+
+
+def test_silu_gateup_against_an_independent_form():
+    """silu(g) * u, pinned to g * expit(g) * u (scipy's logistic function),
+    to g * (1 + tanh(g / 2)) / 2 * u where that form has no cancellation, to
+    its closed-form values, and its tolerance's slope constant to the
+    derivative's maximum."""
+    from scipy.special import expit
+    g = np.linspace(-30.0, 30.0, 6001)
+    u = np.cos(g) * 3.0 + 0.5
+    got = oracle.silu_gateup(g, u)
+    assert np.allclose(got, g * expit(g) * u, rtol=1e-14, atol=1e-300)
+    ok = g > -4.0
+    assert np.allclose(got[ok], (g * (1.0 + np.tanh(g / 2.0)) / 2.0 * u)[ok], rtol=1e-12, atol=1e-300)
+    assert oracle.silu_gateup(np.array([0.0]), np.array([7.0]))[0] == 0.0
+    assert oracle.silu_gateup(np.array([40.0]), np.array([1.0]))[0] == 40.0
+    assert math.isclose(oracle.silu_gateup(np.array([1.0]), np.array([2.0]))[0], 2.0 / (1.0 + math.exp(-1.0)),
+                        rel_tol=1e-15)
+    assert math.isnan(oracle.silu_gateup(np.array([np.nan]), np.array([1.0]))[0])
+    # the bound's slope constant covers |silu'|, whose maximum is about 1.0998
+    gg = np.linspace(-20.0, 20.0, 400001)
+    sig = 1.0 / (1.0 + np.exp(-gg))
+    slope = np.max(np.abs(sig * (1.0 + gg * (1.0 - sig))))
+    assert 1.0998 < slope <= oracle.SILU_SLOPE < 1.1
+    # the bound grows with either input bound and is positive at zero error
+    g3, u3 = np.array([0.7, -2.0, 5.0]), np.array([1.5, -0.3, 2.0])
+    t0 = oracle.tol_gateup(g3, u3, np.zeros(3), np.zeros(3))
+    t1 = oracle.tol_gateup(g3, u3, np.full(3, 1e-6), np.zeros(3))
+    t2 = oracle.tol_gateup(g3, u3, np.zeros(3), np.full(3, 1e-6))
+    assert np.all(t0 > 0) and np.all(t1 > t0) and np.all(t2 > t0)
 
 
 def test_indexed_is_plain_on_the_expert():
