@@ -226,7 +226,12 @@ def test_gateup_refusals():
                               ("gd", 256, dt, 1), ("ud", 256, dt, 1), ("ge", 256, mf, 4), ("ue", 256, mf, 4)):
         rc, hs[name] = qgemv.qgemv_create_arith(6, 32, n, 2048, W, S, B, arith, n_experts=e)
         assert rc == 0
-    gu, gi = qgemv.qgemv_run_gateup, qgemv.qgemv_run_gateup_indexed
+    def gu(*args):
+        return qgemv.qgemv_run_gateup(*args, 0)
+
+    def gi(*args):
+        return qgemv.qgemv_run_gateup_indexed(*args, 0)
+
     assert gu(None, hs["u"], X, 1, Y, 256) == qgemv.QGEMV_E_ARG
     assert gu(hs["gd"], hs["ud"], X, 1, Y, 256) == qgemv.QGEMV_E_NOKERNEL
     assert gu(hs["g"], hs["ud"], X, 1, Y, 256) == qgemv.QGEMV_E_NOKERNEL
