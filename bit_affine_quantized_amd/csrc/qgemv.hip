@@ -57,6 +57,40 @@ static KernelFn unpack_fn(int bits) {
   return nullptr;
 }
 
+// Exact widen: unit t of the flattened rows (bin words) is re-cut at bout
+// bits per code (bout words), the same integer codes, low code first.
+__global__ __launch_bounds__(kThreads) void widen_kernel(const uint32_t* __restrict__ w_in, int bin,
+                                                         uint32_t* __restrict__ w_out, int bout,
+                                                         int64_t units) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (t >= units) return;
+  const uint32_t* src = w_in + t * bin;
+  uint32_t* dst = w_out + t * bout;
+  const uint32_t mask = (1u << bin) - 1u;
+  uint64_t acc = 0;
+  int have = 0, wo = 0;
+  for (int j = 0; j < 32; ++j) {
+    const int bit = j * bin, wi = bit >> 5, sh = bit & 31;
+    const uint64_t win = static_cast<uint64_t>(src[wi]) | (wi + 1 < bin ? static_cast<uint64_t>(src[wi + 1]) << 32 : 0);
+    acc |= static_cast<uint64_t>(static_cast<uint32_t>(win >> sh) & mask) << have;
+    have += bout;
+    if (have >= 32) {
+      dst[wo++] = static_cast<uint32_t>(acc);
+      acc >>= 32;
+      have -= 32;
+    }
+  }
+}
+
+// Exact regroup: each group's value repeated for the `ratio` smaller groups
+// it splits into (rows stay aligned: a row of g groups becomes g * ratio).
+__global__ __launch_bounds__(kThreads) void regroup_kernel(const uint16_t* __restrict__ in,
+                                                           uint16_t* __restrict__ out, int ratio,
+                                                           int64_t total) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (t < total) out[t] = in[t / ratio];
+}
+
 }  // namespace qg
 
 // ---------------------------------------------------------------------------
@@ -536,6 +570,62 @@ int qgemv_debug_unpack(qgemv_t h, int32_t expert, uint8_t* codes, void* stream) 
   return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_E_HIP;
 }
 
+
+int qgemv_common_width(const int32_t* bits, const int32_t* groups, int32_t count, int32_t* bits_out,
+                       int32_t* group_out) {
+  if (!bits || !groups || !bits_out || !group_out || count < 1) return QGEMV_E_ARG;
+  int32_t b = 0, g = 1 << 30;
+  for (int32_t i = 0; i < count; ++i) {
+    if (qg::bits_index(bits[i]) < 0) return QGEMV_E_BITS;
+    if (qg::group_index(groups[i]) < 0) return QGEMV_E_GROUP;
+    if (bits[i] > b) b = bits[i];
+    if (groups[i] < g) g = groups[i];
+  }
+  *bits_out = b;
+  *group_out = g;
+  return QGEMV_OK;
+}
+
+int qgemv_widen(const qgemv_desc* src, int32_t bits_out, int32_t group_out, uint32_t* w_out, uint16_t* scales_out,
+                uint16_t* biases_out, void* stream) {
+  if (!src || !w_out || !scales_out || !biases_out) return QGEMV_E_ARG;
+  // the source is admitted exactly as qgemv_create admits it
+  qgemv_t probe = nullptr;
+  const int rc = qgemv_create(src, &probe);
+  if (rc != QGEMV_OK) return rc;
+  qgemv_destroy(probe);
+  if (qg::bits_index(bits_out) < 0 || bits_out < src->bits) return QGEMV_E_BITS;
+  if (qg::group_index(group_out) < 0 || src->group % group_out != 0) return QGEMV_E_GROUP;
+  if (reinterpret_cast<uintptr_t>(w_out) & 15 || reinterpret_cast<uintptr_t>(scales_out) & 1 ||
+      reinterpret_cast<uintptr_t>(biases_out) & 1)
+    return QGEMV_E_ALIGN;
+  const int64_t rows = src->n * src->n_experts;
+  const int64_t units = rows * (src->k / 32);
+  const int64_t groups_out = rows * (src->k / group_out);
+  const size_t in_w = static_cast<size_t>(units) * src->bits * 4, out_w = static_cast<size_t>(units) * bits_out * 4;
+  const size_t in_s = static_cast<size_t>(rows) * (src->k / src->group) * 2, out_s = static_cast<size_t>(groups_out) * 2;
+  for (const void* o : {static_cast<const void*>(w_out), static_cast<const void*>(scales_out),
+                        static_cast<const void*>(biases_out)}) {
+    const size_t ob = o == w_out ? out_w : out_s;
+    if (overlaps(o, ob, src->w, in_w) || overlaps(o, ob, src->scales, in_s) || overlaps(o, ob, src->biases, in_s))
+      return QGEMV_E_ALIAS;
+  }
+  if (overlaps(w_out, out_w, scales_out, out_s) || overlaps(w_out, out_w, biases_out, out_s) ||
+      overlaps(scales_out, out_s, biases_out, out_s))
+    return QGEMV_E_ALIAS;
+  if (!current_device()) return QGEMV_E_HIP;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const int ratio = src->group / group_out;
+  hipLaunchKernelGGL(qg::widen_kernel, dim3(static_cast<unsigned>((units + qg::kThreads - 1) / qg::kThreads)),
+                     dim3(qg::kThreads), 0, st, src->w, static_cast<int>(src->bits), w_out,
+                     static_cast<int>(bits_out), units);
+  const unsigned gb = static_cast<unsigned>((groups_out + qg::kThreads - 1) / qg::kThreads);
+  hipLaunchKernelGGL(qg::regroup_kernel, dim3(gb), dim3(qg::kThreads), 0, st, src->scales, scales_out, ratio,
+                     groups_out);
+  hipLaunchKernelGGL(qg::regroup_kernel, dim3(gb), dim3(qg::kThreads), 0, st, src->biases, biases_out, ratio,
+                     groups_out);
+  return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_E_HIP;
+}
 
 struct qgemv_stack {
   int n_runs;

@@ -79,6 +79,10 @@ def load(path: str | None = None):
             lib.qgemv_run_gateup.restype = ctypes.c_int
             lib.qgemv_run_gateup_indexed.argtypes = [p, p, p, i32, p, i32, p, p]
             lib.qgemv_run_gateup_indexed.restype = ctypes.c_int
+            lib.qgemv_common_width.argtypes = [p, p, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+            lib.qgemv_common_width.restype = ctypes.c_int
+            lib.qgemv_widen.argtypes = [ctypes.POINTER(qgemv_desc), i32, i32, p, p, p, p]
+            lib.qgemv_widen.restype = ctypes.c_int
             lib.qgemv_debug_unpack.argtypes = [p, i32, p, p]
             lib.qgemv_debug_unpack.restype = ctypes.c_int
             lib.qgemv_strerror.argtypes = [ctypes.c_int]
@@ -164,6 +168,23 @@ def qgemv_run_gateup(gate, up, x, m, y, ldy, stream=None) -> int:
 
 def qgemv_run_gateup_indexed(gate, up, x, m, idx, slots, y, stream=None) -> int:
     return load().qgemv_run_gateup_indexed(gate, up, _addr(x), m, _addr(idx), slots, _addr(y), _stream(stream))
+
+
+def qgemv_common_width(bits, groups):
+    """Returns (status, bits, group) for lists of member bits and groups."""
+    n = len(bits)
+    ab = (ctypes.c_int32 * max(1, n))(*bits)
+    ag = (ctypes.c_int32 * max(1, n))(*groups)
+    ob, og = ctypes.c_int32(), ctypes.c_int32()
+    rc = load().qgemv_common_width(ctypes.addressof(ab), ctypes.addressof(ag), n, ctypes.byref(ob), ctypes.byref(og))
+    return rc, ob.value, og.value
+
+
+def qgemv_widen(bits, group, n, k, w, scales, biases, bits_out, group_out, w_out, scales_out, biases_out,
+                n_experts=1, stream=None) -> int:
+    d = qgemv_desc(bits, group, n, k, n_experts, _addr(w), _addr(scales), _addr(biases))
+    return load().qgemv_widen(ctypes.byref(d), bits_out, group_out, _addr(w_out), _addr(scales_out),
+                              _addr(biases_out), _stream(stream))
 
 
 def qgemv_debug_unpack(h, expert, codes, stream=None) -> int:

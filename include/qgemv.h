@@ -200,6 +200,31 @@ int qgemv_run_gateup(qgemv_t gate, qgemv_t up, const uint16_t* x, int32_t m, flo
 int qgemv_run_gateup_indexed(qgemv_t gate, qgemv_t up, const uint16_t* x, int32_t m, const int32_t* idx,
                              int32_t slots, float* y, void* stream);
 
+/* ---- exact widen / regroup ----------------------------------------------
+ * A projection of mixed-width members can be read as one matrix at their
+ * common width, the most bits and the smallest group (P788, the commit that
+ * adds widen.zig, "...tables repeated for a smaller group").
+ * qgemv_common_width: that width of `count` members (bits and groups as in
+ *   qgemv_desc; QGEMV_E_BITS / QGEMV_E_GROUP for values the kernels do not
+ *   run, QGEMV_E_ARG for count < 1).  Host only.
+ * qgemv_widen: src's codes re-cut at bits_out bits (the same integer codes,
+ *   low code first) and each group's scale and bias repeated for the
+ *   src->group / group_out groups it splits into, so every dequantized value
+ *   scale * q + bias is unchanged, bit for bit.  src is admitted as
+ *   qgemv_create admits it; an expert stack widens row for row.  Output
+ *   arrays (device, caller-owned): w_out uint32 [E][N][K*bits_out/32]
+ *   16-byte aligned, scales_out and biases_out bf16 [E][N][K/group_out].
+ *   Narrowing (bits_out < src->bits) is refused with QGEMV_E_BITS, a group
+ *   that does not divide the source group with QGEMV_E_GROUP, outputs that
+ *   overlap the source or each other with QGEMV_E_ALIAS.  Enqueued on
+ *   `stream`; the same width and group copy the arrays as they are.  A
+ *   fused projection's members widen one call each into consecutive rows of
+ *   one output, keeping each member's values in order. */
+int qgemv_common_width(const int32_t* bits, const int32_t* groups, int32_t count, int32_t* bits_out,
+                       int32_t* group_out);
+int qgemv_widen(const qgemv_desc* src, int32_t bits_out, int32_t group_out, uint32_t* w_out, uint16_t* scales_out,
+                uint16_t* biases_out, void* stream);
+
 /* Test hook: the kernels' own unpack of expert `expert` into codes[n][k]
  * (uint8, device, n*k bytes): each code is cut and converted exactly as the
  * product kernels do it, then written back as an integer. */

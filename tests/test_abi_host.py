@@ -246,3 +246,24 @@ def test_gateup_refusals():
     assert gi(hs["ge"], hs["ue"], X, 2, IDX + 2, 8, Y) == qgemv.QGEMV_E_ALIGN
     for h in hs.values():
         qgemv.qgemv_destroy(h)
+
+
+def test_common_width_and_widen_refusals():
+    """The common width takes the most bits and the smallest group; narrowing,
+    a group that does not divide the source's, and widths the kernels do not
+    run are refused before any HIP call."""
+    assert qgemv.qgemv_common_width([4, 5, 6], [64, 128, 32]) == (0, 6, 32)
+    assert qgemv.qgemv_common_width([3], [128]) == (0, 3, 128)
+    assert qgemv.qgemv_common_width([4, 7], [64, 64])[0] == qgemv.QGEMV_E_BITS
+    assert qgemv.qgemv_common_width([4, 4], [64, 48])[0] == qgemv.QGEMV_E_GROUP
+    assert qgemv.qgemv_common_width([], [])[0] == qgemv.QGEMV_E_ARG
+    WO, SO, BO = 0x1000000, 0x2000000, 0x3000000
+    wd = lambda *a, **kw: qgemv.qgemv_widen(*a, stream=0, **kw)
+    assert wd(5, 64, 16, 2048, W, S, B, 4, 64, WO, SO, BO) == qgemv.QGEMV_E_BITS     # narrowing
+    assert wd(5, 64, 16, 2048, W, S, B, 7, 64, WO, SO, BO) == qgemv.QGEMV_E_BITS
+    assert wd(5, 64, 16, 2048, W, S, B, 6, 128, WO, SO, BO) == qgemv.QGEMV_E_GROUP   # growing the group
+    assert wd(5, 64, 16, 2048, W, S, B, 6, 48, WO, SO, BO) == qgemv.QGEMV_E_GROUP
+    assert wd(5, 64, 16, 2080, W, S, B, 6, 32, WO, SO, BO) == qgemv.QGEMV_E_SHAPE    # the source's own admission
+    assert wd(5, 64, 16, 2048, W, S, B, 6, 32, W + 64, SO, BO) == qgemv.QGEMV_E_ALIAS
+    assert wd(5, 64, 16, 2048, W, S, B, 6, 32, WO, SO, SO + 8) == qgemv.QGEMV_E_ALIAS
+    assert wd(5, 64, 16, 2048, W, S, B, 6, 32, WO + 4, SO, BO) == qgemv.QGEMV_E_ALIGN

@@ -268,6 +268,90 @@ def test_gateup_indexed_and_refusals():
     assert qgemv.qgemv_run_gateup(vg0.h, narrow.h, xt, 1, y1, n) == qgemv.QGEMV_E_SHAPE
 
 
+def _dequant64(words, scales, biases, bits, group, n, k):
+    q = oracle.unpack(words, bits, n, k).astype(np.float64)
+    s = synth.bf16_bits_to_f32(scales).astype(np.float64)
+    b = synth.bf16_bits_to_f32(biases).astype(np.float64)
+    g = np.arange(k) // group
+    return s[:, g] * q + b[:, g]
+
+
+WIDEN = [(bi, gi, bo, go) for bi in (2, 3, 4, 5, 6, 8) for bo in (2, 3, 4, 5, 6, 8) if bo >= bi
+         for gi in (32, 64, 128) for go in (32, 64, 128) if gi % go == 0]
+
+
+def test_widen_is_exact():
+    """Every source width and every wider target, every group and every group
+    that divides it: the fp64 dequantized values are equal bit for bit (two
+    experts widen row for row); the same width comes back as it is."""
+    n, k, e = 6, 1024, 2
+    for (bi, gi, bo, go) in WIDEN:
+        d = synth.matrix(9100 + bi * 1000 + gi + bo * 7 + go, bi, gi, n, k, n_experts=e)
+        tw, ts, tb = dev(d["words"]), dev(d["scales"]), dev(d["biases"])
+        wo = torch.zeros((e, n, k * bo // 32), dtype=torch.int32, device=DEV)
+        so = torch.zeros((e, n, k // go), dtype=torch.int16, device=DEV)
+        bo_ = torch.zeros((e, n, k // go), dtype=torch.int16, device=DEV)
+        rc = qgemv.qgemv_widen(bi, gi, n, k, tw, ts, tb, bo, go, wo, so, bo_, n_experts=e)
+        assert rc == qgemv.QGEMV_OK, qgemv.qgemv_strerror(rc)
+        torch.cuda.synchronize()
+        w2 = wo.cpu().numpy().view(np.uint32)
+        s2, b2 = so.cpu().numpy().view(np.uint16), bo_.cpu().numpy().view(np.uint16)
+        for x in range(e):
+            a = _dequant64(d["words"][x], d["scales"][x], d["biases"][x], bi, gi, n, k)
+            c = _dequant64(w2[x], s2[x], b2[x], bo, go, n, k)
+            assert np.array_equal(a.view(np.int64), c.view(np.int64)), (bi, gi, bo, go, x)
+        if (bi, gi) == (bo, go):
+            assert np.array_equal(w2, d["words"]) and np.array_equal(s2, d["scales"])
+
+
+def test_widen_fused_members_in_order_and_products():
+    """Two members widen to their common width into one matrix, each keeping
+    its values in order; the widened matrix's products, in both forms, meet
+    the bound around the source's fp64 product (the dequantized values are
+    the same; a smaller group re-associates the fp32 sums, so bit equality
+    with the source's product is not expected)."""
+    k = 2048
+    members = [(4, 64, 100), (5, 128, 48)]
+    rc, cb, cg = qgemv.qgemv_common_width([m[0] for m in members], [m[1] for m in members])
+    assert (rc, cb, cg) == (0, 5, 64)
+    rows = sum(m[2] for m in members)
+    wo = torch.zeros((rows, k * cb // 32), dtype=torch.int32, device=DEV)
+    so = torch.zeros((rows, k // cg), dtype=torch.int16, device=DEV)
+    bo = torch.zeros((rows, k // cg), dtype=torch.int16, device=DEV)
+    r0, srcs = 0, []
+    for i, (bits, group, n) in enumerate(members):
+        d = synth.matrix(9500 + i, bits, group, n, k)
+        srcs.append(d)
+        rc = qgemv.qgemv_widen(bits, group, n, k, dev(d["words"]), dev(d["scales"]), dev(d["biases"]),
+                               cb, cg, wo[r0:], so[r0:], bo[r0:])
+        assert rc == qgemv.QGEMV_OK
+        r0 += n
+    torch.cuda.synchronize()
+    full = _dequant64(wo.cpu().numpy().view(np.uint32), so.cpu().numpy().view(np.uint16),
+                      bo.cpu().numpy().view(np.uint16), cb, cg, rows, k)
+    r0 = 0
+    for (bits, group, n), d in zip(members, srcs):
+        a = _dequant64(d["words"], d["scales"], d["biases"], bits, group, n, k)
+        assert np.array_equal(a.view(np.int64), full[r0:r0 + n].view(np.int64))
+        r0 += n
+    # products of widened handles against the source's fp64 product
+    for (bi, gi, bo_, go) in [(3, 64, 6, 32), (5, 128, 8, 64), (2, 128, 4, 128)]:
+        n = 520
+        d = synth.matrix(9600 + bi, bi, gi, n, k, 8)
+        y64, a64, _ = oracle.gemv(d["words"], d["scales"], d["biases"], d["x"], bi, gi, n, k)
+        tw, ts, tb = dev(d["words"]), dev(d["scales"]), dev(d["biases"])
+        w2 = torch.zeros((n, k * bo_ // 32), dtype=torch.int32, device=DEV)
+        s2 = torch.zeros((n, k // go), dtype=torch.int16, device=DEV)
+        b2 = torch.zeros((n, k // go), dtype=torch.int16, device=DEV)
+        assert qgemv.qgemv_widen(bi, gi, n, k, tw, ts, tb, bo_, go, w2, s2, b2) == qgemv.QGEMV_OK
+        xt = dev(d["x"])
+        for arith in ARITHS:
+            wid = qgemv.Matrix(bo_, go, n, k, w2, s2, b2, arith=arith)
+            for m in (1, 8):
+                y = run(wid, xt, m).cpu().numpy()
+                check_bound(y, y64[:m], a64[:m], k, f"widen {bi}/{gi}->{bo_}/{go} arith {arith} m {m}")
+
+
 @arith_param
 @pytest.mark.parametrize("bits,group", PAIRS)
 def test_exact_representable_inputs(bits, group, arith):
