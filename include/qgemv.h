@@ -201,9 +201,10 @@ int qgemv_run_gateup_indexed(qgemv_t gate, qgemv_t up, const uint16_t* x, int32_
                              int32_t slots, float* y, void* stream);
 
 /* ---- exact widen / regroup ----------------------------------------------
- * A projection of mixed-width members can be read as one matrix at their
- * common width, the most bits and the smallest group (P788, the commit that
- * adds widen.zig, "...tables repeated for a smaller group").
+ * Members of one projection stored at different widths can be brought to a
+ * single width: the largest bit count and the smallest group among them
+ * (P788, the commit that adds widen.zig, "...tables repeated for a smaller
+ * group").
  * qgemv_common_width: that width of `count` members (bits and groups as in
  *   qgemv_desc; QGEMV_E_BITS / QGEMV_E_GROUP for values the kernels do not
  *   run, QGEMV_E_ARG for count < 1).  Host only.

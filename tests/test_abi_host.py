@@ -249,9 +249,10 @@ def test_gateup_refusals():
 
 
 def test_common_width_and_widen_refusals():
-    """The common width takes the most bits and the smallest group; narrowing,
-    a group that does not divide the source's, and widths the kernels do not
-    run are refused before any HIP call."""
+    """qgemv_common_width returns the largest bit count and the smallest
+    group of its members.  qgemv_widen refuses, before any HIP call, fewer
+    bits than the source, a target group that does not divide the source
+    group, widths without kernels, and overlapping buffers."""
     assert qgemv.qgemv_common_width([4, 5, 6], [64, 128, 32]) == (0, 6, 32)
     assert qgemv.qgemv_common_width([3], [128]) == (0, 3, 128)
     assert qgemv.qgemv_common_width([4, 7], [64, 64])[0] == qgemv.QGEMV_E_BITS

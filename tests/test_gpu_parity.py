@@ -281,9 +281,10 @@ WIDEN = [(bi, gi, bo, go) for bi in (2, 3, 4, 5, 6, 8) for bo in (2, 3, 4, 5, 6,
 
 
 def test_widen_is_exact():
-    """Every source width and every wider target, every group and every group
-    that divides it: the fp64 dequantized values are equal bit for bit (two
-    experts widen row for row); the same width comes back as it is."""
+    """For each source width, each target of at least as many bits, and each
+    target group dividing the source group, the fp64 dequantized values are
+    identical bit for bit (both experts of a two-expert stack); a target equal
+    to the source returns identical bytes."""
     n, k, e = 6, 1024, 2
     for (bi, gi, bo, go) in WIDEN:
         d = synth.matrix(9100 + bi * 1000 + gi + bo * 7 + go, bi, gi, n, k, n_experts=e)
@@ -305,8 +306,8 @@ def test_widen_is_exact():
 
 
 def test_widen_fused_members_in_order_and_products():
-    """Two members widen to their common width into one matrix, each keeping
-    its values in order; the widened matrix's products, in both forms, meet
+    """Two members of different widths, widened to their common width one call
+    each into consecutive rows of one matrix, keep their values in order; the widened matrix's products, in both forms, meet
     the bound around the source's fp64 product (the dequantized values are
     the same; a smaller group re-associates the fp32 sums, so bit equality
     with the source's product is not expected)."""
