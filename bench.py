@@ -76,7 +76,7 @@ def read_traffic(workload: str):
         return None
 
 
-ARITH_NAMES = {1: "dot", 2: "mfma"}
+ARITH_NAMES = {1: "dot", 2: "mfma", 3: "wide"}
 
 
 class Workload:
@@ -256,7 +256,7 @@ def main():
     ap.add_argument("--m", type=int, default=1, help="window rows")
     ap.add_argument("--all", action="store_true", help="also time the other workloads and windows")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--arith", default="auto", choices=["auto", "dot", "mfma"],
+    ap.add_argument("--arith", default="auto", choices=["auto", "dot", "mfma", "wide"],
                     help="arithmetic of the handles (the fused stack always uses the library's choice)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (known bytes) for counter scaling")
@@ -283,7 +283,7 @@ def main():
 
     qgemv.load()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    arith = {"auto": 0, "dot": 1, "mfma": 2}[args.arith]
+    arith = {"auto": 0, "dot": 1, "mfma": 2, "wide": 3}[args.arith]
     wl = Workload(args.workload, args.m, torch, qgemv, synth, arith)
     ms, batches = time_workload(wl, args.steps, args.warmup, torch)
     gbs = wl.bytes / (ms * 1e-3) / 1e9
@@ -314,8 +314,10 @@ def main():
         for name, m, ar in [("lmhead", 1, arith), ("lmhead", 8, arith), ("lmhead", 16, arith),
                             ("lmhead", 1, 1), ("lmhead", 8, 1), ("lmhead", 16, 1),
                             ("lmhead", 1, 2), ("lmhead", 8, 2), ("lmhead", 16, 2),
+                            ("lmhead", 1, 3), ("lmhead", 8, 3), ("lmhead", 16, 3),
                             ("stack", 1, arith), ("stack", 16, arith), ("stack3", 1, arith), ("stack3", 16, arith),
-                            ("experts", 16, arith), ("experts", 16, 1), ("experts", 16, 2)]:
+                            ("stack3", 16, 3),
+                            ("experts", 16, arith), ("experts", 16, 1), ("experts", 16, 2), ("experts", 16, 3)]:
             w2 = Workload(name, m, torch, qgemv, synth, ar)
             key = f"{name}_m{w2.m}_{w2.arith_used}"
             if key in extra or (name == args.workload and m == wl.m and w2.arith_used == wl.arith_used):

@@ -19,6 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 SOURCES = (["qgemv.hip"] + [f"qgemv_b{b}.hip" for b in (2, 3, 4, 5, 6, 8)]
+           + [f"qgemv_wide_b{b}.hip" for b in (2, 3, 4, 5, 6, 8)]
            + [f"qgemv_stack_m{m}.hip" for m in (1, 2, 4, 8, 16)])
 LIB = os.path.join(HERE, "libqgemv.so")
 BUILD_DIR = os.path.join(HERE, "_build")

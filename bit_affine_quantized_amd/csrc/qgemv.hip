@@ -33,6 +33,12 @@ static const Entry& entry(int bi, int gi) {
   return tables[bi][gi];
 }
 
+static const WideEntry& wide_entry(int bi, int gi) {
+  static const WideEntry* const tables[6] = {wide_entries_b2(), wide_entries_b3(), wide_entries_b4(),
+                                             wide_entries_b5(), wide_entries_b6(), wide_entries_b8()};
+  return tables[bi][gi];
+}
+
 // Geometry of the fast kernels per width: 16-byte pieces and codes per chunk.
 static void fast_geometry(int bits, int* ppc, int* cpc) {
   switch (bits) {
@@ -104,9 +110,10 @@ struct qgemv_handle {
   int lpr, cpl, nchunks; // lanes per column, chunks per lane, chunks per row
   int vec_groups;        // scales/biases aligned for packed loads
   int64_t wpr, gpr;
-  int arith;             // QGEMV_ARITH_DOT or QGEMV_ARITH_MFMA
-  int ksplit;            // matrix-core form: K-parts per column (1, 2 or 4)
+  int arith;             // QGEMV_ARITH_DOT, QGEMV_ARITH_MFMA or QGEMV_ARITH_WIDE
+  int ksplit;            // matrix-core forms: K-parts per column (1, 2 or 4)
   const qg::Entry* entry;
+  const qg::WideEntry* wide;
   // resident blocks per CU of each (window variant, staging) kernel, 0 =
   // not yet known; a benign cache: every thread that fills it writes the
   // same value
@@ -150,9 +157,10 @@ void init_device(DeviceInfo* info) {
                                         hipFuncAttributeMaxDynamicSharedMemorySize,
                                         static_cast<int>(qg::kMaxDynamicLds)) != hipSuccess)
             return;
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(e.mfma[v]), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                static_cast<int>(qg::kMaxMfmaLds)) != hipSuccess)
-          return;
+        for (qg::KernelFn fn : {e.mfma[v], qg::wide_entry(bi, gi).k[v]})
+          if (hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  static_cast<int>(qg::kMaxMfmaLds)) != hipSuccess)
+            return;
       }
     }
   for (int v = 0; v < 5; ++v) {
@@ -182,6 +190,12 @@ bool overlaps(const void* a, size_t abytes, const void* b, size_t bbytes) {
   return a0 < b0 + bbytes && b0 < a0 + abytes;
 }
 
+// Both matrix-core forms share the load groups, K split, window passes and
+// LDS plan; they differ only in how a round's products are formed.
+bool matrix_cores(const qgemv_handle* h) {
+  return h->arith == QGEMV_ARITH_MFMA || h->arith == QGEMV_ARITH_WIDE;
+}
+
 // The window variant of m rows: the narrowest that holds them, the widest
 // (passes of 16 rows) beyond 16.
 int window_variant(int m) {
@@ -205,15 +219,17 @@ size_t lds_bytes(const qgemv_handle* h, int var, int stage) {
 // The matrix-core kernels' LDS: the staged window (rows of k/32 units x 64
 // bytes, a zero area of R * 256 bytes, unit sums; rows padded by 16 bytes),
 // the routed list of an indexed call, one load-group slot per wave, and with
-// a K split the waves' partial sums.  Returns false when it exceeds one
+// a K split the waves' partial sums (one per 4-row block per lane, or in the
+// wide form up to 4 rows per lane).  Returns false when it exceeds one
 // block's LDS.
 bool mfma_plan(const qgemv_handle* h, int var, bool indexed, size_t* lds) {
   const size_t mb = static_cast<size_t>(qg::kWindows[var]);
   const size_t units = static_cast<size_t>(h->d.k) / 32;
   const size_t waves = static_cast<size_t>(h->entry->mfma_waves[var]);
+  const size_t per_lane = h->arith == QGEMV_ARITH_WIDE ? (mb < 4 ? mb : 4) : (mb + 3) / 4;
   const size_t b = mb * (units * 64 + 16) + 256 * static_cast<size_t>(h->entry->mfma_group) + mb * (units + 4) * 4 +
                    (indexed ? qg::kMaxList * 4 : 0) + waves * h->entry->mfma_slot +
-                   (h->ksplit > 1 ? waves * ((mb + 3) / 4) * qg::kWave * 4 : 0);
+                   (h->ksplit > 1 ? waves * per_lane * qg::kWave * 4 : 0);
   if (b > qg::kMaxMfmaLds) return false;
   *lds = b;
   return true;
@@ -242,7 +258,7 @@ int launch(const qgemv_handle* h, const uint16_t* x, int32_t m, float* y, int64_
   // same bits with more scattered loads
   int stage = (h->fast && h->ppc > 1) ? 1 : 0;
   if (stage && lds_bytes(h, var, 1) > qg::kMaxDynamicLds) stage = 0;
-  const bool mfma = h->arith == QGEMV_ARITH_MFMA;
+  const bool mfma = matrix_cores(h);
   size_t lds = 0;
   if (mfma) {
     stage = 0;
@@ -262,7 +278,7 @@ int launch(const qgemv_handle* h, const uint16_t* x, int32_t m, float* y, int64_
   int64_t tile_rows = 0;
   if (mfma) {
     // one wave per 16 output columns
-    fn = h->entry->mfma[var];
+    fn = h->arith == QGEMV_ARITH_WIDE ? h->wide->k[var] : h->entry->mfma[var];
     threads = h->entry->mfma_waves[var] * qg::kWave;
     tile_rows = static_cast<int64_t>(h->entry->mfma_waves[var] / h->ksplit) * (up ? 8 : 16);
   } else {
@@ -368,7 +384,9 @@ int qgemv_arith(qgemv_t h) { return h ? h->arith : QGEMV_E_ARG; }
 
 int qgemv_create_arith(const qgemv_desc* d, int32_t arith, qgemv_t* out) {
   if (!d || !out) return QGEMV_E_ARG;
-  if (arith != QGEMV_ARITH_AUTO && arith != QGEMV_ARITH_DOT && arith != QGEMV_ARITH_MFMA) return QGEMV_E_ARG;
+  if (arith != QGEMV_ARITH_AUTO && arith != QGEMV_ARITH_DOT && arith != QGEMV_ARITH_MFMA &&
+      arith != QGEMV_ARITH_WIDE)
+    return QGEMV_E_ARG;
   const int bi = qg::bits_index(d->bits);
   if (bi < 0) return QGEMV_E_BITS;
   const int gi = qg::group_index(d->group);
@@ -395,6 +413,7 @@ int qgemv_create_arith(const qgemv_desc* d, int32_t arith, qgemv_t* out) {
   h.wpr = d->k * d->bits / 32;
   h.gpr = d->k / d->group;
   h.entry = &qg::entry(bi, gi);
+  h.wide = &qg::wide_entry(bi, gi);
   // Fast geometry when a row is a whole number of chunks and at least 16
   // lanes share a column; otherwise one 32-code unit per lane step.
   int ppc = 0, cpc = 0;
@@ -418,15 +437,16 @@ int qgemv_create_arith(const qgemv_desc* d, int32_t arith, qgemv_t* out) {
   const uintptr_t sb = reinterpret_cast<uintptr_t>(d->scales) | reinterpret_cast<uintptr_t>(d->biases);
   const bool mfma_ok = d->k % qgemv_mfma_codes(d->bits, d->group) == 0 &&
                        sb % static_cast<uintptr_t>(h.entry->mfma_salign) == 0;
-  if (arith == QGEMV_ARITH_MFMA && !mfma_ok) return QGEMV_E_NOKERNEL;
-  h.arith = (arith == QGEMV_ARITH_MFMA || (arith == QGEMV_ARITH_AUTO && mfma_ok)) ? QGEMV_ARITH_MFMA
-                                                                               : QGEMV_ARITH_DOT;
+  if ((arith == QGEMV_ARITH_MFMA || arith == QGEMV_ARITH_WIDE) && !mfma_ok) return QGEMV_E_NOKERNEL;
+  h.arith = arith == QGEMV_ARITH_WIDE ? QGEMV_ARITH_WIDE
+            : (arith == QGEMV_ARITH_MFMA || (arith == QGEMV_ARITH_AUTO && mfma_ok)) ? QGEMV_ARITH_MFMA
+                                                                                  : QGEMV_ARITH_DOT;
   // matrix-core K split, from one expert's shape only (an indexed call must
   // give each expert the bits of that expert's own single-expert handle):
   // small matrices split K in 2 or 4 parts so that enough waves stream at
   // once (about 2048, two per SIMD), when the row's load groups divide evenly
   h.ksplit = 1;
-  if (h.arith == QGEMV_ARITH_MFMA) {
+  if (matrix_cores(&h)) {
     const int64_t groups = d->k / (128 * static_cast<int64_t>(h.entry->mfma_group));
     const int64_t col_tiles = (d->n + 15) / 16;
     while (h.ksplit < 4 && col_tiles * h.ksplit < 2048 && groups % (2 * h.ksplit) == 0) h.ksplit *= 2;
@@ -434,7 +454,7 @@ int qgemv_create_arith(const qgemv_desc* d, int32_t arith, qgemv_t* out) {
   {
     // groups one packed scale load spans: a lane chunk's, or a 128-code
     // macro step's for the matrix-core form
-    const int span_codes = h.arith == QGEMV_ARITH_MFMA ? 128 : h.cpc;
+    const int span_codes = matrix_cores(&h) ? 128 : h.cpc;
     const int gspan = span_codes >= d->group ? span_codes / d->group : 1;
     const uintptr_t a = reinterpret_cast<uintptr_t>(d->scales) | reinterpret_cast<uintptr_t>(d->biases);
     h.vec_groups = (a % (2 * gspan) == 0) && (h.gpr % gspan == 0);
@@ -442,10 +462,10 @@ int qgemv_create_arith(const qgemv_desc* d, int32_t arith, qgemv_t* out) {
   // The one-row window must fit in LDS; wider windows are refused at run
   // time when theirs does not (QGEMV_E_WINDOW), or, in the matrix-core
   // form, run as passes of fewer rows.
-  if (h.arith == QGEMV_ARITH_MFMA) {
+  if (matrix_cores(&h)) {
     size_t lds = 0;
     if (!mfma_plan(&h, 0, false, &lds)) {
-      if (arith == QGEMV_ARITH_MFMA) return QGEMV_E_NOKERNEL;
+      if (arith == QGEMV_ARITH_MFMA || arith == QGEMV_ARITH_WIDE) return QGEMV_E_NOKERNEL;
       h.arith = QGEMV_ARITH_DOT;
       h.ksplit = 1;
     }
@@ -473,7 +493,7 @@ static int check_run_common(qgemv_t h, const uint16_t* x, int32_t m, const float
 int qgemv_run_strided(qgemv_t h, const uint16_t* x, int32_t m, float* y, int64_t ldy, int32_t epi,
                       void* stream) {
   int rc = check_run_common(h, x, m, y, epi,
-                            h && h->arith == QGEMV_ARITH_MFMA ? QGEMV_MAX_PROMPT : QGEMV_MAX_WINDOW);
+                            h && matrix_cores(h) ? QGEMV_MAX_PROMPT : QGEMV_MAX_WINDOW);
   if (rc != QGEMV_OK) return rc;
   if (h->d.n_experts != 1) return QGEMV_E_ARG;
   if (ldy < h->d.n) return QGEMV_E_STRIDE;
@@ -509,7 +529,7 @@ int qgemv_run_indexed(qgemv_t h, const uint16_t* x, int32_t m, const int32_t* id
 
 static int check_gateup_pair(qgemv_t gate, qgemv_t up) {
   if (!gate || !up) return QGEMV_E_ARG;
-  if (gate->arith != QGEMV_ARITH_MFMA || up->arith != QGEMV_ARITH_MFMA) return QGEMV_E_NOKERNEL;
+  if (!matrix_cores(gate) || up->arith != gate->arith) return QGEMV_E_NOKERNEL;
   if (gate->d.bits != up->d.bits || gate->d.group != up->d.group || gate->d.n != up->d.n ||
       gate->d.k != up->d.k || gate->d.n_experts != up->d.n_experts || gate->ksplit != up->ksplit)
     return QGEMV_E_SHAPE;
@@ -834,7 +854,7 @@ int qgemv_stack_run(qgemv_stack_t s, const uint16_t* x, int32_t m, float* y, int
 
 int qgemv_query(qgemv_t h, int64_t out[6]) {
   if (!h || !out) return QGEMV_E_ARG;
-  if (h->arith == QGEMV_ARITH_MFMA) {
+  if (matrix_cores(h)) {
     // four lanes per column (one 32-code unit each), 16 columns per wave
     out[0] = 4;
     out[1] = 16;

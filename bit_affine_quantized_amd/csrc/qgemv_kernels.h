@@ -1008,13 +1008,48 @@ template <int MB> struct MWaves {
   static constexpr int v = MB >= 8 ? 8 : 4;
 };
 
-template <int B, int G, int MB>
+// 4 x 4 transpose of 4-dword items across the four 16-lane rows of a wave.
+// On entry the lanes of row q hold items X_q[0..3] in q[4t..4t+3]; on exit
+// they hold X_0[q], X_1[q], X_2[q], X_3[q].  First the rows two apart swap
+// (permlane32: the upper 32 lanes of the first operand with the lower 32 of
+// the second), then adjacent rows (permlane16: the odd rows of the first
+// operand with the even rows of the second).
+__device__ __forceinline__ void transpose_rows(uint32_t* q) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const auto a = __builtin_amdgcn_permlane32_swap(q[d], q[8 + d], false, false);
+    q[d] = a[0];
+    q[8 + d] = a[1];
+    const auto b = __builtin_amdgcn_permlane32_swap(q[4 + d], q[12 + d], false, false);
+    q[4 + d] = b[0];
+    q[12 + d] = b[1];
+  }
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const auto a = __builtin_amdgcn_permlane16_swap(q[d], q[4 + d], false, false);
+    q[d] = a[0];
+    q[4 + d] = a[1];
+    const auto b = __builtin_amdgcn_permlane16_swap(q[8 + d], q[12 + d], false, false);
+    q[8 + d] = b[0];
+    q[12 + d] = b[1];
+  }
+}
+
+// WIDE selects the wide-window form: after the unpack, the four lanes of a
+// column trade quarters of their units (transpose_rows), so that lane (j, q)
+// holds k-quarter q of all four units of the round; each unit is then one
+// 16x16x32 product over every window row at once (A row i = window row i),
+// and lane (j, q) folds window rows 4q .. 4q+3 of column j.
+template <int B, int G, int MB, bool WIDE = false>
 __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const int gx, unsigned char* smem,
                                           int* s_wave_cnt, int* s_xrow, int64_t* s_yoff) {
   using MG = MGroup<B, G>;
   constexpr int R = MG::R, CH = MG::CH, SSZ = MG::SSZ;
   constexpr int NW = MWaves<MB>::v, NT = NW * kWave;
   constexpr int NMB = (MB + 3) / 4;         // 4-row blocks of the window
+  // outputs each lane folds: one per 4-row block, or (wide form) window rows
+  // 4q .. 4q+3 of its column, as many as the window can hold
+  constexpr int NACC = WIDE ? (MB < 4 ? MB : 4) : NMB;
   constexpr int ZB = R * 256;               // zero area: one group's activations
 
   const int units = static_cast<int>(p.k / 32);
@@ -1171,25 +1206,38 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
     }
   };
 
-  float acc[NMB];
+  float acc[NACC];
 #pragma unroll
-  for (int mb = 0; mb < NMB; ++mb) acc[mb] = 0.0f;
+  for (int mb = 0; mb < NACC; ++mb) acc[mb] = 0.0f;
   int mcount = 0;
 
-  // per-lane LDS offsets (from smem) of the A operand and unit sums of each
-  // 4-row block, set for each pass of window rows and advanced per group
-  int a_base[NMB], x_base[NMB], a_live[NMB];
+  // per-lane LDS offsets (from smem) of the A operand and of the unit sums
+  // this lane folds, set for each pass of window rows and advanced per group
+  int a_base[NMB], a_live[NMB], x_base[NACC];
   auto set_bases = [&]() {
+    if constexpr (WIDE) {
+      // A operand of lane (row ai, k-quarter qd): quarter qd of each unit of
+      // window row ai (rows past the window read row 0 and are never stored)
+      const int ai = lane % 16;
+      a_base[0] = (ai < mcount ? ai : 0) * xstride + qd * 16;
+      a_live[0] = 1;
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) {
-      const int ai = lane % 16, am = 4 * mb + ai / 4;
-      // lane (row ai, k-quarter qd) is live when its quarter is its row's
-      // unit and the window row exists
-      const bool live = (qd == ai % 4) && (am < mcount);
-      a_live[mb] = live ? 1 : 0;
-      a_base[mb] = live ? am * xstride + qd * 64 : mrows * xstride;
-      const int em = 4 * mb + qd;
-      x_base[mb] = mrows * xstride + ZB + (em < mcount ? em : 0) * sstride * 4;
+      for (int i = 0; i < NACC; ++i) {
+        const int em = 4 * qd + i;
+        x_base[i] = mrows * xstride + ZB + (em < mcount ? em : 0) * sstride * 4;
+      }
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+        const int ai = lane % 16, am = 4 * mb + ai / 4;
+        // lane (row ai, k-quarter qd) is live when its quarter is its row's
+        // unit and the window row exists
+        const bool live = (qd == ai % 4) && (am < mcount);
+        a_live[mb] = live ? 1 : 0;
+        a_base[mb] = live ? am * xstride + qd * 64 : mrows * xstride;
+        const int em = 4 * mb + qd;
+        x_base[mb] = mrows * xstride + ZB + (em < mcount ? em : 0) * sstride * 4;
+      }
     }
   };
 
@@ -1210,12 +1258,11 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
         *reinterpret_cast<uint32_t*>(slot + MG::WBYTES + 16 * MG::SSTR + s_woff) = sg.b[0];
       }
     }
-    int a_grp[NMB], x_grp[NMB];
+    int a_grp[NMB], x_grp[NACC];
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) {
-      a_grp[mb] = a_base[mb] + a_live[mb] * (c.gr * R * 256);
-      x_grp[mb] = x_base[mb] + c.gr * R * 16;
-    }
+    for (int mb = 0; mb < NMB; ++mb) a_grp[mb] = a_base[mb] + a_live[mb] * (c.gr * R * 256);
+#pragma unroll
+    for (int mb = 0; mb < NACC; ++mb) x_grp[mb] = x_base[mb] + c.gr * R * 16;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       uint32_t wu[B];
@@ -1268,6 +1315,42 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
           bv[q2] = b1;
         }
       }
+      if constexpr (WIDE) {
+        // A operand: quarter qd of the round's four units of row lane % 16;
+        // the unit sums of the rows this lane folds
+        u32x4 aw[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) aw[u] = *reinterpret_cast<const u32x4*>(smem + a_grp[0] + r * 256 + u * 64);
+        f32x4_t xw[NACC];
+#pragma unroll
+        for (int i = 0; i < NACC; ++i) xw[i] = *reinterpret_cast<const f32x4_t*>(smem + x_grp[i] + r * 16);
+        // B operand: this lane's unit as 16 exact bf16 pairs, then quarter
+        // qd of each of the four units
+        uint32_t qp[16];
+        unpack_codes<B, 32>(wu, qp);
+        transpose_rows(qp);
+        f32x4_t d[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          u32x4 bq;
+          bq.x = qp[4 * u];
+          bq.y = qp[4 * u + 1];
+          bq.z = qp[4 * u + 2];
+          bq.w = qp[4 * u + 3];
+          d[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, aw[u]),
+                                                         __builtin_bit_cast(bf16x8_t, bq),
+                                                         f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+        }
+        // lane = (column j, window rows 4qd + i): units 0..3 in order
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int i = 0; i < NACC; ++i) {
+            acc[i] = __builtin_fmaf(sv[u], d[u][i], acc[i]);
+            acc[i] = __builtin_fmaf(bv[u], xw[i][u], acc[i]);
+          }
+        continue;
+      }
       // A operand and unit sums of every 4-row block (rows past the window
       // read zeros and are never stored)
       u32x4 av[NMB][4];
@@ -1308,22 +1391,22 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
     }
     if (c.gr == gr0 + gpp - 1) {
       const int col = ((bx + c.i * gx) * ncg + cg) * cw + j;
-      float out[NMB];
+      float out[NACC];
       bool store = true;
       if (S == 1) {
 #pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) out[mb] = acc[mb];
+        for (int mb = 0; mb < NACC; ++mb) out[mb] = acc[mb];
       } else {
         // the column group's parts meet in LDS and are added in part order
 #pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) partial[(wv * NMB + mb) * kWave + lane] = acc[mb];
+        for (int mb = 0; mb < NACC; ++mb) partial[(wv * NACC + mb) * kWave + lane] = acc[mb];
         __syncthreads();
         store = ks == 0;
         if (store) {
 #pragma unroll
-          for (int mb = 0; mb < NMB; ++mb) {
-            float v = partial[((cg * S) * NMB + mb) * kWave + lane];
-            for (int q = 1; q < S; ++q) v += partial[((cg * S + q) * NMB + mb) * kWave + lane];
+          for (int mb = 0; mb < NACC; ++mb) {
+            float v = partial[((cg * S) * NACC + mb) * kWave + lane];
+            for (int q = 1; q < S; ++q) v += partial[((cg * S + q) * NACC + mb) * kWave + lane];
             out[mb] = v;
           }
         }
@@ -1332,15 +1415,15 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
       if (gu) {
         // lane j + 8 (up) hands its value to lane j (gate) in each 16-lane row
 #pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) {
+        for (int mb = 0; mb < NACC; ++mb) {
           const float u = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(out[mb]), 0x128, 0xf, 0xf, false));
           out[mb] = silu_f32(out[mb]) * u;
         }
       }
       if (store) {
 #pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) {
-          const int em = 4 * mb + qd;
+        for (int mb = 0; mb < NACC; ++mb) {
+          const int em = WIDE ? 4 * qd + mb : 4 * mb + qd;
           const bool ok = em < mcount && col < n && j < cw;
           const int off = ok ? static_cast<int>((s_yoff[ok ? em : 0] + mapped_column(p, col)) * 4) : 0x7ffffff0;
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(gu ? out[mb] : apply_epi(out[mb], p.epi)), yres,
@@ -1348,7 +1431,7 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
         }
       }
 #pragma unroll
-      for (int mb = 0; mb < NMB; ++mb) acc[mb] = 0.0f;
+      for (int mb = 0; mb < NACC; ++mb) acc[mb] = 0.0f;
     }
   };
 
@@ -1431,6 +1514,15 @@ __global__ __launch_bounds__(MWaves<MB>::v * kWave) void qrow_mfma(const Params 
   __shared__ int s_xrow[QGEMV_MAX_WINDOW];
   __shared__ int64_t s_yoff[QGEMV_MAX_WINDOW];
   mfma_body<B, G, MB>(p, blockIdx.x, gridDim.x, smem, s_wave_cnt, s_xrow, s_yoff);
+}
+
+template <int B, int G, int MB>
+__global__ __launch_bounds__(MWaves<MB>::v * kWave) void qrow_mfma_wide(const Params p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int s_wave_cnt[MWaves<MB>::v];
+  __shared__ int s_xrow[QGEMV_MAX_WINDOW];
+  __shared__ int64_t s_yoff[QGEMV_MAX_WINDOW];
+  mfma_body<B, G, MB, true>(p, blockIdx.x, gridDim.x, smem, s_wave_cnt, s_xrow, s_yoff);
 }
 
 // ---------------------------------------------------------------------------
@@ -1645,6 +1737,22 @@ Entry make_entry() {
   return e;
 }
 
+// The wide-window matrix-core kernels of one (bits, group) by window variant.
+struct WideEntry {
+  KernelFn k[5];
+};
+
+template <int B, int G>
+WideEntry make_wide_entry() {
+  WideEntry e{};
+  e.k[0] = qrow_mfma_wide<B, G, 1>;
+  e.k[1] = qrow_mfma_wide<B, G, 2>;
+  e.k[2] = qrow_mfma_wide<B, G, 4>;
+  e.k[3] = qrow_mfma_wide<B, G, 8>;
+  e.k[4] = qrow_mfma_wide<B, G, 16>;
+  return e;
+}
+
 // One table of kernels per code width, each built in its own translation
 // unit: index [group 32/64/128].
 const Entry* entries_b2();
@@ -1653,6 +1761,12 @@ const Entry* entries_b4();
 const Entry* entries_b5();
 const Entry* entries_b6();
 const Entry* entries_b8();
+const WideEntry* wide_entries_b2();
+const WideEntry* wide_entries_b3();
+const WideEntry* wide_entries_b4();
+const WideEntry* wide_entries_b5();
+const WideEntry* wide_entries_b6();
+const WideEntry* wide_entries_b8();
 
 // Fused-stack kernels (both arithmetic forms) by window variant (1, 2, 4,
 // 8, 16 rows), one translation unit each.

@@ -1,0 +1,11 @@
+// Wide-window matrix-core kernels of the 3-bit code width, groups of 32, 64 and 128.
+#include "qgemv_kernels.h"
+
+namespace qg {
+
+const WideEntry* wide_entries_b3() {
+  static const WideEntry table[3] = {make_wide_entry<3, 32>(), make_wide_entry<3, 64>(), make_wide_entry<3, 128>()};
+  return table;
+}
+
+}  // namespace qg

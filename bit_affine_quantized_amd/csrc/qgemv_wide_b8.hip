@@ -1,0 +1,11 @@
+// Wide-window matrix-core kernels of the 8-bit code width, groups of 32, 64 and 128.
+#include "qgemv_kernels.h"
+
+namespace qg {
+
+const WideEntry* wide_entries_b8() {
+  static const WideEntry table[3] = {make_wide_entry<8, 32>(), make_wide_entry<8, 64>(), make_wide_entry<8, 128>()};
+  return table;
+}
+
+}  // namespace qg

@@ -19,7 +19,7 @@ QGEMV_OK = 0
 QGEMV_E_ARG, QGEMV_E_BITS, QGEMV_E_GROUP, QGEMV_E_SHAPE, QGEMV_E_STRIDE = -1, -2, -3, -4, -5
 QGEMV_E_ALIGN, QGEMV_E_WINDOW, QGEMV_E_ALIAS, QGEMV_E_NOKERNEL, QGEMV_E_HIP = -6, -7, -8, -9, -10
 QGEMV_EPI_NONE, QGEMV_EPI_RELU2 = 0, 1
-QGEMV_ARITH_AUTO, QGEMV_ARITH_DOT, QGEMV_ARITH_MFMA = 0, 1, 2
+QGEMV_ARITH_AUTO, QGEMV_ARITH_DOT, QGEMV_ARITH_MFMA, QGEMV_ARITH_WIDE = 0, 1, 2, 3
 QGEMV_MAX_WINDOW = 16
 QGEMV_MAX_PROMPT = 65
 

@@ -120,18 +120,30 @@ int qgemv_create(const qgemv_desc* d, qgemv_t* out);
  *                     added in order.  Needs k a multiple of
  *                     qgemv_mfma_codes(bits, group) and aligned scales
  *                     and biases (QGEMV_E_NOKERNEL otherwise).
+ *   QGEMV_ARITH_WIDE  matrix cores for wide windows: the same loads, K
+ *                     split and shape rules as QGEMV_ARITH_MFMA, but after
+ *                     the unpack the four lanes of a column trade quarters
+ *                     of their units, so each unit is one 16x16x32 product
+ *                     over all window rows at once (4 products per 128-code
+ *                     round, against 4 per 4 window rows in the MFMA form).
+ *                     Each lane folds the units of its column for window
+ *                     rows 4q..4q+3.  The trade costs 16 lane swaps per
+ *                     round: on MI355X it is faster at 16-row windows and
+ *                     prompt passes, slower at 1-8 rows; never chosen by
+ *                     AUTO.
  *   QGEMV_ARITH_AUTO  the library's choice (what qgemv_create uses): the
  *                     MFMA form when the shape and alignment allow it,
  *                     else the dot form.                                  */
 #define QGEMV_ARITH_AUTO 0
 #define QGEMV_ARITH_DOT 1
 #define QGEMV_ARITH_MFMA 2
+#define QGEMV_ARITH_WIDE 3
 
 /* As qgemv_create, with the arithmetic chosen by the caller. */
 int qgemv_create_arith(const qgemv_desc* d, int32_t arith, qgemv_t* out);
 
-/* The arithmetic a handle was created with (QGEMV_ARITH_DOT or _MFMA), or
- * QGEMV_E_ARG for a NULL handle. */
+/* The arithmetic a handle was created with (QGEMV_ARITH_DOT, _MFMA or
+ * _WIDE), or QGEMV_E_ARG for a NULL handle. */
 int qgemv_arith(qgemv_t h);
 
 /* The multiple of k that the MFMA form needs, its load group of 128-code
@@ -147,12 +159,13 @@ void qgemv_destroy(qgemv_t h);
 
 /* y[i][j] for i < m, j < n, contiguous (row stride n).
  *   x  bf16 bits [m][k] device, 16-byte aligned.
- *   m  window rows: 0..16 (decode windows), and on a QGEMV_ARITH_MFMA
- *      handle up to QGEMV_MAX_PROMPT = 65 (prompt windows: P788 keeps a
- *      row's bits in every window of 1-65 rows in prompt).  m == 0 launches
+ *   m  window rows: 0..16 (decode windows), and on a matrix-core
+ *      (QGEMV_ARITH_MFMA or _WIDE) handle up to QGEMV_MAX_PROMPT = 65
+ *      (prompt windows: P788 keeps a row's bits in every window of 1-65
+ *      rows in prompt).  m == 0 launches
  *      nothing and returns QGEMV_OK.  QGEMV_ARITH_DOT: a window whose staged
  *      activations exceed the LDS of one block (m*k*2.125 bytes > 152 KiB)
- *      is refused with QGEMV_E_WINDOW.  QGEMV_ARITH_MFMA: a window above 16
+ *      is refused with QGEMV_E_WINDOW.  Matrix-core forms: a window above 16
  *      rows, or one too wide for the LDS, runs as passes of fewer rows (the
  *      weights are read once per pass); each row's bits are those of the
  *      row alone.
@@ -190,8 +203,9 @@ int qgemv_run_indexed(qgemv_t h, const uint16_t* x, int32_t m, const int32_t* id
  *                            u = row j of `up`   times x[i],
  *   silu(g) = g / (1 + exp(-g)) in fp32 (the device library's expf).
  * g and u have exactly the bits qgemv_run gives each handle; one dispatch
- * reads both matrices.  gate and up: QGEMV_ARITH_MFMA handles of equal bits,
- * group, n, k and n_experts (QGEMV_E_NOKERNEL for another form,
+ * reads both matrices.  gate and up: matrix-core handles of one form
+ * (QGEMV_ARITH_MFMA or _WIDE) and of equal bits, group, n, k and
+ * n_experts (QGEMV_E_NOKERNEL for another form,
  * QGEMV_E_SHAPE for unequal shapes).  Windows, strides, alignment, aliasing
  * and refusals as qgemv_run_strided (m up to QGEMV_MAX_PROMPT) and
  * qgemv_run_indexed (the same expert of both stacks for each slot). */

@@ -177,13 +177,13 @@ def test_arith_choice_fixed_at_create():
     for bits in (2, 3, 4, 5, 6, 8):
         for group in (32, 64, 128):
             k = 4 * qgemv.qgemv_mfma_codes(bits, group)
-            for arith in (qgemv.QGEMV_ARITH_DOT, qgemv.QGEMV_ARITH_MFMA):
+            for arith in (qgemv.QGEMV_ARITH_DOT, qgemv.QGEMV_ARITH_MFMA, qgemv.QGEMV_ARITH_WIDE):
                 rc, h = qgemv.qgemv_create_arith(bits, group, 48, k, W, S, B, arith)
                 assert rc == 0, (bits, group, arith, qgemv.qgemv_strerror(rc))
                 assert qgemv.qgemv_arith(h) == arith
                 rc, geo = qgemv.qgemv_query(h)
                 assert rc == 0
-                if arith == qgemv.QGEMV_ARITH_MFMA:
+                if arith != qgemv.QGEMV_ARITH_DOT:
                     assert geo[:5] == [4, 16, 32, 256, 64]
                 qgemv.qgemv_destroy(h)
             rc, h = qgemv.qgemv_create(bits, group, 48, k, W, S, B)
@@ -192,38 +192,44 @@ def test_arith_choice_fixed_at_create():
     # refused for that form only: k not a multiple of the step, scales
     # only 2-byte aligned
     for k, s in ((4096 + 512, S), (4096, S + 4)):
-        rc, h = qgemv.qgemv_create_arith(3, 128, 48, k, W, s, B, qgemv.QGEMV_ARITH_MFMA)
-        assert rc == qgemv.QGEMV_E_NOKERNEL and h is None
+        for arith in (qgemv.QGEMV_ARITH_MFMA, qgemv.QGEMV_ARITH_WIDE):
+            rc, h = qgemv.qgemv_create_arith(3, 128, 48, k, W, s, B, arith)
+            assert rc == qgemv.QGEMV_E_NOKERNEL and h is None
         rc, h = qgemv.qgemv_create_arith(3, 128, 48, k, W, s, B, qgemv.QGEMV_ARITH_AUTO)
         assert rc == 0 and qgemv.qgemv_arith(h) == qgemv.QGEMV_ARITH_DOT
         qgemv.qgemv_destroy(h)
-    assert qgemv.qgemv_create_arith(4, 64, 48, 2048, W, S, B, 3)[0] == qgemv.QGEMV_E_ARG
+    assert qgemv.qgemv_create_arith(4, 64, 48, 2048, W, S, B, 4)[0] == qgemv.QGEMV_E_ARG
+    assert qgemv.qgemv_create_arith(4, 64, 48, 2048, W, S, B, -1)[0] == qgemv.QGEMV_E_ARG
     assert qgemv.qgemv_arith(None) == qgemv.QGEMV_E_ARG
 
 
 def test_window_limits_by_form():
     """Decode windows of 1-16 rows for every handle; prompt windows up to 65
-    rows for plain and strided calls in the MFMA form only."""
+    rows for plain and strided calls in the matrix-core forms only."""
     assert qgemv.QGEMV_MAX_WINDOW == 16 and qgemv.QGEMV_MAX_PROMPT == 65
     rc, hd = qgemv.qgemv_create_arith(4, 64, 256, 2048, W, S, B, qgemv.QGEMV_ARITH_DOT)
-    rc2, hm = qgemv.qgemv_create_arith(4, 64, 256, 2048, W, S, B, qgemv.QGEMV_ARITH_MFMA)
-    rc3, he = qgemv.qgemv_create_arith(4, 64, 256, 2048, W, S, B, qgemv.QGEMV_ARITH_MFMA, n_experts=4)
-    assert rc == rc2 == rc3 == 0
+    assert rc == 0
     assert qgemv.qgemv_run(hd, X, 17, Y, 0, 0) == qgemv.QGEMV_E_WINDOW
     assert qgemv.qgemv_run_strided(hd, X, 17, Y, 512, 0, 0) == qgemv.QGEMV_E_WINDOW
-    assert qgemv.qgemv_run(hm, X, 66, Y, 0, 0) == qgemv.QGEMV_E_WINDOW
-    assert qgemv.qgemv_run_strided(hm, X, 66, Y, 512, 0, 0) == qgemv.QGEMV_E_WINDOW
-    assert qgemv.qgemv_run_indexed(he, X, 17, IDX, 8, Y, 0, 0) == qgemv.QGEMV_E_WINDOW
-    for h in (hd, hm, he):
-        qgemv.qgemv_destroy(h)
+    qgemv.qgemv_destroy(hd)
+    for arith in (qgemv.QGEMV_ARITH_MFMA, qgemv.QGEMV_ARITH_WIDE):
+        rc2, hm = qgemv.qgemv_create_arith(4, 64, 256, 2048, W, S, B, arith)
+        rc3, he = qgemv.qgemv_create_arith(4, 64, 256, 2048, W, S, B, arith, n_experts=4)
+        assert rc2 == rc3 == 0
+        assert qgemv.qgemv_run(hm, X, 66, Y, 0, 0) == qgemv.QGEMV_E_WINDOW
+        assert qgemv.qgemv_run_strided(hm, X, 66, Y, 512, 0, 0) == qgemv.QGEMV_E_WINDOW
+        assert qgemv.qgemv_run_indexed(he, X, 17, IDX, 8, Y, 0, 0) == qgemv.QGEMV_E_WINDOW
+        for h in (hm, he):
+            qgemv.qgemv_destroy(h)
 
 
 def test_gateup_refusals():
-    """Gate/up pairs: both handles in the MFMA form with equal shapes."""
-    mf, dt = qgemv.QGEMV_ARITH_MFMA, qgemv.QGEMV_ARITH_DOT
+    """Gate/up pairs: both handles in one matrix-core form, with equal shapes."""
+    mf, dt, wd = qgemv.QGEMV_ARITH_MFMA, qgemv.QGEMV_ARITH_DOT, qgemv.QGEMV_ARITH_WIDE
     hs = {}
     for name, n, arith, e in (("g", 256, mf, 1), ("u", 256, mf, 1), ("u255", 255, mf, 1),
-                              ("gd", 256, dt, 1), ("ud", 256, dt, 1), ("ge", 256, mf, 4), ("ue", 256, mf, 4)):
+                              ("gd", 256, dt, 1), ("ud", 256, dt, 1), ("ge", 256, mf, 4), ("ue", 256, mf, 4),
+                              ("gw", 256, wd, 1), ("uw", 256, wd, 1)):
         rc, hs[name] = qgemv.qgemv_create_arith(6, 32, n, 2048, W, S, B, arith, n_experts=e)
         assert rc == 0
     def gu(*args):
@@ -235,6 +241,9 @@ def test_gateup_refusals():
     assert gu(None, hs["u"], X, 1, Y, 256) == qgemv.QGEMV_E_ARG
     assert gu(hs["gd"], hs["ud"], X, 1, Y, 256) == qgemv.QGEMV_E_NOKERNEL
     assert gu(hs["g"], hs["ud"], X, 1, Y, 256) == qgemv.QGEMV_E_NOKERNEL
+    assert gu(hs["g"], hs["uw"], X, 1, Y, 256) == qgemv.QGEMV_E_NOKERNEL      # two matrix-core forms
+    assert gu(hs["gw"], hs["u"], X, 1, Y, 256) == qgemv.QGEMV_E_NOKERNEL
+    assert gu(hs["gw"], hs["uw"], X, 66, Y, 256) == qgemv.QGEMV_E_WINDOW
     assert gu(hs["g"], hs["u255"], X, 1, Y, 256) == qgemv.QGEMV_E_SHAPE
     assert gu(hs["g"], hs["ue"], X, 1, Y, 256) == qgemv.QGEMV_E_SHAPE
     assert gu(hs["g"], hs["u"], X, 66, Y, 256) == qgemv.QGEMV_E_WINDOW

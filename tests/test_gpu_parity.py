@@ -38,9 +38,12 @@ def dev(a: np.ndarray):
 
 
 # both arithmetic forms of a handle, each held to the same bars
-ARITHS = [qgemv.QGEMV_ARITH_DOT, qgemv.QGEMV_ARITH_MFMA]
-ARITH_IDS = ["dot", "mfma"]
+ARITHS = [qgemv.QGEMV_ARITH_DOT, qgemv.QGEMV_ARITH_MFMA, qgemv.QGEMV_ARITH_WIDE]
+ARITH_IDS = ["dot", "mfma", "wide"]
 arith_param = pytest.mark.parametrize("arith", ARITHS, ids=ARITH_IDS)
+# the two matrix-core forms (prompt windows, gate/up pairs)
+MC = [qgemv.QGEMV_ARITH_MFMA, qgemv.QGEMV_ARITH_WIDE]
+mc_param = pytest.mark.parametrize("arith", MC, ids=["mfma", "wide"])
 
 
 def matrix_of(d, expert=None, arith=qgemv.QGEMV_ARITH_AUTO):
@@ -149,17 +152,19 @@ def test_window_invariance(bits, group, arith):
             assert bits_equal(y, alone[s0:s0 + m]), f"window {m} at {s0}"
 
 
+@mc_param
 @pytest.mark.parametrize("bits,group", [(6, 32), (4, 64), (3, 128), (8, 32), (2, 64), (5, 64)])
-def test_prompt_windows(bits, group):
-    """MFMA form: windows of 17-65 rows (passes of 16) give every row the bits
-    it has alone, and stay within the bound; the dot form refuses them."""
-    print_case("prompt", bits, group)
+def test_prompt_windows(bits, group, arith):
+    """Matrix-core forms: windows of 17-65 rows (passes of 16) give every row
+    the bits it has alone, and stay within the bound; the dot form refuses
+    them."""
+    print_case("prompt", bits, group, arith)
     n, k = 1000, 2048
     d = synth.matrix(7000 + bits * 10 + group, bits, group, n, k)
     rng = np.random.default_rng(7100 + bits * 10 + group)
     pool_np = synth.draw_x(rng, 80, k)
     pool = dev(pool_np)
-    mat = matrix_of(d, arith=qgemv.QGEMV_ARITH_MFMA)
+    mat = matrix_of(d, arith=arith)
     alone = torch.empty((80, n), dtype=torch.float32, device=DEV)
     for r in range(80):
         mat.run(pool[r:r + 1], alone[r:r + 1], m=1)
@@ -187,16 +192,17 @@ def _gateup_pair(bits, group, n, k, m, seed, n_experts=1):
     return dg, du
 
 
+@mc_param
 @pytest.mark.parametrize("bits,group,n,k", GATEUP)
-def test_gateup_pair(bits, group, n, k):
+def test_gateup_pair(bits, group, n, k, arith):
     """y = silu(g) * u in one dispatch over the gate and up matrices: within
     a few fp32 roundings of fp64 silu over the plain calls' own g and u, within
     the bound against the oracle, and each row's bits the same in every
     window and position."""
-    print_case("gateup", bits, group, n, k)
+    print_case("gateup", bits, group, n, k, arith)
     dg, du = _gateup_pair(bits, group, n, k, 16, 7500 + bits * 10 + group)
-    gate = matrix_of(dg, arith=qgemv.QGEMV_ARITH_MFMA)
-    up = matrix_of(du, arith=qgemv.QGEMV_ARITH_MFMA)
+    gate = matrix_of(dg, arith=arith)
+    up = matrix_of(du, arith=arith)
     xt = dev(dg["x"])
     rows = {}
     for m in (1, 5, 16):
@@ -233,7 +239,8 @@ def test_gateup_pair(bits, group, n, k):
     assert torch.equal(ys.view(torch.int32)[gap], sentinel[gap])
 
 
-def test_gateup_indexed_and_refusals():
+@mc_param
+def test_gateup_indexed_and_refusals(arith):
     """Indexed gate/up: each (row, slot) equals the pair call on that expert's
     own gate and up handles; unequal shapes and the dot form are refused."""
     bits, group, n, k, e = 3, 64, 300, 1024, 6
@@ -242,7 +249,7 @@ def test_gateup_indexed_and_refusals():
                     [1, 5, 1], [0, 0, 0], [2, 1, 4], [3, 3, 1]], dtype=np.int32)
     tg = [dev(dg[key]) for key in ("words", "scales", "biases")]
     tu = [dev(du[key]) for key in ("words", "scales", "biases")]
-    mf = qgemv.QGEMV_ARITH_MFMA
+    mf = arith
     gate = qgemv.Matrix(bits, group, n, k, *tg, n_experts=e, arith=mf)
     up = qgemv.Matrix(bits, group, n, k, *tu, n_experts=e, arith=mf)
     xt = dev(dg["x"])
@@ -450,7 +457,7 @@ EDGE = [(6, 64, 48, 2048), (5, 128, 6192, 2048), (4, 32, 1, 2048), (3, 32, 33, 3
 def test_edge_shapes(bits, group, n, k, arith):
     print_case("edge", bits, group, n, k, arith)
     d = synth.matrix(8000 + n + k, bits, group, n, k, 3)
-    if arith == qgemv.QGEMV_ARITH_MFMA and k % qgemv.qgemv_mfma_codes(bits, group):
+    if arith in MC and k % qgemv.qgemv_mfma_codes(bits, group):
         with pytest.raises(qgemv.QgemvError, match="QGEMV_E_NOKERNEL"):
             matrix_of(d, arith=arith)
         return
