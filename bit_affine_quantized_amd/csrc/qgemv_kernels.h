@@ -1206,37 +1206,40 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
     }
   };
 
-  float acc[NACC];
-#pragma unroll
-  for (int mb = 0; mb < NACC; ++mb) acc[mb] = 0.0f;
+  // this lane's outputs: element i is window row 4i + qd (4-row blocks) or
+  // 4qd + i (wide form) of column j; elements past NACC are never stored
+  f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
   int mcount = 0;
 
-  // per-lane LDS offsets (from smem) of the A operand and of the unit sums
-  // this lane folds, set for each pass of window rows and advanced per group
-  int a_base[NMB], a_live[NMB], x_base[NACC];
+  // Bias terms: a round's sum over its four units of bias(u) * X(row, u)
+  // is one fp32 16x16x4 product, X [16 rows][4 units] times bias [4 units]
+  // [16 columns], accumulated straight into acc.  Its A row rho carries the
+  // window row that lands in the element of acc that folds that row: rho
+  // itself in the wide form, 4 (rho % 4) + rho / 4 for 4-row blocks.
+  const int ai = lane % 16;
+  const int xrow = WIDE ? ai : 4 * (ai % 4) + ai / 4;
+  // bias of unit 4r + qd of column j, from the slot's bias bytes
+  const int b_lane = (G == 32) ? qd * 2 : ((G == 64) ? (qd / 2) * 2 : 0);
+
+  // per-lane LDS offsets (from smem) of the A operands, set for each pass of
+  // window rows and advanced per group
+  int a_base[NMB], a_live[NMB], xa_base = 0;
   auto set_bases = [&]() {
+    xa_base = mrows * xstride + ZB + ((xrow < mcount ? xrow : 0) * sstride + qd) * 4;
     if constexpr (WIDE) {
       // A operand of lane (row ai, k-quarter qd): quarter qd of each unit of
       // window row ai (rows past the window read row 0 and are never stored)
-      const int ai = lane % 16;
       a_base[0] = (ai < mcount ? ai : 0) * xstride + qd * 16;
       a_live[0] = 1;
-#pragma unroll
-      for (int i = 0; i < NACC; ++i) {
-        const int em = 4 * qd + i;
-        x_base[i] = mrows * xstride + ZB + (em < mcount ? em : 0) * sstride * 4;
-      }
     } else {
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb) {
-        const int ai = lane % 16, am = 4 * mb + ai / 4;
+        const int am = 4 * mb + ai / 4;
         // lane (row ai, k-quarter qd) is live when its quarter is its row's
         // unit and the window row exists
         const bool live = (qd == ai % 4) && (am < mcount);
         a_live[mb] = live ? 1 : 0;
         a_base[mb] = live ? am * xstride + qd * 64 : mrows * xstride;
-        const int em = 4 * mb + qd;
-        x_base[mb] = mrows * xstride + ZB + (em < mcount ? em : 0) * sstride * 4;
       }
     }
   };
@@ -1258,11 +1261,10 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
         *reinterpret_cast<uint32_t*>(slot + MG::WBYTES + 16 * MG::SSTR + s_woff) = sg.b[0];
       }
     }
-    int a_grp[NMB], x_grp[NACC];
+    int a_grp[NMB];
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) a_grp[mb] = a_base[mb] + a_live[mb] * (c.gr * R * 256);
-#pragma unroll
-    for (int mb = 0; mb < NACC; ++mb) x_grp[mb] = x_base[mb] + c.gr * R * 16;
+    const int xa_grp = xa_base + c.gr * R * 16;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       uint32_t wu[B];
@@ -1282,38 +1284,35 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
           wu[h] = *reinterpret_cast<const uint32_t*>(slot + r_off[r][h]);
         }
       }
-      // scales and biases of the round's four units
-      float sv[4], bv[4];
+      // scales of the round's four units; the bias of unit 4r + qd
+      float sv[4];
+      int bofs;
       if constexpr (G == 32) {
         const u32x2 sgv = *reinterpret_cast<const u32x2*>(slot + s_off + r * 8);
-        const u32x2 bgv = *reinterpret_cast<const u32x2*>(slot + b_off + r * 8);
-        const uint32_t sw[2] = {sgv.x, sgv.y}, bw[2] = {bgv.x, bgv.y};
+        const uint32_t sw[2] = {sgv.x, sgv.y};
 #pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2) {
-          sv[q2] = group_value<4>(sw, q2);
-          bv[q2] = group_value<4>(bw, q2);
-        }
+        for (int q2 = 0; q2 < 4; ++q2) sv[q2] = group_value<4>(sw, q2);
+        bofs = r * 8;
       } else if constexpr (G == 64) {
         const uint32_t sw = *reinterpret_cast<const uint32_t*>(slot + s_off + r * 4);
-        const uint32_t bw = *reinterpret_cast<const uint32_t*>(slot + b_off + r * 4);
 #pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2) {
+        for (int q2 = 0; q2 < 4; ++q2)
           sv[q2] = q2 >= 2 ? __uint_as_float(sw & 0xffff0000u) : __uint_as_float(sw << 16);
-          bv[q2] = q2 >= 2 ? __uint_as_float(bw & 0xffff0000u) : __uint_as_float(bw << 16);
-        }
+        bofs = r * 4;
       } else {
         // group index of this round within the kept bytes: r, or at SB = 2
         // the half of the aligned dword
         const int gi = MG::SB < 4 ? ((c.gr * R + r) & 1) : r;
         const uint32_t sw = *reinterpret_cast<const uint32_t*>(slot + s_off + (gi / 2) * 4);
-        const uint32_t bw = *reinterpret_cast<const uint32_t*>(slot + b_off + (gi / 2) * 4);
         const float s1 = (gi & 1) ? __uint_as_float(sw & 0xffff0000u) : __uint_as_float(sw << 16);
-        const float b1 = (gi & 1) ? __uint_as_float(bw & 0xffff0000u) : __uint_as_float(bw << 16);
 #pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2) {
-          sv[q2] = s1;
-          bv[q2] = b1;
-        }
+        for (int q2 = 0; q2 < 4; ++q2) sv[q2] = s1;
+        bofs = gi * 2;
+      }
+      {
+        const float xa = *reinterpret_cast<const float*>(smem + xa_grp + r * 16);
+        const uint32_t braw = *reinterpret_cast<const uint16_t*>(slot + b_off + b_lane + bofs);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xa, __uint_as_float(braw << 16), acc, 0, 0, 0);
       }
       if constexpr (WIDE) {
         // A operand: quarter qd of the round's four units of row lane % 16;
@@ -1321,9 +1320,6 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
         u32x4 aw[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) aw[u] = *reinterpret_cast<const u32x4*>(smem + a_grp[0] + r * 256 + u * 64);
-        f32x4_t xw[NACC];
-#pragma unroll
-        for (int i = 0; i < NACC; ++i) xw[i] = *reinterpret_cast<const f32x4_t*>(smem + x_grp[i] + r * 16);
         // B operand: this lane's unit as 16 exact bf16 pairs, then quarter
         // qd of each of the four units
         uint32_t qp[16];
@@ -1345,23 +1341,17 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
-          for (int i = 0; i < NACC; ++i) {
-            acc[i] = __builtin_fmaf(sv[u], d[u][i], acc[i]);
-            acc[i] = __builtin_fmaf(bv[u], xw[i][u], acc[i]);
-          }
+          for (int i = 0; i < NACC; ++i) acc[i] = __builtin_fmaf(sv[u], d[u][i], acc[i]);
         continue;
       }
       // A operand and unit sums of every 4-row block (rows past the window
       // read zeros and are never stored)
       u32x4 av[NMB][4];
-      f32x4_t xsv[NMB];
 #pragma unroll
-      for (int mb = 0; mb < NMB; ++mb) {
+      for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
         for (int sidx = 0; sidx < 4; ++sidx)
           av[mb][sidx] = *reinterpret_cast<const u32x4*>(smem + a_grp[mb] + r * 256 + sidx * 16);
-        xsv[mb] = *reinterpret_cast<const f32x4_t*>(smem + x_grp[mb] + r * 16);
-      }
       // B operand: this lane's unit as 16 exact bf16 pairs
       uint32_t qp[16];
       unpack_codes<B, 32>(wu, qp);
@@ -1384,10 +1374,7 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2) {
-          acc[mb] = __builtin_fmaf(sv[q2], d[mb][q2], acc[mb]);
-          acc[mb] = __builtin_fmaf(bv[q2], xsv[mb][q2], acc[mb]);
-        }
+        for (int q2 = 0; q2 < 4; ++q2) acc[mb] = __builtin_fmaf(sv[q2], d[mb][q2], acc[mb]);
     }
     if (c.gr == gr0 + gpp - 1) {
       const int col = ((bx + c.i * gx) * ncg + cg) * cw + j;
@@ -1430,8 +1417,7 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
                                                 off, 0, 0);
         }
       }
-#pragma unroll
-      for (int mb = 0; mb < NACC; ++mb) acc[mb] = 0.0f;
+      acc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
   };
 
