@@ -218,18 +218,15 @@ size_t lds_bytes(const qgemv_handle* h, int var, int stage) {
 
 // The matrix-core kernels' LDS: the staged window (rows of k/32 units x 64
 // bytes, a zero area of R * 256 bytes, unit sums; rows padded by 16 bytes),
-// the routed list of an indexed call, one load-group slot per wave, and with
-// a K split the waves' partial sums (one per 4-row block per lane, or in the
-// wide form up to 4 rows per lane).  Returns false when it exceeds one
-// block's LDS.
+// the routed list of an indexed call, and one load-group slot per wave (which
+// also holds the wave's K-split partial sums at a tile's end).  Returns false
+// when it exceeds one block's LDS.
 bool mfma_plan(const qgemv_handle* h, int var, bool indexed, size_t* lds) {
   const size_t mb = static_cast<size_t>(qg::kWindows[var]);
   const size_t units = static_cast<size_t>(h->d.k) / 32;
   const size_t waves = static_cast<size_t>(h->entry->mfma_waves[var]);
-  const size_t per_lane = h->arith == QGEMV_ARITH_WIDE ? (mb < 4 ? mb : 4) : (mb + 3) / 4;
   const size_t b = mb * (units * 64 + 16) + 256 * static_cast<size_t>(h->entry->mfma_group) + mb * (units + 4) * 4 +
-                   (indexed ? qg::kMaxList * 4 : 0) + waves * h->entry->mfma_slot +
-                   (h->ksplit > 1 ? waves * per_lane * qg::kWave * 4 : 0);
+                   (indexed ? qg::kMaxList * 4 : 0) + waves * h->entry->mfma_slot;
   if (b > qg::kMaxMfmaLds) return false;
   *lds = b;
   return true;

@@ -1064,8 +1064,11 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
   // read at the same offsets as a live lane's), unit sums [mrows][units]
   // fp32 (rows of activations and of sums padded by 16 bytes, so the rows a
   // wave reads at once fall in different banks), the routed list (indexed
-  // calls), one slot per wave, then (K split) the partial sums
-  // [waves][NMB][64 lanes] fp32.
+  // calls), one slot per wave.  With a K split, each wave's partial sums
+  // [NACC][64 lanes] fp32 go to the start of its own slot at a tile's end:
+  // the slot's last group has been read by then (a wave's LDS operations
+  // stay in order), and the next hand-off into it follows the barrier after
+  // the partials are read.
   unsigned char* zero_area = smem + static_cast<size_t>(mrows) * xstride;
   float* xsum = reinterpret_cast<float*>(zero_area + ZB);
   int* s_list = reinterpret_cast<int*>(xsum + static_cast<size_t>(mrows) * sstride);
@@ -1077,7 +1080,7 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
   const int j = lane % 16, qd = lane / 16;
   const int cg = wv / S, ks = wv - (wv / S) * S;   // column group, K-part
   unsigned char* slot = slots + static_cast<size_t>(wv) * MG::SLOT;
-  float* partial = reinterpret_cast<float*>(slots + static_cast<size_t>(NW) * MG::SLOT);
+  static_assert(4 * kWave * 4 <= MG::SLOT, "partial sums fit a slot");
 
   int expert = 0;
   int total = p.m;
@@ -1386,14 +1389,15 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
       } else {
         // the column group's parts meet in LDS and are added in part order
 #pragma unroll
-        for (int mb = 0; mb < NACC; ++mb) partial[(wv * NACC + mb) * kWave + lane] = acc[mb];
+        for (int mb = 0; mb < NACC; ++mb) reinterpret_cast<float*>(slot)[mb * kWave + lane] = acc[mb];
         __syncthreads();
         store = ks == 0;
         if (store) {
 #pragma unroll
           for (int mb = 0; mb < NACC; ++mb) {
-            float v = partial[((cg * S) * NACC + mb) * kWave + lane];
-            for (int q = 1; q < S; ++q) v += partial[((cg * S + q) * NACC + mb) * kWave + lane];
+            float v = reinterpret_cast<const float*>(slots + static_cast<size_t>(cg * S) * MG::SLOT)[mb * kWave + lane];
+            for (int q = 1; q < S; ++q)
+              v += reinterpret_cast<const float*>(slots + static_cast<size_t>(cg * S + q) * MG::SLOT)[mb * kWave + lane];
             out[mb] = v;
           }
         }
