@@ -213,6 +213,33 @@ def time_workload(wl: Workload, steps: int, warmup: int, torch):
     return ms, batches
 
 
+def launch_floor(torch, kernels: int = 200, replays: int = 20) -> float:
+    """Device-side interval between back-to-back trivial kernels (one-element
+    adds), in microseconds: a captured graph of `kernels` launches is replayed
+    so that the host's issue cost stays out of the measurement."""
+    z = torch.zeros(1, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            z.add_(1.0)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(kernels):
+            z.add_(1.0)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (kernels * replays)
+
+
 def cpu_baseline(budget_s: float = 12.0):
     """The oracle, as it stands, on a bounded sample of LM-head columns at a
     1-row window, threads = host cores (capped at 16)."""
@@ -331,6 +358,10 @@ def main():
             del w2
             torch.cuda.empty_cache()
         out["workloads"] = extra
+        floor = launch_floor(torch)
+        out["launch_floor_us"] = round(floor, 3)
+        print(f"# launch floor (trivial kernels back to back, graph replay): {floor:.3f} us", file=sys.stderr,
+              flush=True)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)
