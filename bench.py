@@ -33,17 +33,18 @@ sys.path.insert(0, ROOT)
 
 PEAK_GBS = 8000.0          # MI355X HBM3E, published
 ROTATE_BYTES = 1 << 30     # at least 1 GiB of distinct weight copies
-KERNEL_DIR = os.path.join(ROOT, "bit_affine_quantized_amd", "csrc")
+LIB_DEFAULT = os.path.join(ROOT, "bit_affine_quantized_amd", "libqgemv.so")
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
 def kernel_hash() -> str:
-    """Hash of every kernel and host source of the library."""
+    """Hash of the built library this run loads (the kernels' machine code):
+    a counter summary applies to the run only when it was taken on the same
+    build."""
+    path = os.environ.get("QGEMV_LIB") or LIB_DEFAULT
     h = hashlib.sha256()
-    for name in sorted(os.listdir(KERNEL_DIR)):
-        if name.endswith((".hip", ".h")):
-            h.update(name.encode())
-            h.update(open(os.path.join(KERNEL_DIR, name), "rb").read())
+    with open(path, "rb") as f:
+        h.update(f.read())
     return h.hexdigest()[:16]
 
 

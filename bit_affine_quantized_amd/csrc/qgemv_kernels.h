@@ -956,8 +956,10 @@ __global__ __launch_bounds__(kThreads) void qrow_fast(const Params p) {
 // 8q'..8q'+7 and zeros elsewhere, so after the four steps D[4m + q'][j] is
 // the fp32 dot of unit q' of column j with window row m, every product
 // exact.  Lane l holds D[4(l/16) + q'][l % 16] for q' = 0..3 (one window
-// row, one column, four units) and folds them in unit order:
-// P = fma(s, D, P); P = fma(bias, X, P).  No lane reduction follows, and
+// row, one column, four units).  Per round the bias terms of the four units,
+// sum over u of bias(u) * X(row, u), come first as one fp32 16x16x4 product
+// accumulated into the lane's outputs; then the lane folds its units' scale
+// terms in unit order, P = fma(s, D, P).  No lane reduction follows, and
 // each output depends only on its own window row's activations, wherever the
 // row sits in the window.
 //
@@ -973,7 +975,8 @@ __global__ __launch_bounds__(kThreads) void qrow_fast(const Params p) {
 // K split: a handle may split K into S = 1, 2 or 4 consecutive parts (fixed
 // at create from its shape, never from the window).  The S waves of a
 // column group each fold their part's units in order from zero, and the
-// parts are then added in order, P = ((P0 + P1) + P2) + P3, through LDS.
+// parts are then added in order, P = ((P0 + P1) + P2) + P3, through the
+// waves' LDS slots.
 //
 // Gate/up pairs: the 16 MFMA columns of a tile are rows f0..f0+7 of the gate
 // matrix (columns 0-7) and the same rows of the up matrix (columns 8-15).

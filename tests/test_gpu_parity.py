@@ -314,10 +314,11 @@ def test_widen_is_exact():
 
 def test_widen_fused_members_in_order_and_products():
     """Two members of different widths, widened to their common width one call
-    each into consecutive rows of one matrix, keep their values in order; the widened matrix's products, in both forms, meet
-    the bound around the source's fp64 product (the dequantized values are
-    the same; a smaller group re-associates the fp32 sums, so bit equality
-    with the source's product is not expected)."""
+    each into consecutive rows of one matrix, keep their values in order; the
+    widened matrices' products, in every arithmetic form, meet the bound
+    around the source's fp64 product (the dequantized values are the same; a
+    smaller group re-associates the fp32 sums, so bit equality with the
+    source's product is not expected)."""
     k = 2048
     members = [(4, 64, 100), (5, 128, 48)]
     rc, cb, cg = qgemv.qgemv_common_width([m[0] for m in members], [m[1] for m in members])
