@@ -278,8 +278,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=300,
-                    help="untimed steps; the GPU clock needs ~20 ms of load to settle")
+    ap.add_argument("--warmup", type=int, default=1000,
+                    help="untimed steps; the GPU clock needs tens of ms of load to settle")
     ap.add_argument("--workload", default="lmhead", choices=["lmhead", "stack", "stack3", "experts"])
     ap.add_argument("--m", type=int, default=1, help="window rows")
     ap.add_argument("--all", action="store_true", help="also time the other workloads and windows")
