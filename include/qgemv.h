@@ -57,7 +57,8 @@ extern "C" {
                                  k*bits not a multiple of 32, too large     */
 #define QGEMV_E_STRIDE (-5)   /* output row stride below n                  */
 #define QGEMV_E_ALIGN (-6)    /* pointer not aligned to its element type    */
-#define QGEMV_E_WINDOW (-7)   /* window rows outside 0..16                  */
+#define QGEMV_E_WINDOW (-7)   /* window rows outside 0..16 (0..65 for plain
+                                 and strided calls, matrix-core forms)      */
 #define QGEMV_E_ALIAS (-8)    /* output overlaps an input                   */
 #define QGEMV_E_NOKERNEL (-9) /* no compiled kernel for this shape          */
 #define QGEMV_E_HIP (-10)     /* a HIP runtime call failed                  */
@@ -67,7 +68,7 @@ extern "C" {
 #define QGEMV_EPI_RELU2 1     /* y > 0 ? y*y : (y is NaN ? y : +0), on fp32 y */
 
 #define QGEMV_MAX_WINDOW 16
-#define QGEMV_MAX_PROMPT 65   /* prompt windows: plain and strided calls, MFMA form */
+#define QGEMV_MAX_PROMPT 65   /* prompt windows: plain and strided calls, matrix-core forms */
 
 /* Weights of one handle.
  *   bits       code width: 2, 3, 4, 5, 6 or 8.
@@ -100,13 +101,15 @@ typedef struct qgemv_handle* qgemv_t;
 int qgemv_create(const qgemv_desc* d, qgemv_t* out);
 
 /* ---- arithmetic of a handle --------------------------------------------
- * Both forms compute, per output, the sum over the row's 32-code units u of
+ * Every form computes, per output, the sum over the row's 32-code units u of
  *   scale(u) * A(u) + bias(u) * X(u),
  * A(u) the fp32 dot of the unit's exact bf16 codes with its activations and
  * X(u) the fp32 sum of its activations ("Exactness", item "Precision", on
- * "...support for oQ..." #774: bf16 activations, fp32 group sums).  They
- * differ in how A(u) is summed and in the order of the folds, so their bits
- * differ (each stays within the fp64 bound).  The form is fixed at create
+ * "...support for oQ..." #774: bf16 activations, fp32 group sums).  The
+ * forms differ in how A(u) is summed and in the order of the folds (the
+ * matrix-core forms add each 128-code round's four bias terms first, as one
+ * fp32 matrix-core product), so their bits differ; each stays within the
+ * fp64 bound.  The form is fixed at create
  * for every window, strided and indexed call of the handle, which is what
  * keeps a row's bits the same alone and inside any window.
  *   QGEMV_ARITH_DOT   lanes own slices of a row's K; v_dot2 chains, then one
