@@ -947,16 +947,18 @@ __global__ __launch_bounds__(kThreads) void qrow_fast(const Params p) {
 // MFMA kernel: v_mfma_f32_16x16x32_bf16 with a block-diagonal activation
 // operand.
 //
-// A wave owns 16 output columns and walks K in rounds of 128 codes per
-// column.  In a round, lane l (column j = l % 16, quarter q = l / 16) holds
-// the 32-code unit q of its column as exact bf16 pairs in the unpack's slot
-// order.  MFMA step s (0..3) feeds slots 8s..8s+7 of every lane's unit as
-// the B operand (k-index 8q + e of column j).  Row i = 4m + q' of the A
-// operand holds window row m's activations of unit q' in k-indices
-// 8q'..8q'+7 and zeros elsewhere, so after the four steps D[4m + q'][j] is
-// the fp32 dot of unit q' of column j with window row m, every product
-// exact.  Lane l holds D[4(l/16) + q'][l % 16] for q' = 0..3 (one window
-// row, one column, four units).  Per round the bias terms of the four units,
+// A wave owns 16 output columns and walks K in load groups of R rounds of
+// 128 codes per column.  Lane l (column j = l % 16, quarter q = l / 16) owns
+// units qR .. qR + R - 1 of its column's share of a group (whole 16-byte
+// pieces, read from LDS once per group) and in round r holds unit qR + r as
+// exact bf16 pairs in the unpack's slot order.  MFMA step s (0..3) feeds
+// slots 8s..8s+7 of every lane's unit as the B operand (k-index 8q + e of
+// column j).  Row i = 4m + q' of the A operand holds window row m's
+// activations of unit q'R + r in k-indices 8q'..8q'+7 and zeros elsewhere,
+// so after the four steps D[4m + q'][j] is the fp32 dot of unit q'R + r of
+// column j with window row m, every product exact.  Lane l holds
+// D[4(l/16) + q'][l % 16] for q' = 0..3 (one window row, one column, four
+// units).  Per round the bias terms of the four units,
 // sum over u of bias(u) * X(row, u), come first as one fp32 16x16x4 product
 // accumulated into the lane's outputs; then the lane folds its units' scale
 // terms in unit order, P = fma(s, D, P).  No lane reduction follows, and
@@ -1002,7 +1004,6 @@ template <int B, int G> struct MGroup {
   static constexpr int SSTR = SBP % 32 == 0 ? SBP + 16 : SBP;   // LDS bytes per column of scales
   static constexpr int WBYTES = 16 * L * 128;
   static constexpr int SLOT = WBYTES + 2 * 16 * SSTR;
-  static constexpr int CH = (B % 4 == 0) ? 4 : ((B % 2 == 0) ? 2 : 1);   // words per LDS read
   static_assert(R * B % 8 == 0 && SLANES <= 64, "group geometry");
 };
 
@@ -1047,7 +1048,7 @@ template <int B, int G, int MB, bool WIDE = false>
 __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const int gx, unsigned char* smem,
                                           int* s_wave_cnt, int* s_xrow, int64_t* s_yoff) {
   using MG = MGroup<B, G>;
-  constexpr int R = MG::R, CH = MG::CH, SSZ = MG::SSZ;
+  constexpr int R = MG::R, SSZ = MG::SSZ;
   constexpr int NW = MWaves<MB>::v, NT = NW * kWave;
   constexpr int NMB = (MB + 3) / 4;         // 4-row blocks of the window
   // outputs each lane folds: one per 4-row block, or (wide form) window rows
@@ -1126,19 +1127,21 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
   const int s_col = lane / SPER;
   const int s_voff = (gu ? (s_col & 7) : s_col) * gpr2 + (lane % SPER) * SSZ;
   const int s_woff = (lane / SPER) * MG::SSTR + (lane % SPER) * SSZ;   // its place in the slot
-  // this lane's unit words in round r: word w = r*4B + qd*B + h of column
-  // j's share sits at piece w / 4 -> line (w/4) / 8, piece (w/4) % 8
-  auto word_off = [&](int w) {
-    const int pc = w / 4, ln = pc / 8, pp = pc % 8;
-    return ((ln * 16 + j) * 8 + ((pp + j / 2) & 7)) * 16 + (w % 4) * 4;
-  };
-  int r_off[R][B / CH];
+  // Lane (j, qd) owns units qd*R .. qd*R + R - 1 of column j's share of a
+  // group (unit qd*R + r in round r): NP = R*B/4 whole 16-byte pieces,
+  // pieces qd*NP + t of the share, at line (qd*NP + t) / 8, piece
+  // (qd*NP + t) % 8 of the slot (rotated by j / 2).
+  constexpr int NP = R * B / 4;
+  static_assert((R * B) % 4 == 0, "a lane's units are whole pieces");
+  int p_off[NP];
 #pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int h = 0; h < B / CH; ++h) r_off[r][h] = word_off(r * 4 * B + qd * B + h * CH);
+  for (int t = 0; t < NP; ++t) {
+    const int pc = qd * NP + t, ln = pc / 8, pp = pc % 8;
+    p_off[t] = ((ln * 16 + j) * 8 + ((pp + j / 2) & 7)) * 16;
+  }
   const int s_off = MG::WBYTES + j * MG::SSTR;
   const int b_off = s_off + 16 * MG::SSTR;
+  constexpr int UPG = G / 32;                 // units per group
 
   // A step is one group of this wave's K-part of one tile; cursors walk the
   // steps in order (gr counts groups from the start of the row)
@@ -1224,14 +1227,16 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
   // itself in the wide form, 4 (rho % 4) + rho / 4 for 4-row blocks.
   const int ai = lane % 16;
   const int xrow = WIDE ? ai : 4 * (ai % 4) + ai / 4;
-  // bias of unit 4r + qd of column j, from the slot's bias bytes
-  const int b_lane = (G == 32) ? qd * 2 : ((G == 64) ? (qd / 2) * 2 : 0);
+  // bias of unit qd*R + r of column j, from the slot's bias bytes: group
+  // (qd*R + r) / UPG of the share, = qd*R/UPG + r/UPG when UPG divides R,
+  // else qd*R/UPG (r < R <= UPG/2 never crosses a group)
+  const int b_lane = ((qd * R) / UPG) * 2;
 
   // per-lane LDS offsets (from smem) of the A operands, set for each pass of
   // window rows and advanced per group
   int a_base[NMB], a_live[NMB], xa_base = 0;
   auto set_bases = [&]() {
-    xa_base = mrows * xstride + ZB + ((xrow < mcount ? xrow : 0) * sstride + qd) * 4;
+    xa_base = mrows * xstride + ZB + ((xrow < mcount ? xrow : 0) * sstride + qd * R) * 4;
     if constexpr (WIDE) {
       // A operand of lane (row ai, k-quarter qd): quarter qd of each unit of
       // window row ai (rows past the window read row 0 and are never stored)
@@ -1245,7 +1250,7 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
         // unit and the window row exists
         const bool live = (qd == ai % 4) && (am < mcount);
         a_live[mb] = live ? 1 : 0;
-        a_base[mb] = live ? am * xstride + qd * 64 : mrows * xstride;
+        a_base[mb] = live ? am * xstride + qd * R * 64 : mrows * xstride;
       }
     }
   };
@@ -1271,52 +1276,50 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) a_grp[mb] = a_base[mb] + a_live[mb] * (c.gr * R * 256);
     const int xa_grp = xa_base + c.gr * R * 16;
+    // the group's scale bytes of column j (the kept bytes), read once
+    constexpr int NSW = MG::SBP / 4;
+    uint32_t sw[NSW];
+    if constexpr (MG::SBP >= 16) {
+#pragma unroll
+      for (int t = 0; t < MG::SBP / 16; ++t) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(slot + s_off + t * 16);
+        sw[4 * t] = v.x;
+        sw[4 * t + 1] = v.y;
+        sw[4 * t + 2] = v.z;
+        sw[4 * t + 3] = v.w;
+      }
+    } else if constexpr (MG::SBP == 8) {
+      const u32x2 v = *reinterpret_cast<const u32x2*>(slot + s_off);
+      sw[0] = v.x;
+      sw[1] = v.y;
+    } else {
+      sw[0] = *reinterpret_cast<const uint32_t*>(slot + s_off);
+    }
+    u32x4 pcs[NP];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
+      // this round's unit (words rB .. rB + B - 1 of the lane's pieces): read
+      // the pieces the previous round has not
+#pragma unroll
+      for (int t = 0; t < NP; ++t)
+        if (t >= (r * B) / 4 && t <= (r * B + B - 1) / 4 && (r == 0 || t > ((r - 1) * B + B - 1) / 4))
+          pcs[t] = *reinterpret_cast<const u32x4*>(slot + p_off[t]);
       uint32_t wu[B];
 #pragma unroll
-      for (int h = 0; h < B / CH; ++h) {
-        if constexpr (CH == 4) {
-          const u32x4 v = *reinterpret_cast<const u32x4*>(slot + r_off[r][h]);
-          wu[4 * h] = v.x;
-          wu[4 * h + 1] = v.y;
-          wu[4 * h + 2] = v.z;
-          wu[4 * h + 3] = v.w;
-        } else if constexpr (CH == 2) {
-          const u32x2 v = *reinterpret_cast<const u32x2*>(slot + r_off[r][h]);
-          wu[2 * h] = v.x;
-          wu[2 * h + 1] = v.y;
-        } else {
-          wu[h] = *reinterpret_cast<const uint32_t*>(slot + r_off[r][h]);
-        }
-      }
-      // scales of the round's four units; the bias of unit 4r + qd
+      for (int h = 0; h < B; ++h) wu[h] = pcs[(r * B + h) / 4][(r * B + h) % 4];
+      // scales of the round's four units i*R + r; at SB = 2 the round's one
+      // group is a half of the aligned dword
       float sv[4];
-      int bofs;
-      if constexpr (G == 32) {
-        const u32x2 sgv = *reinterpret_cast<const u32x2*>(slot + s_off + r * 8);
-        const uint32_t sw[2] = {sgv.x, sgv.y};
 #pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2) sv[q2] = group_value<4>(sw, q2);
-        bofs = r * 8;
-      } else if constexpr (G == 64) {
-        const uint32_t sw = *reinterpret_cast<const uint32_t*>(slot + s_off + r * 4);
-#pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2)
-          sv[q2] = q2 >= 2 ? __uint_as_float(sw & 0xffff0000u) : __uint_as_float(sw << 16);
-        bofs = r * 4;
-      } else {
-        // group index of this round within the kept bytes: r, or at SB = 2
-        // the half of the aligned dword
-        const int gi = MG::SB < 4 ? ((c.gr * R + r) & 1) : r;
-        const uint32_t sw = *reinterpret_cast<const uint32_t*>(slot + s_off + (gi / 2) * 4);
-        const float s1 = (gi & 1) ? __uint_as_float(sw & 0xffff0000u) : __uint_as_float(sw << 16);
-#pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2) sv[q2] = s1;
-        bofs = gi * 2;
+      for (int i = 0; i < 4; ++i) {
+        const int si = MG::SB < 4 ? ((c.gr * R + r) & 1) : (i * R + r) / UPG;
+        const uint32_t w = sw[MG::SB < 4 ? 0 : si / 2];
+        sv[i] = (si & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
       }
+      // the bias of this lane's unit qd*R + r
+      const int bofs = MG::SB < 4 ? ((c.gr * R + r) & 1) * 2 : (UPG <= R ? (r / UPG) * 2 : 0);
       {
-        const float xa = *reinterpret_cast<const float*>(smem + xa_grp + r * 16);
+        const float xa = *reinterpret_cast<const float*>(smem + xa_grp + r * 4);
         const uint32_t braw = *reinterpret_cast<const uint16_t*>(slot + b_off + b_lane + bofs);
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xa, __uint_as_float(braw << 16), acc, 0, 0, 0);
       }
@@ -1325,7 +1328,7 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
         // the unit sums of the rows this lane folds
         u32x4 aw[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) aw[u] = *reinterpret_cast<const u32x4*>(smem + a_grp[0] + r * 256 + u * 64);
+        for (int u = 0; u < 4; ++u) aw[u] = *reinterpret_cast<const u32x4*>(smem + a_grp[0] + (u * R + r) * 64);
         // B operand: this lane's unit as 16 exact bf16 pairs, then quarter
         // qd of each of the four units
         uint32_t qp[16];
@@ -1357,7 +1360,7 @@ __device__ __forceinline__ void mfma_body(const Params& p, const int bx, const i
       for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
         for (int sidx = 0; sidx < 4; ++sidx)
-          av[mb][sidx] = *reinterpret_cast<const u32x4*>(smem + a_grp[mb] + r * 256 + sidx * 16);
+          av[mb][sidx] = *reinterpret_cast<const u32x4*>(smem + a_grp[mb] + r * 64 + sidx * 16);
       // B operand: this lane's unit as 16 exact bf16 pairs
       uint32_t qp[16];
       unpack_codes<B, 32>(wu, qp);
