@@ -11,6 +11,7 @@ ordinary VGPRs (the epilogue reads them with plain VALU operands).
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -23,6 +24,9 @@ SOURCES = (["qgemv.hip"] + [f"qgemv_b{b}.hip" for b in (2, 3, 4, 5, 6, 8)]
            + [f"qgemv_stack_m{m}.hip" for m in (1, 2, 4, 8, 16)])
 LIB = os.path.join(HERE, "libqgemv.so")
 BUILD_DIR = os.path.join(HERE, "_build")
+# per-kernel registers, scratch, LDS and occupancy, from the compiler's
+# resource remarks of the last build
+RESOURCES = os.path.join(BUILD_DIR, "kernel_resources.txt")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [
@@ -30,7 +34,29 @@ FLAGS = [
     "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+    "-Rpass-analysis=kernel-resource-usage",
 ]
+_FIELDS = (("VGPRs", "vgprs"), ("AGPRs", "agprs"), ("ScratchSize [bytes/lane]", "scratch"),
+           ("Occupancy [waves/SIMD]", "occupancy"), ("VGPRs Spill", "vgpr_spill"),
+           ("LDS Size [bytes/block]", "static_lds"))
+
+
+def _resources(text: str) -> dict:
+    """Kernel name -> resource fields, from -Rpass-analysis=kernel-resource-usage remarks."""
+    out, cur = {}, None
+    for line in text.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            cur = m.group(1)
+            out[cur] = {}
+            continue
+        if cur is None:
+            continue
+        for label, key in _FIELDS:
+            m = re.search(r"remark:\s+" + re.escape(label) + r": (\d+)", line)
+            if m:
+                out[cur][key] = int(m.group(1))
+    return out
 
 
 def _run(cmd):
@@ -52,7 +78,16 @@ def build(out: str = LIB, extra=(), jobs: int | None = None) -> str:
         objs.append(obj)
         cmds.append([HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(jobs) as ex:
-        list(ex.map(_run, cmds))
+        results = list(ex.map(_run, cmds))
+    res = {}
+    for r in results:
+        res.update(_resources(r.stderr))
+    with open(RESOURCES, "w") as f:
+        f.write("# kernel vgprs agprs scratch_bytes_per_lane vgpr_spill static_lds occupancy_waves_per_simd\n")
+        for name in sorted(res):
+            v = res[name]
+            f.write(f"{name} {v.get('vgprs', -1)} {v.get('agprs', -1)} {v.get('scratch', -1)} "
+                    f"{v.get('vgpr_spill', -1)} {v.get('static_lds', -1)} {v.get('occupancy', -1)}\n")
     tmp = out + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, out)

@@ -277,3 +277,19 @@ def test_common_width_and_widen_refusals():
     assert wd(5, 64, 16, 2048, W, S, B, 6, 32, W + 64, SO, BO) == qgemv.QGEMV_E_ALIAS
     assert wd(5, 64, 16, 2048, W, S, B, 6, 32, WO, SO, SO + 8) == qgemv.QGEMV_E_ALIAS
     assert wd(5, 64, 16, 2048, W, S, B, 6, 32, WO + 4, SO, BO) == qgemv.QGEMV_E_ALIGN
+
+
+def test_kernel_resources_recorded_without_spills():
+    """The build records every kernel's registers, scratch, LDS and occupancy
+    from the compiler's resource remarks; no kernel spills to scratch, and the
+    matrix-core kernels keep at least 2 waves per SIMD."""
+    from bit_affine_quantized_amd import build as hip_build
+    if not os.path.exists(hip_build.RESOURCES):
+        pytest.skip("library not built here")
+    rows = [line.split() for line in open(hip_build.RESOURCES) if not line.startswith("#")]
+    assert len(rows) > 300
+    for name, vgprs, agprs, scratch, spill, lds, occ in rows:
+        assert int(scratch) == 0 and int(spill) == 0, f"{name} spills"
+        assert 0 < int(vgprs) + int(agprs) <= 512 and int(lds) <= 64 * 1024, name
+        if "qrow_mfma" in name:
+            assert int(occ) >= 2, f"{name}: occupancy {occ}"
