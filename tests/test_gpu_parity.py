@@ -667,3 +667,60 @@ def test_fused_stack_all_widths(epi):
     specs = [(2, 32, [(300, 5000)]), (3, 64, [(128, 0), (72, 4000)]), (4, 128, [(512, 200)]),
              (5, 32, [(64, 712)]), (6, 128, [(1000, 3000)]), (8, 64, [(256, 776), (16, 1100)])]
     _check_stack(specs, 4096, 5400, 5, 3300 + epi, epi)
+
+
+# ---------------------------------------------------------------------------
+# seeded random shapes across widths, groups, forms and windows
+# ---------------------------------------------------------------------------
+
+def _random_cases(count=40, seed=20260):
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < count:
+        bits, group = PAIRS[int(rng.integers(len(PAIRS)))]
+        arith = ARITHS[int(rng.integers(len(ARITHS)))]
+        step = qgemv.qgemv_mfma_codes(bits, group) if arith != qgemv.QGEMV_ARITH_DOT else group
+        k = step * int(rng.integers(1, max(2, 4096 // step) + 1))
+        n = int(rng.integers(1, 2600))
+        top = qgemv.QGEMV_MAX_PROMPT if arith != qgemv.QGEMV_ARITH_DOT else qgemv.QGEMV_MAX_WINDOW
+        m = int(rng.integers(1, top + 1))
+        if n * k * m > 12_000_000 or k > 4096:
+            continue
+        cases.append((bits, group, n, k, m, arith, int(rng.integers(1 << 30))))
+    return cases
+
+
+@pytest.mark.parametrize("bits,group,n,k,m,arith,seed", _random_cases())
+def test_random_shapes(bits, group, n, k, m, arith, seed):
+    """Random (seeded) shapes: ragged N, every admissible K of the form up to
+    4096, windows up to the form's limit.  Outputs meet the bound; two rows
+    equal their 1-row calls bit for bit; a strided call equals the plain one
+    and leaves the gaps untouched."""
+    print_case("random", bits, group, n, k, m, arith, seed)
+    d = synth.matrix(seed, bits, group, n, k, m)
+    try:
+        mat = matrix_of(d, arith=arith)
+    except qgemv.QgemvError as e:
+        # the dot form's fast and generic kernels take every admitted K; a
+        # window too wide for LDS is the only refusal expected here
+        assert arith == qgemv.QGEMV_ARITH_DOT and "WINDOW" in str(e), str(e)
+        return
+    xt = dev(d["x"])
+    y = torch.empty((m, n), dtype=torch.float32, device=DEV)
+    try:
+        mat.run(xt, y, m=m)
+    except qgemv.QgemvError as e:
+        assert arith == qgemv.QGEMV_ARITH_DOT and "QGEMV_E_WINDOW" in str(e), str(e)
+        return
+    y64, a64, _ = oracle.gemv(d["words"], d["scales"], d["biases"], d["x"], bits, group, n, k, threads=THREADS)
+    check_bound(y.cpu().numpy(), y64, a64, k, f"random {bits}/{group} {n}x{k} m={m} arith={arith}")
+    for r in sorted({0, m - 1, m // 2}):
+        assert bits_equal(run(mat, xt[r:r + 1])[0], y[r]), f"row {r}"
+    ldy = n + 3
+    sentinel = torch.full((m, ldy), 0x7FC0BEEF, dtype=torch.int32, device=DEV)
+    ys = sentinel.clone().view(torch.float32)
+    mat.run_strided(xt, ys.view(-1)[1:], ldy, m=m)
+    assert bits_equal(ys[:, 1:1 + n], y)
+    gap = torch.ones((m, ldy), dtype=torch.bool, device=DEV)
+    gap[:, 1:1 + n] = False
+    assert torch.equal(ys.view(torch.int32)[gap], sentinel[gap])
