@@ -170,6 +170,17 @@ class Workload:
         first = self.copies[0][1][0]
         self.arith_used = "auto" if self.kind == "fused" else ARITH_NAMES[first.arith]
 
+    def counts(self):
+        """(weight elements streamed, multiply-adds) per step: rows x cols of
+        every matrix read (the distinct experts for an indexed call), and
+        window rows x output columns x K."""
+        rows_cols = sum(n for _, _, n in self.runs) * self.k
+        if self.kind == "indexed":
+            macs = self.m * self.slots * self.n_each * self.k
+        else:
+            macs = self.m * rows_cols
+        return rows_cols, macs
+
     def step(self, i: int, stream: int):
         _, mats = self.copies[i % len(self.copies)]
         q = self.qgemv
@@ -315,6 +326,7 @@ def main():
     wl = Workload(args.workload, args.m, torch, qgemv, synth, arith)
     ms, batches = time_workload(wl, args.steps, args.warmup, torch)
     gbs = wl.bytes / (ms * 1e-3) / 1e9
+    rows_cols, macs = wl.counts()
     traffic = read_traffic(f"{args.workload}_m{wl.m}")
     out = {
         "metric": "effective HBM GB/s (% of MI355X peak) for affine-quant GEMV, 1-16 row windows",
@@ -334,6 +346,8 @@ def main():
                    "arithmetic": f"exact codes as bf16, bf16 activations, fp32 sums ({wl.arith_used} form)"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_GBS, 4), "traffic": traffic},
+        "rows_cols_per_s": round(rows_cols / (ms * 1e-3), 1),
+        "mnk_per_s": round(macs / (ms * 1e-3), 1),
         "batch_ms": [round(b, 6) for b in batches],
         "kernel_sha": kernel_hash(),
     }
@@ -353,7 +367,9 @@ def main():
                 continue
             ms2, _ = time_workload(w2, max(50, args.steps // 2), args.warmup, torch)
             g2 = w2.bytes / (ms2 * 1e-3) / 1e9
+            rc2, mac2 = w2.counts()
             extra[key] = {"us_per_call": round(ms2 * 1e3, 3), "GB/s": round(g2, 1),
+                          "rows_cols_per_s": round(rc2 / (ms2 * 1e-3), 1), "mnk_per_s": round(mac2 / (ms2 * 1e-3), 1),
                           "frac": round(g2 / PEAK_GBS, 4), "bytes": w2.bytes}
             print(f"# {key}: {ms2 * 1e3:.3f} us, {g2:.1f} GB/s", file=sys.stderr, flush=True)
             del w2
