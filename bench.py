@@ -125,6 +125,29 @@ class Workload:
             self.ldy = st["ldy"]
             self.members = [[(6144, 2048), (48, 8192)] if r["n"] == 6192 else [(r["n"], r["col"])]
                             for r in st["runs"]]
+        elif name == "gateup":
+            # the experts config's routing over a gate stack and an up stack
+            # (the up weights are the next seed's draw), silu(g) * u per slot
+            d = synth.experts()
+            du = synth.matrix(5001, d["bits"], d["group"], d["n"], d["k"], 0, d["n_experts"])
+            self.k = d["k"]
+            distinct = len(np.unique(d["idx"]))
+            self.runs = [(d["bits"], d["group"], d["n"] * distinct)] * 2
+            m = d["idx"].shape[0]
+            self.m = m
+            self.slots = d["idx"].shape[1]
+            self.n_out = self.slots * d["n"]
+            self.desc = (f"indexed gate/up pair: 2 x {d['n_experts']} x (N={d['n']} K={d['k']} 4-bit group 64), "
+                         f"{m} rows x {self.slots} slots ({distinct} distinct experts), silu(g) * u")
+            base = [(t(d["words"]), t(d["scales"]), t(d["biases"])),
+                    (t(du["words"]), t(du["scales"]), t(du["biases"]))]
+            self.x = t(d["x"])
+            self.idx = t(d["idx"])
+            self.y = torch.empty((m, self.slots, d["n"]), dtype=torch.float32, device=dev)
+            self.idx_bytes = d["idx"].size * 4
+            self.kind = "gateup"
+            self.n_experts = d["n_experts"]
+            self.n_each = d["n"]
         elif name == "experts":
             d = synth.experts()
             self.k = d["k"]
@@ -158,8 +181,9 @@ class Workload:
                          for (w, s, b), (bits, group, n), mem in zip(trip_list, self.runs, self.members)]
                 self.copies.append((trip_list, [qgemv.Stack(specs, self.ldy)]))
                 continue
-            for (w, s, b), run_ in zip(trip_list, self.runs if self.kind != "indexed" else [None]):
-                if self.kind == "indexed":
+            for (w, s, b), run_ in zip(trip_list, self.runs if self.kind not in ("indexed", "gateup")
+                                           else [None] * len(trip_list)):
+                if self.kind in ("indexed", "gateup"):
                     mats.append(qgemv.Matrix(4, 64, self.n_each, self.k, w, s, b, n_experts=self.n_experts,
                                              arith=arith))
                 else:
@@ -175,8 +199,8 @@ class Workload:
         every matrix read (the distinct experts for an indexed call), and
         window rows x output columns x K."""
         rows_cols = sum(n for _, _, n in self.runs) * self.k
-        if self.kind == "indexed":
-            macs = self.m * self.slots * self.n_each * self.k
+        if self.kind in ("indexed", "gateup"):
+            macs = self.m * self.slots * self.n_each * self.k * len(self.runs)
         else:
             macs = self.m * rows_cols
         return rows_cols, macs
@@ -194,6 +218,10 @@ class Workload:
             for mat, col in zip(mats, self.cols):
                 rc = q.qgemv_run_strided(mat.h, self.x, self.m, self.flat[col:], self.ldy, 0, stream)
                 assert rc == 0, q.qgemv_strerror(rc)
+        elif self.kind == "gateup":
+            rc = q.qgemv_run_gateup_indexed(mats[0].h, mats[1].h, self.x, self.m, self.idx, self.slots,
+                                            self.y, stream)
+            assert rc == 0, q.qgemv_strerror(rc)
         else:
             rc = q.qgemv_run_indexed(mats[0].h, self.x, self.m, self.idx, self.slots, self.y,
                                      q.QGEMV_EPI_RELU2, stream)
@@ -291,7 +319,7 @@ def main():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=1000,
                     help="untimed steps; the GPU clock needs tens of ms of load to settle")
-    ap.add_argument("--workload", default="lmhead", choices=["lmhead", "stack", "stack3", "experts"])
+    ap.add_argument("--workload", default="lmhead", choices=["lmhead", "stack", "stack3", "experts", "gateup"])
     ap.add_argument("--m", type=int, default=1, help="window rows")
     ap.add_argument("--all", action="store_true", help="also time the other workloads and windows")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -359,7 +387,8 @@ def main():
                             ("lmhead", 1, 3), ("lmhead", 8, 3), ("lmhead", 16, 3),
                             ("stack", 1, arith), ("stack", 16, arith), ("stack3", 1, arith), ("stack3", 16, arith),
                             ("stack3", 16, 3),
-                            ("experts", 16, arith), ("experts", 16, 1), ("experts", 16, 2), ("experts", 16, 3)]:
+                            ("experts", 16, arith), ("experts", 16, 1), ("experts", 16, 2), ("experts", 16, 3),
+                            ("gateup", 16, arith), ("gateup", 16, 3)]:
             w2 = Workload(name, m, torch, qgemv, synth, ar)
             key = f"{name}_m{w2.m}_{w2.arith_used}"
             if key in extra or (name == args.workload and m == wl.m and w2.arith_used == wl.arith_used):

@@ -338,8 +338,10 @@ int launch(const qgemv_handle* h, const uint16_t* x, int32_t m, float* y, int64_
     // on the host) keep every CU's waves streaming, few enough that each
     // block's routing and window staging serve several tiles.  Measured on
     // MI355X (128 experts of 1024 x 2048, 16 rows x 8 slots): the matrix-core
-    // form is fastest with 16 (4 tiles a block), the dot form with 32.
-    const int64_t most = mfma ? 16 : 32;
+    // form is fastest with 16 (4 tiles a block), the dot form with 32.  A
+    // gate/up pair's tiles hold 8 output columns, twice as many tiles: 32
+    // keeps 4 tiles a block.
+    const int64_t most = mfma ? (up ? 32 : 16) : 32;
     const int64_t per = tiles < most ? tiles : most;
     grid.x = static_cast<unsigned>(per);
     grid.y = static_cast<unsigned>(h->d.n_experts);
