@@ -23,6 +23,7 @@ import hashlib
 import json
 import os
 import re
+import struct
 import sys
 import time
 
@@ -37,15 +38,30 @@ LIB_DEFAULT = os.path.join(ROOT, "bit_affine_quantized_amd", "libqgemv.so")
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
+def _elf_section(data: bytes, wanted: str):
+    """Bytes of one section of a 64-bit little-endian ELF file, or None."""
+    if data[:5] != b"\x7fELF\x02":
+        return None
+    shoff = struct.unpack_from("<Q", data, 0x28)[0]
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", data, 0x3A)
+    heads = [struct.unpack_from("<IIQQQQ", data, shoff + i * shentsize) for i in range(shnum)]
+    names = heads[shstrndx][4]
+    for name, _, _, _, off, size in heads:
+        end = data.index(b"\0", names + name)
+        if data[names + name:end].decode() == wanted:
+            return data[off:off + size]
+    return None
+
+
 def kernel_hash() -> str:
-    """Hash of the built library this run loads (the kernels' machine code):
-    a counter summary applies to the run only when it was taken on the same
-    build."""
+    """Hash of the kernels' machine code in the library this run loads (its
+    .hip_fatbin section; the whole file if that is missing): a counter
+    summary applies to the run only when it was taken on the same kernels."""
     path = os.environ.get("QGEMV_LIB") or LIB_DEFAULT
-    h = hashlib.sha256()
     with open(path, "rb") as f:
-        h.update(f.read())
-    return h.hexdigest()[:16]
+        data = f.read()
+    code = _elf_section(data, ".hip_fatbin")
+    return hashlib.sha256(code if code is not None else data).hexdigest()[:16]
 
 
 def algorithmic_bytes(runs, m, k, n_out, idx_bytes=0):
