@@ -99,7 +99,7 @@ ARITH_NAMES = {1: "dot", 2: "mfma", 3: "wide"}
 class Workload:
     """Device inputs of one workload plus rotating weight copies."""
 
-    def __init__(self, name: str, m: int, torch, qgemv, synth, arith: int = 0):
+    def __init__(self, name: str, m: int, torch, qgemv, synth, arith: int = 0, pair=None):
         self.name, self.m = name, m
         self.torch, self.qgemv = torch, qgemv
         self.arith = arith
@@ -111,7 +111,21 @@ class Workload:
                     np.dtype(np.int32): np.int32}[a.dtype]
             return torch.from_numpy(a.view(view)).to(dev)
 
-        if name == "lmhead":
+        if name in ("single", "sweep"):
+            # the single 2048 x 2048 4/64 matrix, or one width/group pair of
+            # the 4096 x 4096 sweep
+            d = synth.single(m=m) if name == "single" else synth.sweep(pair[0], pair[1], m=m)
+            self.k = d["k"]
+            self.runs = [(d["bits"], d["group"], d["n"])]
+            self.n_out = d["n"]
+            self.desc = f"{name} N={d['n']} K={d['k']} {d['bits']}-bit group {d['group']}, {m}-row window"
+            base = [(t(d["words"]), t(d["scales"]), t(d["biases"]))]
+            self.x = t(d["x"])
+            self.y = torch.empty((m, d["n"]), dtype=torch.float32, device=dev)
+            self.idx_bytes = 0
+            self.kind = "plain"
+            self.cols = [0]
+        elif name == "lmhead":
             d = synth.lmhead(m=m)
             self.k = d["k"]
             self.runs = [(d["bits"], d["group"], d["n"])]
@@ -415,6 +429,18 @@ def main():
             rc2, mac2 = w2.counts()
             extra[key] = {"us_per_call": round(ms2 * 1e3, 3), "GB/s": round(g2, 1),
                           "rows_cols_per_s": round(rc2 / (ms2 * 1e-3), 1), "mnk_per_s": round(mac2 / (ms2 * 1e-3), 1),
+                          "frac": round(g2 / PEAK_GBS, 4), "bytes": w2.bytes}
+            print(f"# {key}: {ms2 * 1e3:.3f} us, {g2:.1f} GB/s", file=sys.stderr, flush=True)
+            del w2
+            torch.cuda.empty_cache()
+        # the configs reported but not targeted: the single matrix, and every
+        # width/group pair of the sweep at 1 and 16 rows (the library's choice)
+        for name, m, pair in [("single", 1, None)] + [("sweep", mm, pr) for pr in synth.PAIRS for mm in (1, 16)]:
+            w2 = Workload(name, m, torch, qgemv, synth, 0, pair)
+            ms2, _ = time_workload(w2, max(50, args.steps // 2), args.warmup, torch)
+            g2 = w2.bytes / (ms2 * 1e-3) / 1e9
+            key = f"{name}_m{m}" + (f"_b{pair[0]}g{pair[1]}" if pair else "") + f"_{w2.arith_used}"
+            extra[key] = {"us_per_call": round(ms2 * 1e3, 3), "GB/s": round(g2, 1),
                           "frac": round(g2 / PEAK_GBS, 4), "bytes": w2.bytes}
             print(f"# {key}: {ms2 * 1e3:.3f} us, {g2:.1f} GB/s", file=sys.stderr, flush=True)
             del w2
