@@ -10,6 +10,7 @@
 #include <memory>
 #include <mutex>
 #include <new>
+#include <utility>
 
 #include "qgemv.h"
 #include "qgemv_kernels.h"
@@ -722,6 +723,16 @@ int launch_stack(const qgemv_stack* s, bool mfma, const uint16_t* x, int32_t m, 
   for (int r = 0; r < s->n_runs; ++r)
     if ((s->run[r]->arith == QGEMV_ARITH_MFMA) == mfma) idx[nr++] = r;
   if (nr == 0) return QGEMV_OK;
+  // grid rows in order of a block's serial work (its wave's codes times
+  // their width), longest first: the hardware places blocks in launch order,
+  // so the blocks that bound the dispatch get CUs of their own when the
+  // runs together have more blocks than there are CUs
+  auto work = [&](int r) {
+    const qgemv_handle* h = s->run[r];
+    return (h->d.k / (h->arith == QGEMV_ARITH_DOT ? 1 : h->ksplit)) * h->d.bits;
+  };
+  for (int a = 1; a < nr; ++a)
+    for (int b = a; b > 0 && work(idx[b]) > work(idx[b - 1]); --b) std::swap(idx[b], idx[b - 1]);
   int var = window_variant(m);
   size_t lds = 0;
   if (mfma) {
@@ -809,9 +820,11 @@ int launch_stack(const qgemv_stack* s, bool mfma, const uint16_t* x, int32_t m, 
     s->occupancy[var][mfma].store(occ, std::memory_order_relaxed);
   }
   // blocks per run: every tile its own block when the CUs hold them all,
-  // else a share of the resident blocks in proportion to the run's tiles
+  // else a share of the resident blocks in proportion to the run's tiles.
+  // Grid row q holds run q's blocks; a row's blocks past its run's count
+  // leave at once.
   const int64_t cap = static_cast<int64_t>(dev->cus) * occ;
-  int64_t b0 = 0;
+  int64_t widest = 1;
   for (int q = 0; q < nr; ++q) {
     int64_t nb = tiles[q];
     if (total_tiles > cap) {
@@ -819,11 +832,11 @@ int launch_stack(const qgemv_stack* s, bool mfma, const uint16_t* x, int32_t m, 
       if (nb < 1) nb = 1;
       if (nb > tiles[q]) nb = tiles[q];
     }
-    sp.block0[q] = static_cast<int32_t>(b0);
-    b0 += nb;
+    sp.nblocks[q] = static_cast<int32_t>(nb);
+    if (nb > widest) widest = nb;
   }
-  sp.block0[nr] = static_cast<int32_t>(b0);
-  hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(b0)), dim3(threads), lds, static_cast<hipStream_t>(stream), sp);
+  hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(widest), static_cast<unsigned>(nr)), dim3(threads), lds,
+                     static_cast<hipStream_t>(stream), sp);
   return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_E_HIP;
 }
 

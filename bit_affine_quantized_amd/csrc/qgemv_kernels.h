@@ -37,6 +37,7 @@
 // explicit builtin.
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -624,7 +625,8 @@ __device__ __forceinline__ void load_groups_buf(__amdgpu_buffer_rsrc_t r, int of
 
 // Output column of weight row `row` under the call's column map.
 // (constant indices only, so a Params copy can live in registers)
-__device__ __forceinline__ int64_t mapped_column(const Params& p, int row) {
+template <class PT>
+__device__ __forceinline__ int64_t mapped_column(PT& p, int row) {
   int64_t d = p.seg_delta[0];
 #pragma unroll
   for (int sg = 1; sg < kMaxSeg; ++sg)
@@ -634,9 +636,11 @@ __device__ __forceinline__ int64_t mapped_column(const Params& p, int row) {
 
 // The fast row product for block bx of gx blocks (tiles bx, bx + gx, ...).
 // Shared arrays come from the calling kernel so that several bodies can be
-// inlined into one fused-stack kernel without their LDS adding up.
-template <int B, int G, int MB, bool STAGE>
-__device__ __forceinline__ void fast_body(const Params& p, const int bx, const int gx, unsigned char* smem,
+// inlined into one fused-stack kernel without their LDS adding up.  PT is
+// the kernel's own by-value Params, or a fused stack's run read in place in
+// the argument segment (KParams).
+template <int B, int G, int MB, bool STAGE, class PT>
+__device__ __forceinline__ void fast_body(PT& p, const int bx, const int gx, unsigned char* smem,
                                           int* s_list, int* s_wave_cnt, int* s_xrow, int64_t* s_yoff) {
   constexpr int PPC = Geo<B>::PPC, CPC = Geo<B>::CPC;
   constexpr int WPC = 4 * PPC;                      // words per chunk
@@ -1044,8 +1048,8 @@ __device__ __forceinline__ void transpose_rows(uint32_t* q) {
 // holds k-quarter q of all four units of the round; each unit is then one
 // 16x16x32 product over every window row at once (A row i = window row i),
 // and lane (j, q) folds window rows 4q .. 4q+3 of column j.
-template <int B, int G, int MB, bool WIDE = false>
-__device__ __forceinline__ void mfma_body(const Params& p, const int bx, const int gx, unsigned char* smem,
+template <int B, int G, int MB, bool WIDE = false, class PT = const Params>
+__device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, unsigned char* smem,
                                           int* s_wave_cnt, int* s_xrow, int64_t* s_yoff) {
   using MG = MGroup<B, G>;
   constexpr int R = MG::R, SSZ = MG::SSZ;
@@ -1531,40 +1535,33 @@ __global__ __launch_bounds__(MWaves<MB>::v * kWave) void qrow_mfma_wide(const Pa
 struct StackParams {
   Params run[kMaxRuns];
   int32_t kind[kMaxRuns];         // (bits index * 3 + group index) * 2 + staging
-  int32_t block0[kMaxRuns + 1];   // first block of each run; block0[nruns] = grid
+  int32_t nblocks[kMaxRuns];      // blocks of each run
   int32_t nruns;
 };
 
-// The block's run (blocks [block0[r], block0[r+1]) belong to run r), its
-// place among that run's blocks, its parameters and its kernel kind.  Written
-// out in each kernel (a macro, not a function taking the argument struct by
-// reference), and with constant indices only: either of the other forms
-// copies the whole argument struct to scratch.
-#define QG_SELECT_RUN(sp, p, bx, gx, kind)                                   \
-  do {                                                                       \
-    int r_ = 0, lo_ = (sp).block0[0], hi_ = (sp).block0[1];                  \
-    _Pragma("unroll") for (int q_ = 1; q_ < kMaxRuns; ++q_) if (             \
-        q_ < (sp).nruns && static_cast<int>(blockIdx.x) >= (sp).block0[q_]) { \
-      r_ = q_;                                                               \
-      lo_ = (sp).block0[q_];                                                 \
-      hi_ = (sp).block0[q_ + 1];                                             \
-    }                                                                        \
-    bx = static_cast<int>(blockIdx.x) - lo_;                                 \
-    gx = hi_ - lo_;                                                          \
-    switch (r_) {                                                            \
-      case 0: p = (sp).run[0]; break;                                        \
-      case 1: p = (sp).run[1]; break;                                        \
-      case 2: p = (sp).run[2]; break;                                        \
-      case 3: p = (sp).run[3]; break;                                        \
-      case 4: p = (sp).run[4]; break;                                        \
-      case 5: p = (sp).run[5]; break;                                        \
-      case 6: p = (sp).run[6]; break;                                        \
-      default: p = (sp).run[7]; break;                                       \
-    }                                                                        \
-    kind = (sp).kind[0];                                                     \
-    _Pragma("unroll") for (int q_ = 1; q_ < kMaxRuns; ++q_) if (q_ == r_) kind = (sp).kind[q_]; \
-  } while (0)
-static_assert(kMaxRuns == 8, "one case per run");
+// A fused stack's run read in place in the kernel's argument segment
+// (address space 4): loads through it are scalar loads at a uniform offset,
+// which the compiler issues where a field is used and may issue again
+// instead of holding the value, exactly as for a kernel's own by-value
+// Params.  (A Params copy selected at run time holds every field in scalar
+// registers from the start of the body; indexing the by-value StackParams
+// at run time copies all of it to scratch.)
+typedef const __attribute__((address_space(4))) Params KParams;
+typedef const __attribute__((address_space(4))) int32_t KInt;
+
+// The block's run is blockIdx.y (one grid row per run), its place among
+// that run's blocks blockIdx.x; a row's blocks past its run's block count
+// leave at once.  StackParams is the kernel's only argument, so it starts
+// the argument segment.
+#define QG_SELECT_RUN(p, bx, gx, kind)                                                          \
+  const char __attribute__((address_space(4)))* args_ =                                         \
+      (const char __attribute__((address_space(4)))*)(__builtin_amdgcn_kernarg_segment_ptr());  \
+  const int r_ = static_cast<int>(blockIdx.y);                                                  \
+  KParams& p = reinterpret_cast<KParams*>(args_ + offsetof(StackParams, run))[r_];              \
+  const int gx = reinterpret_cast<KInt*>(args_ + offsetof(StackParams, nblocks))[r_];           \
+  const int kind = reinterpret_cast<KInt*>(args_ + offsetof(StackParams, kind))[r_];            \
+  const int bx = static_cast<int>(blockIdx.x);                                                  \
+  if (bx >= gx) return
 
 // Dot-form runs: kind = (bits index * 3 + group index) * 2 + staging.
 template <int MB>
@@ -1574,9 +1571,8 @@ __global__ __launch_bounds__(kThreads) void qrow_stack(const StackParams sp) {
   __shared__ int s_wave_cnt[kWaves];
   __shared__ int s_xrow[QGEMV_MAX_WINDOW];
   __shared__ int64_t s_yoff[QGEMV_MAX_WINDOW];
-  Params p;
-  int bx, gx, kind;
-  QG_SELECT_RUN(sp, p, bx, gx, kind);
+  (void)sp;
+  QG_SELECT_RUN(p, bx, gx, kind);
 // (the empty asm keeps each case's parameter loads inside the case, so no
 // value is live across the switch)
 #define QG_BODY(B, G, STG)               \
@@ -1614,9 +1610,8 @@ __global__ __launch_bounds__(MWaves<MB>::v * kWave) void qrow_stack_mfma(const S
   __shared__ int s_wave_cnt[MWaves<MB>::v];
   __shared__ int s_xrow[QGEMV_MAX_WINDOW];
   __shared__ int64_t s_yoff[QGEMV_MAX_WINDOW];
-  Params p;
-  int bx, gx, kind;
-  QG_SELECT_RUN(sp, p, bx, gx, kind);
+  (void)sp;
+  QG_SELECT_RUN(p, bx, gx, kind);
 #define QG_BODY(B, G)                    \
   do {                                   \
     asm volatile("" ::: "memory");       \

