@@ -1437,7 +1437,27 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
 
   for (int c0 = 0; c0 < total; c0 += MB) {
     mcount = min(MB, total - c0);
-    // the first group's loads are in flight while the window is staged
+    // A thread's first staging item is loaded before the first group's
+    // weights, then the first group's loads are in flight while the window is
+    // staged.  A wave's loads complete in issue order, so the staging waits
+    // for its activations only, not for the weights behind them.
+    const int nstage = mcount * units;
+    uint32_t xfirst[16];
+    if (tid < nstage) {
+      const int mi = tid / units, un = tid - (tid / units) * units;
+      const int e = c0 + mi;
+      const int row = p.indexed ? s_list[e] / p.slots : e;
+      const u32x4* src = reinterpret_cast<const u32x4*>(p.x + static_cast<int64_t>(row) * p.k +
+                                                        static_cast<int64_t>(un) * 32);
+#pragma unroll
+      for (int pc = 0; pc < 4; ++pc) {
+        const u32x4 v = src[pc];
+        xfirst[4 * pc] = v.x;
+        xfirst[4 * pc + 1] = v.y;
+        xfirst[4 * pc + 2] = v.z;
+        xfirst[4 * pc + 3] = v.w;
+      }
+    }
     Cursor cl = {0, 0, gr0}, cc = {0, 0, gr0};
     Stage sa, sb;
     load_stage(sa, cl);
@@ -1458,18 +1478,23 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
     set_bases();
     __syncthreads();
     // ---- stage the window: each unit's activations in slot order, and its sum ----
-    for (int t = tid; t < mcount * units; t += NT) {
+    for (int t = tid; t < nstage; t += NT) {
       const int mi = t / units, un = t - (t / units) * units;
-      const u32x4* src = reinterpret_cast<const u32x4*>(p.x + static_cast<int64_t>(s_xrow[mi]) * p.k +
-                                                        static_cast<int64_t>(un) * 32);
       uint32_t xin[16];
+      if (t == tid) {
 #pragma unroll
-      for (int pc = 0; pc < 4; ++pc) {
-        const u32x4 v = src[pc];
-        xin[4 * pc] = v.x;
-        xin[4 * pc + 1] = v.y;
-        xin[4 * pc + 2] = v.z;
-        xin[4 * pc + 3] = v.w;
+        for (int q = 0; q < 16; ++q) xin[q] = xfirst[q];
+      } else {
+        const u32x4* src = reinterpret_cast<const u32x4*>(p.x + static_cast<int64_t>(s_xrow[mi]) * p.k +
+                                                          static_cast<int64_t>(un) * 32);
+#pragma unroll
+        for (int pc = 0; pc < 4; ++pc) {
+          const u32x4 v = src[pc];
+          xin[4 * pc] = v.x;
+          xin[4 * pc + 1] = v.y;
+          xin[4 * pc + 2] = v.z;
+          xin[4 * pc + 3] = v.w;
+        }
       }
       float X = 0.0f;
       const uint32_t ones = 0x3f803f80u;  // bf16 pair {1, 1}
