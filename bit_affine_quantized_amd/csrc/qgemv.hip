@@ -116,8 +116,8 @@ struct qgemv_handle {
   const qg::Entry* entry;
   const qg::WideEntry* wide;
   // resident blocks per CU of each (window variant, staging) kernel, 0 =
-  // not yet known; a benign cache: every thread that fills it writes the
-  // same value
+  // not yet known (matrix-core forms: [variant][0] plain, [variant][1] gate/up
+  // pairs); a benign cache: every thread that fills it writes the same value
   mutable std::atomic<int> occupancy[5][2];
 };
 
@@ -158,7 +158,8 @@ void init_device(DeviceInfo* info) {
                                         hipFuncAttributeMaxDynamicSharedMemorySize,
                                         static_cast<int>(qg::kMaxDynamicLds)) != hipSuccess)
             return;
-        for (qg::KernelFn fn : {e.mfma[v], qg::wide_entry(bi, gi).k[v]})
+        const qg::WideEntry& we = qg::wide_entry(bi, gi);
+        for (qg::KernelFn fn : {e.mfma[v], e.mfma_gateup[v], we.k[v], we.gateup[v]})
           if (hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
                                   static_cast<int>(qg::kMaxMfmaLds)) != hipSuccess)
             return;
@@ -276,7 +277,11 @@ int launch(const qgemv_handle* h, const uint16_t* x, int32_t m, float* y, int64_
   int64_t tile_rows = 0;
   if (mfma) {
     // one wave per 16 output columns
-    fn = h->arith == QGEMV_ARITH_WIDE ? h->wide->k[var] : h->entry->mfma[var];
+    // gate/up pairs run their own kernels, with the pairing compiled in
+    if (h->arith == QGEMV_ARITH_WIDE)
+      fn = up ? h->wide->gateup[var] : h->wide->k[var];
+    else
+      fn = up ? h->entry->mfma_gateup[var] : h->entry->mfma[var];
     threads = h->entry->mfma_waves[var] * qg::kWave;
     tile_rows = static_cast<int64_t>(h->entry->mfma_waves[var] / h->ksplit) * (up ? 8 : 16);
   } else {
@@ -321,14 +326,17 @@ int launch(const qgemv_handle* h, const uint16_t* x, int32_t m, float* y, int64_
   // A persistent grid: as many blocks as the CUs hold at once, each walking
   // its tiles with the staged window reused (grid size never changes bits:
   // a column's lanes and their arithmetic do not depend on its block).
-  int occ = h->occupancy[var][stage].load(std::memory_order_relaxed);
+  // (the matrix-core kernels always take staging 0: their slot 1 holds the
+  // gate/up kernel's occupancy)
+  const int oslot = mfma ? (up ? 1 : 0) : stage;
+  int occ = h->occupancy[var][oslot].load(std::memory_order_relaxed);
   if (occ == 0) {
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(fn), threads,
                                                      lds) != hipSuccess || nb < 1)
       nb = 1;
     occ = nb;
-    h->occupancy[var][stage].store(occ, std::memory_order_relaxed);
+    h->occupancy[var][oslot].store(occ, std::memory_order_relaxed);
   }
   int64_t blocks = tiles;
   const int64_t cap = static_cast<int64_t>(dev->cus) * occ;

@@ -229,7 +229,8 @@ struct Params {
   int32_t vec_groups;       // scales/biases aligned for packed loads
   int32_t ksplit;           // matrix-core form: K-parts per column (1, 2 or 4)
   // gate/up pair (matrix-core form): y = silu(gate row) * (up row), the up
-  // matrix at w2/scales2/biases2 with the gate's shape
+  // matrix at w2/scales2/biases2 with the gate's shape; set for the gate/up
+  // kernels only, which have the pairing compiled in
   int32_t gateup;
   const uint32_t* w2;
   const uint16_t* scales2;
@@ -1048,7 +1049,7 @@ __device__ __forceinline__ void transpose_rows(uint32_t* q) {
 // holds k-quarter q of all four units of the round; each unit is then one
 // 16x16x32 product over every window row at once (A row i = window row i),
 // and lane (j, q) folds window rows 4q .. 4q+3 of column j.
-template <int B, int G, int MB, bool WIDE = false, class PT = const Params>
+template <int B, int G, int MB, bool WIDE = false, bool GU = false, class PT = const Params>
 __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, unsigned char* smem,
                                           int* s_wave_cnt, int* s_xrow, int64_t* s_yoff) {
   using MG = MGroup<B, G>;
@@ -1103,7 +1104,9 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
   const unsigned char* wexp = reinterpret_cast<const unsigned char*>(p.w) + static_cast<int64_t>(expert) * p.n * row_bytes;
   const unsigned char* sexp = reinterpret_cast<const unsigned char*>(p.scales) + static_cast<int64_t>(expert) * p.n * gpr2;
   const unsigned char* bexp = reinterpret_cast<const unsigned char*>(p.biases) + static_cast<int64_t>(expert) * p.n * gpr2;
-  const bool gu = p.gateup != 0;
+  // gate/up pairing is compiled in or out: as a run-time flag its pointers
+  // and descriptors held scalar registers in every kernel
+  constexpr bool gu = GU;
   const int cw = gu ? 8 : 16;                 // output columns per column group
   const unsigned char* wexp2 = gu ? reinterpret_cast<const unsigned char*>(p.w2) + static_cast<int64_t>(expert) * p.n * row_bytes : wexp;
   const unsigned char* sexp2 = gu ? reinterpret_cast<const unsigned char*>(p.scales2) + static_cast<int64_t>(expert) * p.n * gpr2 : sexp;
@@ -1550,6 +1553,26 @@ __global__ __launch_bounds__(MWaves<MB>::v * kWave) void qrow_mfma_wide(const Pa
   mfma_body<B, G, MB, true>(p, blockIdx.x, gridDim.x, smem, s_wave_cnt, s_xrow, s_yoff);
 }
 
+// Gate/up pairs (both matrix-core forms): the same bodies with the pairing
+// compiled in.
+template <int B, int G, int MB>
+__global__ __launch_bounds__(MWaves<MB>::v * kWave) void qrow_mfma_gateup(const Params p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int s_wave_cnt[MWaves<MB>::v];
+  __shared__ int s_xrow[QGEMV_MAX_WINDOW];
+  __shared__ int64_t s_yoff[QGEMV_MAX_WINDOW];
+  mfma_body<B, G, MB, false, true>(p, blockIdx.x, gridDim.x, smem, s_wave_cnt, s_xrow, s_yoff);
+}
+
+template <int B, int G, int MB>
+__global__ __launch_bounds__(MWaves<MB>::v * kWave) void qrow_mfma_wide_gateup(const Params p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int s_wave_cnt[MWaves<MB>::v];
+  __shared__ int s_xrow[QGEMV_MAX_WINDOW];
+  __shared__ int64_t s_yoff[QGEMV_MAX_WINDOW];
+  mfma_body<B, G, MB, true, true>(p, blockIdx.x, gridDim.x, smem, s_wave_cnt, s_xrow, s_yoff);
+}
+
 // ---------------------------------------------------------------------------
 // Fused stack: the runs of a fused projection (each a matrix of one width and
 // group whose members write their own output columns) in one dispatch.  The
@@ -1701,6 +1724,7 @@ struct Entry {
   int fast_rows[5];     // columns per lane of the fast kernels
   int generic_rows[5];
   KernelFn mfma[5];     // matrix-core kernels by window variant
+  KernelFn mfma_gateup[5];  // the same for gate/up pairs
   int mfma_slot;        // bytes of one wave's LDS slot (one load group)
   int mfma_waves[5];    // waves per block of the matrix-core kernels by window variant
   int mfma_group;       // 128-code rounds per load group (k is a multiple of 128 * this)
@@ -1742,6 +1766,11 @@ Entry make_entry() {
   e.mfma[2] = qrow_mfma<B, G, 4>;
   e.mfma[3] = qrow_mfma<B, G, 8>;
   e.mfma[4] = qrow_mfma<B, G, 16>;
+  e.mfma_gateup[0] = qrow_mfma_gateup<B, G, 1>;
+  e.mfma_gateup[1] = qrow_mfma_gateup<B, G, 2>;
+  e.mfma_gateup[2] = qrow_mfma_gateup<B, G, 4>;
+  e.mfma_gateup[3] = qrow_mfma_gateup<B, G, 8>;
+  e.mfma_gateup[4] = qrow_mfma_gateup<B, G, 16>;
   e.mfma_slot = MGroup<B, G>::SLOT;
   e.mfma_group = MGroup<B, G>::R;
   e.mfma_waves[0] = MWaves<1>::v;
@@ -1756,6 +1785,7 @@ Entry make_entry() {
 // The wide-window matrix-core kernels of one (bits, group) by window variant.
 struct WideEntry {
   KernelFn k[5];
+  KernelFn gateup[5];   // gate/up pairs
 };
 
 template <int B, int G>
@@ -1766,6 +1796,11 @@ WideEntry make_wide_entry() {
   e.k[2] = qrow_mfma_wide<B, G, 4>;
   e.k[3] = qrow_mfma_wide<B, G, 8>;
   e.k[4] = qrow_mfma_wide<B, G, 16>;
+  e.gateup[0] = qrow_mfma_wide_gateup<B, G, 1>;
+  e.gateup[1] = qrow_mfma_wide_gateup<B, G, 2>;
+  e.gateup[2] = qrow_mfma_wide_gateup<B, G, 4>;
+  e.gateup[3] = qrow_mfma_wide_gateup<B, G, 8>;
+  e.gateup[4] = qrow_mfma_wide_gateup<B, G, 16>;
   return e;
 }
 
