@@ -159,9 +159,11 @@ void init_device(DeviceInfo* info) {
                                         static_cast<int>(qg::kMaxDynamicLds)) != hipSuccess)
             return;
         const qg::WideEntry& we = qg::wide_entry(bi, gi);
-        for (qg::KernelFn fn : {e.mfma[v], e.mfma_gateup[v], we.k[v], we.gateup[v]})
-          if (hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  static_cast<int>(qg::kMaxMfmaLds)) != hipSuccess)
+        for (qg::KernelFn fn : {e.mfma[v], e.mfma_gateup[v], we.k[v], we.gateup[v],
+                                v < 3 ? e.mfma_indexed[v] : nullptr, v < 3 ? e.mfma_gateup_indexed[v] : nullptr,
+                                v < 3 ? we.indexed[v] : nullptr, v < 3 ? we.gateup_indexed[v] : nullptr})
+          if (fn && hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                        static_cast<int>(qg::kMaxMfmaLds)) != hipSuccess)
             return;
       }
     }
@@ -277,11 +279,17 @@ int launch(const qgemv_handle* h, const uint16_t* x, int32_t m, float* y, int64_
   int64_t tile_rows = 0;
   if (mfma) {
     // one wave per 16 output columns
-    // gate/up pairs run their own kernels, with the pairing compiled in
-    if (h->arith == QGEMV_ARITH_WIDE)
-      fn = up ? h->wide->gateup[var] : h->wide->k[var];
-    else
-      fn = up ? h->entry->mfma_gateup[var] : h->entry->mfma[var];
+    // gate/up pairs and indexed calls run kernels of their own, with the
+    // pairing and the routing compiled in
+    const bool wide = h->arith == QGEMV_ARITH_WIDE;
+    if (indexed) {
+      if (var > 2) return QGEMV_E_WINDOW;   // routed windows have at most kIndexedWindow rows
+      fn = wide ? (up ? h->wide->gateup_indexed[var] : h->wide->indexed[var])
+                : (up ? h->entry->mfma_gateup_indexed[var] : h->entry->mfma_indexed[var]);
+    } else {
+      fn = wide ? (up ? h->wide->gateup[var] : h->wide->k[var])
+                : (up ? h->entry->mfma_gateup[var] : h->entry->mfma[var]);
+    }
     threads = h->entry->mfma_waves[var] * qg::kWave;
     tile_rows = static_cast<int64_t>(h->entry->mfma_waves[var] / h->ksplit) * (up ? 8 : 16);
   } else {
@@ -327,22 +335,24 @@ int launch(const qgemv_handle* h, const uint16_t* x, int32_t m, float* y, int64_
   // its tiles with the staged window reused (grid size never changes bits:
   // a column's lanes and their arithmetic do not depend on its block).
   // (the matrix-core kernels always take staging 0: their slot 1 holds the
-  // gate/up kernel's occupancy)
-  const int oslot = mfma ? (up ? 1 : 0) : stage;
-  int occ = h->occupancy[var][oslot].load(std::memory_order_relaxed);
-  if (occ == 0) {
-    int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(fn), threads,
-                                                     lds) != hipSuccess || nb < 1)
-      nb = 1;
-    occ = nb;
-    h->occupancy[var][oslot].store(occ, std::memory_order_relaxed);
-  }
-  int64_t blocks = tiles;
-  const int64_t cap = static_cast<int64_t>(dev->cus) * occ;
-  if (blocks > cap) blocks = cap;
-  dim3 grid(static_cast<unsigned>(blocks), 1u);
-  if (indexed) {
+  // gate/up kernel's occupancy; indexed calls size their grid per expert)
+  dim3 grid(1u, 1u);
+  if (!indexed) {
+    const int oslot = mfma ? (up ? 1 : 0) : stage;
+    int occ = h->occupancy[var][oslot].load(std::memory_order_relaxed);
+    if (occ == 0) {
+      int nb = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(fn), threads,
+                                                       lds) != hipSuccess || nb < 1)
+        nb = 1;
+      occ = nb;
+      h->occupancy[var][oslot].store(occ, std::memory_order_relaxed);
+    }
+    int64_t blocks = tiles;
+    const int64_t cap = static_cast<int64_t>(dev->cus) * occ;
+    if (blocks > cap) blocks = cap;
+    grid.x = static_cast<unsigned>(blocks);
+  } else {
     // blocks per expert: enough that the experts a call routes to (not known
     // on the host) keep every CU's waves streaming, few enough that each
     // block's routing and window staging serve several tiles.  Measured on

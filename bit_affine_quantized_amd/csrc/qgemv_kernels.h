@@ -1049,7 +1049,7 @@ __device__ __forceinline__ void transpose_rows(uint32_t* q) {
 // holds k-quarter q of all four units of the round; each unit is then one
 // 16x16x32 product over every window row at once (A row i = window row i),
 // and lane (j, q) folds window rows 4q .. 4q+3 of column j.
-template <int B, int G, int MB, bool WIDE = false, bool GU = false, class PT = const Params>
+template <int B, int G, int MB, bool WIDE = false, bool GU = false, bool IDX = false, class PT = const Params>
 __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, unsigned char* smem,
                                           int* s_wave_cnt, int* s_xrow, int64_t* s_yoff) {
   using MG = MGroup<B, G>;
@@ -1065,7 +1065,7 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
   const int S = p.ksplit;                   // K-parts per column
   const int gpp = units / (4 * R) / S;      // groups per K-part
   const int ncg = NW / S;                   // column groups (of 16 columns) per block
-  const int mrows = p.indexed ? MB : min(p.m, MB);       // window rows staged
+  const int mrows = IDX ? MB : min(p.m, MB);       // window rows staged
   const int xstride = units * 64 + 16;                     // bytes per staged row
   const int sstride = units + 4;                           // floats per row of unit sums
   // LDS: activations [mrows][units][32 slots] bf16, a zero area of one
@@ -1081,7 +1081,7 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
   unsigned char* zero_area = smem + static_cast<size_t>(mrows) * xstride;
   float* xsum = reinterpret_cast<float*>(zero_area + ZB);
   int* s_list = reinterpret_cast<int*>(xsum + static_cast<size_t>(mrows) * sstride);
-  unsigned char* slots = reinterpret_cast<unsigned char*>(s_list + (p.indexed ? kMaxList : 0));
+  unsigned char* slots = reinterpret_cast<unsigned char*>(s_list + (IDX ? kMaxList : 0));
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -1093,7 +1093,7 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
 
   int expert = 0;
   int total = p.m;
-  if (p.indexed) {
+  if (IDX) {
     expert = blockIdx.y;
     total = build_route_list<NT>(p.idx, p.m * p.slots, expert, s_list, s_wave_cnt);
     if (total == 0) return;
@@ -1449,7 +1449,7 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
     if (tid < nstage) {
       const int mi = tid / units, un = tid - (tid / units) * units;
       const int e = c0 + mi;
-      const int row = p.indexed ? s_list[e] / p.slots : e;
+      const int row = IDX ? s_list[e] / p.slots : e;
       const u32x4* src = reinterpret_cast<const u32x4*>(p.x + static_cast<int64_t>(row) * p.k +
                                                         static_cast<int64_t>(un) * 32);
 #pragma unroll
@@ -1467,7 +1467,7 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
     advance(cl);
     if (tid < mcount) {
       const int e = c0 + tid;
-      if (p.indexed) {
+      if (IDX) {
         const int t = s_list[e];
         const int row = t / p.slots, sl = t % p.slots;
         s_xrow[tid] = row;
@@ -1535,43 +1535,28 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
   }
 }
 
-template <int B, int G, int MB>
-__global__ __launch_bounds__(MWaves<MB>::v * kWave) void qrow_mfma(const Params p) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ int s_wave_cnt[MWaves<MB>::v];
-  __shared__ int s_xrow[QGEMV_MAX_WINDOW];
-  __shared__ int64_t s_yoff[QGEMV_MAX_WINDOW];
-  mfma_body<B, G, MB>(p, blockIdx.x, gridDim.x, smem, s_wave_cnt, s_xrow, s_yoff);
-}
-
-template <int B, int G, int MB>
-__global__ __launch_bounds__(MWaves<MB>::v * kWave) void qrow_mfma_wide(const Params p) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ int s_wave_cnt[MWaves<MB>::v];
-  __shared__ int s_xrow[QGEMV_MAX_WINDOW];
-  __shared__ int64_t s_yoff[QGEMV_MAX_WINDOW];
-  mfma_body<B, G, MB, true>(p, blockIdx.x, gridDim.x, smem, s_wave_cnt, s_xrow, s_yoff);
-}
-
-// Gate/up pairs (both matrix-core forms): the same bodies with the pairing
-// compiled in.
-template <int B, int G, int MB>
-__global__ __launch_bounds__(MWaves<MB>::v * kWave) void qrow_mfma_gateup(const Params p) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ int s_wave_cnt[MWaves<MB>::v];
-  __shared__ int s_xrow[QGEMV_MAX_WINDOW];
-  __shared__ int64_t s_yoff[QGEMV_MAX_WINDOW];
-  mfma_body<B, G, MB, false, true>(p, blockIdx.x, gridDim.x, smem, s_wave_cnt, s_xrow, s_yoff);
-}
-
-template <int B, int G, int MB>
-__global__ __launch_bounds__(MWaves<MB>::v * kWave) void qrow_mfma_wide_gateup(const Params p) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ int s_wave_cnt[MWaves<MB>::v];
-  __shared__ int s_xrow[QGEMV_MAX_WINDOW];
-  __shared__ int64_t s_yoff[QGEMV_MAX_WINDOW];
-  mfma_body<B, G, MB, true, true>(p, blockIdx.x, gridDim.x, smem, s_wave_cnt, s_xrow, s_yoff);
-}
+// The matrix-core kernels: the block-diagonal and wide forms, plain or
+// gate/up pairs, plain/strided or indexed calls.  Pairing and routing are
+// compiled in or out, so no kernel holds the registers of a path it never
+// takes.  Indexed calls stage at most kIndexedWindow routed rows a pass.
+#define QG_MFMA_KERNEL(NAME, WIDE, GU, IDX)                                                  \
+  template <int B, int G, int MB>                                                            \
+  __global__ __launch_bounds__(MWaves<MB>::v * kWave) void NAME(const Params p) {            \
+    extern __shared__ __align__(16) unsigned char smem[];                                    \
+    __shared__ int s_wave_cnt[MWaves<MB>::v];                                                \
+    __shared__ int s_xrow[QGEMV_MAX_WINDOW];                                                 \
+    __shared__ int64_t s_yoff[QGEMV_MAX_WINDOW];                                             \
+    mfma_body<B, G, MB, WIDE, GU, IDX>(p, blockIdx.x, gridDim.x, smem, s_wave_cnt, s_xrow, s_yoff); \
+  }
+QG_MFMA_KERNEL(qrow_mfma, false, false, false)
+QG_MFMA_KERNEL(qrow_mfma_wide, true, false, false)
+QG_MFMA_KERNEL(qrow_mfma_gateup, false, true, false)
+QG_MFMA_KERNEL(qrow_mfma_wide_gateup, true, true, false)
+QG_MFMA_KERNEL(qrow_mfma_indexed, false, false, true)
+QG_MFMA_KERNEL(qrow_mfma_wide_indexed, true, false, true)
+QG_MFMA_KERNEL(qrow_mfma_gateup_indexed, false, true, true)
+QG_MFMA_KERNEL(qrow_mfma_wide_gateup_indexed, true, true, true)
+#undef QG_MFMA_KERNEL
 
 // ---------------------------------------------------------------------------
 // Fused stack: the runs of a fused projection (each a matrix of one width and
@@ -1717,6 +1702,7 @@ constexpr int kBits[6] = {2, 3, 4, 5, 6, 8};
 constexpr int kGroups[3] = {32, 64, 128};
 constexpr int kWindows[5] = {1, 2, 4, 8, 16};
 constexpr int kIndexedWindow = 4;  // routed rows staged per pass
+static_assert(kIndexedWindow == 4, "indexed matrix-core kernels exist for 1, 2 and 4 rows");
 
 struct Entry {
   KernelFn fast[5][2];  // by window variant and staging (0: direct loads, 1: LDS hand-off)
@@ -1725,6 +1711,8 @@ struct Entry {
   int generic_rows[5];
   KernelFn mfma[5];     // matrix-core kernels by window variant
   KernelFn mfma_gateup[5];  // the same for gate/up pairs
+  KernelFn mfma_indexed[3];         // indexed calls (windows of 1, 2 and 4 routed rows)
+  KernelFn mfma_gateup_indexed[3];  // indexed gate/up pairs
   int mfma_slot;        // bytes of one wave's LDS slot (one load group)
   int mfma_waves[5];    // waves per block of the matrix-core kernels by window variant
   int mfma_group;       // 128-code rounds per load group (k is a multiple of 128 * this)
@@ -1771,6 +1759,12 @@ Entry make_entry() {
   e.mfma_gateup[2] = qrow_mfma_gateup<B, G, 4>;
   e.mfma_gateup[3] = qrow_mfma_gateup<B, G, 8>;
   e.mfma_gateup[4] = qrow_mfma_gateup<B, G, 16>;
+  e.mfma_indexed[0] = qrow_mfma_indexed<B, G, 1>;
+  e.mfma_indexed[1] = qrow_mfma_indexed<B, G, 2>;
+  e.mfma_indexed[2] = qrow_mfma_indexed<B, G, 4>;
+  e.mfma_gateup_indexed[0] = qrow_mfma_gateup_indexed<B, G, 1>;
+  e.mfma_gateup_indexed[1] = qrow_mfma_gateup_indexed<B, G, 2>;
+  e.mfma_gateup_indexed[2] = qrow_mfma_gateup_indexed<B, G, 4>;
   e.mfma_slot = MGroup<B, G>::SLOT;
   e.mfma_group = MGroup<B, G>::R;
   e.mfma_waves[0] = MWaves<1>::v;
@@ -1786,6 +1780,8 @@ Entry make_entry() {
 struct WideEntry {
   KernelFn k[5];
   KernelFn gateup[5];   // gate/up pairs
+  KernelFn indexed[3];  // indexed calls (windows of 1, 2 and 4 routed rows)
+  KernelFn gateup_indexed[3];
 };
 
 template <int B, int G>
@@ -1801,6 +1797,12 @@ WideEntry make_wide_entry() {
   e.gateup[2] = qrow_mfma_wide_gateup<B, G, 4>;
   e.gateup[3] = qrow_mfma_wide_gateup<B, G, 8>;
   e.gateup[4] = qrow_mfma_wide_gateup<B, G, 16>;
+  e.indexed[0] = qrow_mfma_wide_indexed<B, G, 1>;
+  e.indexed[1] = qrow_mfma_wide_indexed<B, G, 2>;
+  e.indexed[2] = qrow_mfma_wide_indexed<B, G, 4>;
+  e.gateup_indexed[0] = qrow_mfma_wide_gateup_indexed<B, G, 1>;
+  e.gateup_indexed[1] = qrow_mfma_wide_gateup_indexed<B, G, 2>;
+  e.gateup_indexed[2] = qrow_mfma_wide_gateup_indexed<B, G, 4>;
   return e;
 }
 
