@@ -275,6 +275,38 @@ def test_gateup_indexed_and_refusals(arith):
     assert qgemv.qgemv_run_gateup(vg0.h, narrow.h, xt, 1, y1, n) == qgemv.QGEMV_E_SHAPE
 
 
+@mc_param
+@pytest.mark.parametrize("k", [20480, 40960])
+def test_indexed_narrow_windows_at_large_k(k, arith):
+    """At K = 20480 four staged routed rows no longer fit one block's LDS, so
+    indexed calls stage 2 rows a pass, and at K = 40960 one: the indexed
+    kernels of those windows, each expert taking several passes.  Every (row,
+    slot), plain and as a gate/up pair, equals the call on that expert's own
+    handles bit for bit."""
+    print_case("indexed large k", k, arith)
+    bits, group, n, e = 4, 64, 40, 3
+    dg, du = _gateup_pair(bits, group, n, k, 5, 7900 + k // 1024, n_experts=e)
+    idx = np.array([[0, 2], [1, 1], [2, 0], [1, 2], [0, 0]], dtype=np.int32)
+    tg = [dev(dg[key]) for key in ("words", "scales", "biases")]
+    tu = [dev(du[key]) for key in ("words", "scales", "biases")]
+    gate = qgemv.Matrix(bits, group, n, k, *tg, n_experts=e, arith=arith)
+    up = qgemv.Matrix(bits, group, n, k, *tu, n_experts=e, arith=arith)
+    xt = dev(dg["x"])
+    ti = dev(idx)
+    y = torch.empty((5, 2, n), dtype=torch.float32, device=DEV)
+    yp = torch.empty((5, 2, n), dtype=torch.float32, device=DEV)
+    gate.run_indexed(xt, ti, y.view(-1))
+    assert qgemv.qgemv_run_gateup_indexed(gate.h, up.h, xt, 5, ti, 2, yp.view(-1)) == qgemv.QGEMV_OK
+    y1 = torch.empty((1, n), dtype=torch.float32, device=DEV)
+    for ex in range(e):
+        vg = qgemv.Matrix(bits, group, n, k, tg[0][ex], tg[1][ex], tg[2][ex], arith=arith)
+        vu = qgemv.Matrix(bits, group, n, k, tu[0][ex], tu[1][ex], tu[2][ex], arith=arith)
+        for i, s_ in zip(*np.nonzero(idx == ex)):
+            assert bits_equal(run(vg, xt[i:i + 1])[0], y[i, s_]), (ex, i, s_)
+            assert qgemv.qgemv_run_gateup(vg.h, vu.h, xt[i:i + 1], 1, y1, n) == qgemv.QGEMV_OK
+            assert bits_equal(y1[0], yp[i, s_]), (ex, i, s_)
+
+
 def _dequant64(words, scales, biases, bits, group, n, k):
     q = oracle.unpack(words, bits, n, k).astype(np.float64)
     s = synth.bf16_bits_to_f32(scales).astype(np.float64)
