@@ -776,3 +776,78 @@ def test_random_shapes(bits, group, n, k, m, arith, seed):
     gap = torch.ones((m, ldy), dtype=torch.bool, device=DEV)
     gap[:, 1:1 + n] = False
     assert torch.equal(ys.view(torch.int32)[gap], sentinel[gap])
+
+
+# ---------------------------------------------------------------------------
+# HIP graph capture: launch-bound callers replay captured calls
+# ---------------------------------------------------------------------------
+
+def test_graph_replay_equals_eager():
+    """Plain, strided, fused-stack and indexed (relu2) calls captured in one
+    HIP graph and replayed three times, with eager calls and output resets
+    between the replays: every replay's outputs equal the eager calls' bit for
+    bit, and the strided call's gaps keep their bytes (the library records no
+    memset or host work into a graph)."""
+    print_case("graph replay")
+    k = 2048
+    d1 = synth.matrix(8100, 6, 32, 1000, k, 3)
+    plain = matrix_of(d1)
+    x1 = dev(d1["x"])
+    d2 = synth.matrix(8101, 4, 64, 256, k)
+    strided = matrix_of(d2)
+    ldy = 300
+    specs = [(4, 64, [(256, 0)]), (5, 128, [(192, 256), (8, 500)]), (6, 64, [(48, 448)])]
+    runs, _ = _stack_runs(specs, k, 8102)
+    stack = qgemv.Stack(runs, 512)
+    bits, group, n, ke, e = 3, 64, 300, 1024, 6
+    d3 = synth.matrix(8103, bits, group, n, ke, 9, n_experts=e)
+    experts = qgemv.Matrix(bits, group, n, ke, dev(d3["words"]), dev(d3["scales"]), dev(d3["biases"]),
+                           n_experts=e)
+    x3 = dev(d3["x"])
+    idx = dev(np.array([[1, 1, 2], [1, 0, 5], [1, 3, 3], [1, 2, 0], [1, 4, 4],
+                        [1, 5, 1], [0, 0, 0], [2, 1, 4], [3, 3, 1]], dtype=np.int32))
+    sentinel = torch.full((3, ldy), 0x7FC0BEEF, dtype=torch.int32, device=DEV)
+    gap = torch.ones((3, ldy), dtype=torch.bool, device=DEV)
+    gap[:, 10:10 + 256] = False
+
+    def outputs():
+        return (torch.empty((3, 1000), dtype=torch.float32, device=DEV),
+                sentinel.clone().view(torch.float32),
+                torch.zeros((3, 512), dtype=torch.float32, device=DEV),
+                torch.empty((9, 3, n), dtype=torch.float32, device=DEV))
+
+    def launch(outs, s):
+        yp, ys, yk, yi = outs
+        assert qgemv.qgemv_run(plain.h, x1, 3, yp, 0, s) == qgemv.QGEMV_OK
+        assert qgemv.qgemv_run_strided(strided.h, x1, 3, ys.view(-1)[10:], ldy, 0, s) == qgemv.QGEMV_OK
+        assert qgemv.qgemv_stack_run(stack.h, x1, 3, yk, 0, s) == qgemv.QGEMV_OK
+        assert qgemv.qgemv_run_indexed(experts.h, x3, 9, idx, 3, yi.view(-1), qgemv.QGEMV_EPI_RELU2, s) \
+            == qgemv.QGEMV_OK
+
+    eager = outputs()
+    launch(eager, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    graphed = outputs()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        launch(graphed, side.cuda_stream)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        launch(graphed, torch.cuda.current_stream().cuda_stream)
+    other = outputs()
+    for rep in range(3):
+        # back to each output's initial bytes (the stack's output starts at
+        # zero, so its unwritten columns are checked too)
+        graphed[0].view(torch.int32).fill_(0x7FC0BEEF)
+        graphed[1].view(torch.int32).copy_(sentinel)
+        graphed[2].zero_()
+        graphed[3].view(torch.int32).fill_(0x7FC0BEEF)
+        launch(other, torch.cuda.current_stream().cuda_stream)   # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(eager, graphed):
+            assert bits_equal(a, b), rep
+        assert torch.equal(graphed[1].view(torch.int32)[gap], sentinel[gap]), rep
