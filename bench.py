@@ -283,6 +283,37 @@ def time_workload(wl: Workload, steps: int, warmup: int, torch):
     return ms, batches
 
 
+def time_workload_graph(wl: Workload, steps: int, warmup: int, torch) -> float:
+    """The same K steps captured once in a HIP graph and replayed: the device
+    time per step without the host's issue cost, which is what a caller that
+    captures its launch-bound calls sees.  Warmup steps run eagerly first,
+    then one untimed replay; returns ms per step of one timed replay."""
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        wl.step(i, stream.cuda_stream)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        for i in range(3):
+            wl.step(warmup + i, side.cuda_stream)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sid = torch.cuda.current_stream().cuda_stream
+        for i in range(steps):
+            wl.step(warmup + i, sid)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def launch_floor(torch, kernels: int = 200, replays: int = 20) -> float:
     """Device-side interval between back-to-back trivial kernels (one-element
     adds), in microseconds: a captured graph of `kernels` launches is replayed
@@ -355,6 +386,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--arith", default="auto", choices=["auto", "dot", "mfma", "wide"],
                     help="arithmetic of the handles (the fused stack always uses the library's choice)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the main workload's K steps as one captured HIP graph replay")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (known bytes) for counter scaling")
     args = ap.parse_args()
@@ -383,6 +416,10 @@ def main():
     arith = {"auto": 0, "dot": 1, "mfma": 2, "wide": 3}[args.arith]
     wl = Workload(args.workload, args.m, torch, qgemv, synth, arith)
     ms, batches = time_workload(wl, args.steps, args.warmup, torch)
+    # the same steps as one captured graph: no host issue cost
+    ms_graph = time_workload_graph(wl, args.steps, 100, torch)
+    if args.graph:
+        ms, batches = ms_graph, [ms_graph]
     gbs = wl.bytes / (ms * 1e-3) / 1e9
     rows_cols, macs = wl.counts()
     traffic = read_traffic(f"{args.workload}_m{wl.m}")
@@ -394,6 +431,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 6),
+        "ms_per_step_graph": round(ms_graph, 6),
+        "timing": "HIP graph replay" if args.graph else "eager launches on one stream",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -425,12 +464,15 @@ def main():
                 del w2
                 continue
             ms2, _ = time_workload(w2, max(50, args.steps // 2), args.warmup, torch)
+            msg = time_workload_graph(w2, max(50, args.steps // 2), 100, torch)
             g2 = w2.bytes / (ms2 * 1e-3) / 1e9
             rc2, mac2 = w2.counts()
             extra[key] = {"us_per_call": round(ms2 * 1e3, 3), "GB/s": round(g2, 1),
                           "rows_cols_per_s": round(rc2 / (ms2 * 1e-3), 1), "mnk_per_s": round(mac2 / (ms2 * 1e-3), 1),
-                          "frac": round(g2 / PEAK_GBS, 4), "bytes": w2.bytes}
-            print(f"# {key}: {ms2 * 1e3:.3f} us, {g2:.1f} GB/s", file=sys.stderr, flush=True)
+                          "frac": round(g2 / PEAK_GBS, 4), "bytes": w2.bytes,
+                          "us_per_call_graph": round(msg * 1e3, 3),
+                          "frac_graph": round(w2.bytes / (msg * 1e-3) / 1e9 / PEAK_GBS, 4)}
+            print(f"# {key}: {ms2 * 1e3:.3f} us, {g2:.1f} GB/s; graph {msg * 1e3:.3f} us", file=sys.stderr, flush=True)
             del w2
             torch.cuda.empty_cache()
         # the configs reported but not targeted: the single matrix, and every
@@ -438,11 +480,14 @@ def main():
         for name, m, pair in [("single", 1, None)] + [("sweep", mm, pr) for pr in synth.PAIRS for mm in (1, 16)]:
             w2 = Workload(name, m, torch, qgemv, synth, 0, pair)
             ms2, _ = time_workload(w2, max(50, args.steps // 2), args.warmup, torch)
+            msg = time_workload_graph(w2, max(50, args.steps // 2), 100, torch)
             g2 = w2.bytes / (ms2 * 1e-3) / 1e9
             key = f"{name}_m{m}" + (f"_b{pair[0]}g{pair[1]}" if pair else "") + f"_{w2.arith_used}"
             extra[key] = {"us_per_call": round(ms2 * 1e3, 3), "GB/s": round(g2, 1),
-                          "frac": round(g2 / PEAK_GBS, 4), "bytes": w2.bytes}
-            print(f"# {key}: {ms2 * 1e3:.3f} us, {g2:.1f} GB/s", file=sys.stderr, flush=True)
+                          "frac": round(g2 / PEAK_GBS, 4), "bytes": w2.bytes,
+                          "us_per_call_graph": round(msg * 1e3, 3),
+                          "frac_graph": round(w2.bytes / (msg * 1e-3) / 1e9 / PEAK_GBS, 4)}
+            print(f"# {key}: {ms2 * 1e3:.3f} us, {g2:.1f} GB/s; graph {msg * 1e3:.3f} us", file=sys.stderr, flush=True)
             del w2
             torch.cuda.empty_cache()
         out["workloads"] = extra
