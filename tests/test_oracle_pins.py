@@ -135,6 +135,17 @@ def test_exact_rational_tiny(bits, group):
             bound = Fraction(k - 1) * Fraction(1, 2 ** 53) * mag
             assert abs(Fraction(y[i, r]) - exact) <= bound
             assert abs(Fraction(a[i, r]) - mag) <= bound
+            # the summed terms' magnitudes of the pages' bound (P788 commit
+            # "tf-affine-ref"): the scale part and the bias part of each
+            # product counted separately, sum |s*q*x| + |bias*x|
+            terms = Fraction(0)
+            for kk in range(k):
+                s = bf16_fraction(d["scales"][r, kk // group])
+                b = bf16_fraction(d["biases"][r, kk // group])
+                xv = bf16_fraction(d["x"][i, kk])
+                terms += abs(s * int(codes[r, kk]) * xv) + abs(b * xv)
+            tbound = Fraction(2 * k) * Fraction(1, 2 ** 53) * terms
+            assert abs(Fraction(t[i, r]) - terms) <= tbound
 
 
 @pytest.mark.parametrize("bits,group", [(2, 32), (3, 128), (5, 64), (6, 32), (8, 128)])
@@ -210,6 +221,41 @@ def test_terms_and_abs_relations():
     # row split over threads computes the same numbers
     y2, a2, t2 = oracle.gemv(d["words"], d["scales"], d["biases"], d["x"], bits, group, n, k, threads=3)
     assert np.array_equal(y, y2) and np.array_equal(a, a2) and np.array_equal(t, t2)
+
+
+@pytest.mark.parametrize("group", synth.GROUPS)
+def test_negative_control_scales_only(group):
+    """The 1%-off control of P788 commit "tf-affine-ref" perturbs the scales
+    and nothing else: with x = e_k, y_bad[n] is 101/100 * s * q + bias
+    (one-hot: the sum holds one product), within a few fp64 roundings of the
+    exact rational value, and exactly the bias where the code is 0."""
+    bits, n, k = 6, 6, 256
+    rng = np.random.default_rng(40 + group)
+    codes = rng.integers(0, 64, size=(n, k)).astype(np.uint8)
+    codes[:, ::7] = 0                                  # zero codes in every group
+    d = synth.matrix(50 + group, bits, group, n, k)
+    words = synth.pack_codes(codes, bits)
+    ks = sorted({e + o for e in range(0, k, group) for o in (0, 1, group - 1) if 0 <= e + o < k} | {7, 14})
+    x = np.zeros((len(ks), k))
+    for i, kk in enumerate(ks):
+        x[i, kk] = 1.0
+    yb, _, _ = oracle.gemv(words, d["scales"], d["biases"], synth.to_bf16_bits(x), bits, group, n, k,
+                           scale_mult=1.01)
+    zeros_seen = 0
+    for i, kk in enumerate(ks):
+        for r in range(n):
+            s = bf16_fraction(d["scales"][r, kk // group])
+            b = bf16_fraction(d["biases"][r, kk // group])
+            q = int(codes[r, kk])
+            want = Fraction(101, 100) * s * q + b
+            if q == 0:
+                zeros_seen += 1
+                assert Fraction(yb[i, r]) == b
+            else:
+                # s*1.01 rounded, times q rounded, plus bias rounded: <= 3 ulps
+                tol = Fraction(3, 2 ** 52) * (abs(Fraction(101, 100) * s * q) + abs(b))
+                assert abs(Fraction(yb[i, r]) - want) <= tol
+    assert zeros_seen >= n
 
 
 def test_negative_control_moves_outputs():
@@ -292,6 +338,9 @@ MUTANTS = {
                    "const uint8_t *row = base + (r % 2) * row_bytes;\n    for (int64_t kk = 0; kk < k; kk++) {"),
     "scale multiplier": (") * scale_mult;", ");"),
     "relu2 sign": ("v > 0.0 ? v * v", "v < 0.0 ? v * v"),
+    "terms as |w*x|": ("terms += fabs(sq[kk] * xv) + fabs(bb[kk] * xv);", "terms += fabs(prod);"),
+    "multiplier on the bias": ("const double b = bf16_value(biases[r * groups + g]);",
+                               "const double b = bf16_value(biases[r * groups + g]) * scale_mult;"),
 }
 
 
