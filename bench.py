@@ -38,8 +38,8 @@ LIB_DEFAULT = os.path.join(ROOT, "bit_affine_quantized_amd", "libqgemv.so")
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
-def _elf_section(data: bytes, wanted: str):
-    """Bytes of one section of a 64-bit little-endian ELF file, or None."""
+def _elf_section_range(data: bytes, wanted: str):
+    """(offset, size) of one section of a 64-bit little-endian ELF file, or None."""
     if data[:5] != b"\x7fELF\x02":
         return None
     shoff = struct.unpack_from("<Q", data, 0x28)[0]
@@ -49,19 +49,96 @@ def _elf_section(data: bytes, wanted: str):
     for name, _, _, _, off, size in heads:
         end = data.index(b"\0", names + name)
         if data[names + name:end].decode() == wanted:
-            return data[off:off + size]
+            return off, size
     return None
 
 
-def kernel_hash() -> str:
-    """Hash of the kernels' machine code in the library this run loads (its
-    .hip_fatbin section; the whole file if that is missing): a counter
-    summary applies to the run only when it was taken on the same kernels."""
-    path = os.environ.get("QGEMV_LIB") or LIB_DEFAULT
+def _elf_section(data: bytes, wanted: str):
+    """Bytes of one section of a 64-bit little-endian ELF file, or None."""
+    r = _elf_section_range(data, wanted)
+    return None if r is None else data[r[0]:r[0] + r[1]]
+
+
+BUNDLE_MAGIC = b"__CLANG_OFFLOAD_BUNDLE__"
+
+
+def code_objects(fatbin: bytes):
+    """The GPU code objects (ELF files) of a .hip_fatbin section: one clang
+    offload bundle per translation unit, each a header (magic, entry count,
+    then per entry its offset from the bundle start, size and target
+    triple) followed by its entries."""
+    out, pos = [], 0
+    while True:
+        start = fatbin.find(BUNDLE_MAGIC, pos)
+        if start < 0:
+            return out
+        count = struct.unpack_from("<Q", fatbin, start + len(BUNDLE_MAGIC))[0]
+        p = start + len(BUNDLE_MAGIC) + 8
+        end = p
+        for _ in range(count):
+            off, size, tlen = struct.unpack_from("<QQQ", fatbin, p)
+            triple = fatbin[p + 24:p + 24 + tlen].decode(errors="replace")
+            p += 24 + tlen
+            if "amdgcn" in triple and size:
+                out.append(fatbin[start + off:start + off + size])
+            end = max(end, start + off + size)
+        pos = end
+
+
+def kernel_hash(path: str | None = None) -> str:
+    """Hash of the kernels' machine code in the library this run loads: the
+    .text section of every GPU code object in its .hip_fatbin, in order.
+    Symbol names that the compiler derives from the build path (and any other
+    section) do not enter, so an identical rebuild elsewhere hashes the same;
+    a counter summary applies to the run only when it was taken on the same
+    machine code."""
+    path = path or os.environ.get("QGEMV_LIB") or LIB_DEFAULT
     with open(path, "rb") as f:
         data = f.read()
-    code = _elf_section(data, ".hip_fatbin")
-    return hashlib.sha256(code if code is not None else data).hexdigest()[:16]
+    fatbin = _elf_section(data, ".hip_fatbin")
+    h = hashlib.sha256()
+    objs = code_objects(fatbin) if fatbin is not None else []
+    texts = [_elf_section(obj, ".text") for obj in objs]
+    if not objs or any(t is None for t in texts):
+        raise SystemExit(f"{path}: no GPU code objects with a .text section found")
+    for t in texts:
+        h.update(struct.pack("<Q", len(t)))
+        h.update(t)
+    return h.hexdigest()[:16]
+
+
+def device_info(torch) -> dict:
+    """Name, architecture and compute units of the GPU, its peak shader and
+    memory clocks (hipDeviceGetAttribute), and the shader and memory clock
+    levels the driver reports as current (sysfs pp_dpm_*, when readable)."""
+    props = torch.cuda.get_device_properties(0)
+    info = {"name": props.name, "arch": props.gcnArchName, "compute_units": props.multi_processor_count}
+    try:
+        import ctypes
+        hip = ctypes.CDLL("libamdhip64.so")
+        dev = torch.cuda.current_device()
+
+        def attr(a):
+            v = ctypes.c_int(0)
+            return v.value if hip.hipDeviceGetAttribute(ctypes.byref(v), a, dev) == 0 else None
+
+        # hipDeviceAttribute_t values of ROCm 7's hip_runtime_api.h: ClockRate 5,
+        # MemoryClockRate 60, MultiprocessorCount 63 (checked against torch's count)
+        if attr(63) == props.multi_processor_count:
+            info["peak_sclk_mhz"] = attr(5) // 1000
+            info["peak_mclk_mhz"] = attr(60) // 1000
+    except (OSError, TypeError, AttributeError):
+        pass
+    pci = f"{props.pci_domain_id:04x}:{props.pci_bus_id:02x}:{props.pci_device_id:02x}.0"
+    for key, fname in (("current_sclk", "pp_dpm_sclk"), ("current_mclk", "pp_dpm_mclk")):
+        try:
+            with open(f"/sys/bus/pci/devices/{pci}/{fname}") as f:
+                cur = [line.split(":", 1)[1].strip().rstrip("*").strip() for line in f if line.strip().endswith("*")]
+            if cur:
+                info[key] = cur[0]
+        except OSError:
+            pass
+    return info
 
 
 def algorithmic_bytes(runs, m, k, n_out, idx_bytes=0):
@@ -283,11 +360,12 @@ def time_workload(wl: Workload, steps: int, warmup: int, torch):
     return ms, batches
 
 
-def time_workload_graph(wl: Workload, steps: int, warmup: int, torch) -> float:
+def time_workload_graph(wl: Workload, steps: int, warmup: int, torch, replays: int = 5) -> float:
     """The same K steps captured once in a HIP graph and replayed: the device
     time per step without the host's issue cost, which is what a caller that
     captures its launch-bound calls sees.  Warmup steps run eagerly first,
-    then one untimed replay; returns ms per step of one timed replay."""
+    then three untimed replays; returns ms per step over `replays` timed
+    replays issued back to back."""
     stream = torch.cuda.current_stream()
     for i in range(warmup):
         wl.step(i, stream.cuda_stream)
@@ -304,14 +382,16 @@ def time_workload_graph(wl: Workload, steps: int, warmup: int, torch) -> float:
         sid = torch.cuda.current_stream().cuda_stream
         for i in range(steps):
             wl.step(warmup + i, sid)
-    g.replay()
+    for _ in range(3):
+        g.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    g.replay()
+    for _ in range(replays):
+        g.replay()
     e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    return e0.elapsed_time(e1) / (steps * replays)
 
 
 def launch_floor(torch, kernels: int = 200, replays: int = 20) -> float:
@@ -457,6 +537,7 @@ def main():
         "mnk_per_s": round(macs / (ms * 1e-3), 1),
         "batch_ms": [round(b, 6) for b in batches],
         "kernel_sha": kernel_hash(),
+        "device": device_info(torch),
     }
     if args.all:
         extra = {}
@@ -486,8 +567,10 @@ def main():
             del w2
             torch.cuda.empty_cache()
         # the configs reported but not targeted: the single matrix, and every
-        # width/group pair of the sweep at 1 and 16 rows (the library's choice)
-        for name, m, pair in [("single", 1, None)] + [("sweep", mm, pr) for pr in synth.PAIRS for mm in (1, 16)]:
+        # width/group pair of the sweep at the config's windows of 1, 2, 3, 8
+        # and 16 rows (the library's choice)
+        for name, m, pair in [("single", 1, None)] + [("sweep", mm, pr) for pr in synth.PAIRS
+                                                      for mm in (1, 2, 3, 8, 16)]:
             w2 = Workload(name, m, torch, qgemv, synth, 0, pair)
             ms2, _ = time_workload(w2, max(50, args.steps // 2), args.warmup, torch)
             msg = time_workload_graph(w2, max(50, args.steps // 2), 100, torch)

@@ -123,6 +123,17 @@ struct qgemv_handle {
 
 namespace {
 
+// Enqueue fn with its by-value arguments and return the launch's own status
+// (a stale error left by the caller's earlier HIP work is neither reported
+// as the library's nor cleared).
+template <class... A>
+int enqueue(const void* fn, dim3 grid, dim3 block, size_t lds, void* stream, A... args) {
+  void* argv[] = {static_cast<void*>(&args)...};
+  return hipLaunchKernel(fn, grid, block, argv, lds, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? QGEMV_OK
+             : QGEMV_E_HIP;
+}
+
 // Per-device facts, fetched once per device at the first launch on it:
 // the compute-unit count, and every kernel's dynamic-LDS limit raised.
 struct DeviceInfo {
@@ -365,8 +376,7 @@ int launch(const qgemv_handle* h, const uint16_t* x, int32_t m, float* y, int64_
     grid.x = static_cast<unsigned>(per);
     grid.y = static_cast<unsigned>(h->d.n_experts);
   }
-  hipLaunchKernelGGL(fn, grid, dim3(threads), lds, static_cast<hipStream_t>(stream), p);
-  return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_E_HIP;
+  return enqueue(reinterpret_cast<const void*>(fn), grid, dim3(threads), lds, stream, p);
 }
 
 }  // namespace
@@ -386,6 +396,7 @@ const char* qgemv_strerror(int status) {
     case QGEMV_E_ALIAS: return "QGEMV_E_ALIAS";
     case QGEMV_E_NOKERNEL: return "QGEMV_E_NOKERNEL";
     case QGEMV_E_HIP: return "QGEMV_E_HIP";
+    case QGEMV_E_INDEX: return "QGEMV_E_INDEX";
   }
   return "QGEMV_E_UNKNOWN";
 }
@@ -522,7 +533,7 @@ int qgemv_run_strided(qgemv_t h, const uint16_t* x, int32_t m, float* y, int64_t
   if (m == 0) return QGEMV_OK;
   const size_t xbytes = static_cast<size_t>(m) * h->d.k * 2;
   const size_t ybytes = (static_cast<size_t>(m - 1) * ldy + h->d.n) * 4;
-  if (ybytes > 0x7fffffffu) return QGEMV_E_STRIDE;
+  if (ybytes > static_cast<size_t>(qg::kNoOffset)) return QGEMV_E_STRIDE;
   rc = check_y_alias(h, y, ybytes, x, xbytes, nullptr, 0);
   if (rc != QGEMV_OK) return rc;
   return launch(h, x, m, y, ldy, nullptr, 0, epi, stream, ybytes);
@@ -543,10 +554,28 @@ int qgemv_run_indexed(qgemv_t h, const uint16_t* x, int32_t m, const int32_t* id
   if (reinterpret_cast<uintptr_t>(idx) & 3) return QGEMV_E_ALIGN;
   const size_t xbytes = static_cast<size_t>(m) * h->d.k * 2;
   const size_t ybytes = static_cast<size_t>(m) * slots * h->d.n * 4;
-  if (ybytes > 0x7fffffffu) return QGEMV_E_SHAPE;
+  if (ybytes > static_cast<size_t>(qg::kNoOffset)) return QGEMV_E_SHAPE;
   rc = check_y_alias(h, y, ybytes, x, xbytes, idx, static_cast<size_t>(m) * slots * 4);
   if (rc != QGEMV_OK) return rc;
   return launch(h, x, m, y, h->d.n, idx, slots, epi, stream, ybytes);
+}
+
+int qgemv_check_indices(qgemv_t h, const int32_t* idx, int32_t m, int32_t slots, void* stream) {
+  if (!h) return QGEMV_E_ARG;
+  if (m < 0 || m > QGEMV_MAX_WINDOW) return QGEMV_E_WINDOW;
+  if (slots < 0 || slots > qg::kMaxSlots) return QGEMV_E_ARG;
+  if (m == 0 || slots == 0) return QGEMV_OK;
+  if (!idx) return QGEMV_E_ARG;
+  if (reinterpret_cast<uintptr_t>(idx) & 3) return QGEMV_E_ALIGN;
+  int32_t host[QGEMV_MAX_WINDOW * qg::kMaxSlots];
+  const size_t count = static_cast<size_t>(m) * slots;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(host, idx, count * sizeof(int32_t), hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return QGEMV_E_HIP;
+  for (size_t i = 0; i < count; ++i)
+    if (host[i] < 0 || host[i] >= h->d.n_experts) return QGEMV_E_INDEX;
+  return QGEMV_OK;
 }
 
 static int check_gateup_pair(qgemv_t gate, qgemv_t up) {
@@ -569,7 +598,7 @@ int qgemv_run_gateup(qgemv_t gate, qgemv_t up, const uint16_t* x, int32_t m, flo
   if (m == 0) return QGEMV_OK;
   const size_t xbytes = static_cast<size_t>(m) * gate->d.k * 2;
   const size_t ybytes = (static_cast<size_t>(m - 1) * ldy + gate->d.n) * 4;
-  if (ybytes > 0x7fffffffu) return QGEMV_E_STRIDE;
+  if (ybytes > static_cast<size_t>(qg::kNoOffset)) return QGEMV_E_STRIDE;
   rc = check_y_alias(gate, y, ybytes, x, xbytes, nullptr, 0);
   if (rc == QGEMV_OK) rc = check_y_alias(up, y, ybytes, x, xbytes, nullptr, 0);
   if (rc != QGEMV_OK) return rc;
@@ -588,7 +617,7 @@ int qgemv_run_gateup_indexed(qgemv_t gate, qgemv_t up, const uint16_t* x, int32_
   if (reinterpret_cast<uintptr_t>(idx) & 3) return QGEMV_E_ALIGN;
   const size_t xbytes = static_cast<size_t>(m) * gate->d.k * 2;
   const size_t ybytes = static_cast<size_t>(m) * slots * gate->d.n * 4;
-  if (ybytes > 0x7fffffffu) return QGEMV_E_SHAPE;
+  if (ybytes > static_cast<size_t>(qg::kNoOffset)) return QGEMV_E_SHAPE;
   const size_t ib = static_cast<size_t>(m) * slots * 4;
   rc = check_y_alias(gate, y, ybytes, x, xbytes, idx, ib);
   if (rc == QGEMV_OK) rc = check_y_alias(up, y, ybytes, x, xbytes, idx, ib);
@@ -607,9 +636,8 @@ int qgemv_debug_unpack(qgemv_t h, int32_t expert, uint8_t* codes, void* stream) 
   typedef void (*UnpackFn)(const uint32_t*, int64_t, int64_t, uint8_t*);
   UnpackFn fn = reinterpret_cast<UnpackFn>(qg::unpack_fn(h->d.bits));
   if (!fn) return QGEMV_E_NOKERNEL;
-  hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(blocks)), dim3(qg::kThreads), 0,
-                     static_cast<hipStream_t>(stream), w, n, k, codes);
-  return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_E_HIP;
+  return enqueue(reinterpret_cast<const void*>(fn), dim3(static_cast<unsigned>(blocks)), dim3(qg::kThreads), 0,
+                 stream, w, n, k, codes);
 }
 
 
@@ -656,17 +684,18 @@ int qgemv_widen(const qgemv_desc* src, int32_t bits_out, int32_t group_out, uint
       overlaps(scales_out, out_s, biases_out, out_s))
     return QGEMV_E_ALIAS;
   if (!current_device()) return QGEMV_E_HIP;
-  const hipStream_t st = static_cast<hipStream_t>(stream);
   const int ratio = src->group / group_out;
-  hipLaunchKernelGGL(qg::widen_kernel, dim3(static_cast<unsigned>((units + qg::kThreads - 1) / qg::kThreads)),
-                     dim3(qg::kThreads), 0, st, src->w, static_cast<int>(src->bits), w_out,
-                     static_cast<int>(bits_out), units);
+  int rc2 = enqueue(reinterpret_cast<const void*>(qg::widen_kernel),
+                    dim3(static_cast<unsigned>((units + qg::kThreads - 1) / qg::kThreads)), dim3(qg::kThreads), 0,
+                    stream, src->w, static_cast<int>(src->bits), w_out, static_cast<int>(bits_out), units);
   const unsigned gb = static_cast<unsigned>((groups_out + qg::kThreads - 1) / qg::kThreads);
-  hipLaunchKernelGGL(qg::regroup_kernel, dim3(gb), dim3(qg::kThreads), 0, st, src->scales, scales_out, ratio,
-                     groups_out);
-  hipLaunchKernelGGL(qg::regroup_kernel, dim3(gb), dim3(qg::kThreads), 0, st, src->biases, biases_out, ratio,
-                     groups_out);
-  return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_E_HIP;
+  if (rc2 == QGEMV_OK)
+    rc2 = enqueue(reinterpret_cast<const void*>(qg::regroup_kernel), dim3(gb), dim3(qg::kThreads), 0, stream,
+                  src->scales, static_cast<uint16_t*>(scales_out), ratio, groups_out);
+  if (rc2 == QGEMV_OK)
+    rc2 = enqueue(reinterpret_cast<const void*>(qg::regroup_kernel), dim3(gb), dim3(qg::kThreads), 0, stream,
+                  src->biases, static_cast<uint16_t*>(biases_out), ratio, groups_out);
+  return rc2;
 }
 
 struct qgemv_stack {
@@ -853,9 +882,8 @@ int launch_stack(const qgemv_stack* s, bool mfma, const uint16_t* x, int32_t m, 
     sp.nblocks[q] = static_cast<int32_t>(nb);
     if (nb > widest) widest = nb;
   }
-  hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(widest), static_cast<unsigned>(nr)), dim3(threads), lds,
-                     static_cast<hipStream_t>(stream), sp);
-  return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_E_HIP;
+  return enqueue(reinterpret_cast<const void*>(fn), dim3(static_cast<unsigned>(widest), static_cast<unsigned>(nr)),
+                 dim3(threads), lds, stream, sp);
 }
 
 }  // namespace
@@ -872,7 +900,7 @@ int qgemv_stack_run(qgemv_stack_t s, const uint16_t* x, int32_t m, float* y, int
   const int64_t k = s->run[0]->d.k;
   const size_t xbytes = static_cast<size_t>(m) * k * 2;
   const size_t ybytes = (static_cast<size_t>(m - 1) * s->ldy + s->col_end) * 4;
-  if (ybytes > 0x7fffffffu) return QGEMV_E_STRIDE;
+  if (ybytes > static_cast<size_t>(qg::kNoOffset)) return QGEMV_E_STRIDE;
   for (int r = 0; r < s->n_runs; ++r) {
     const int rc = check_y_alias(s->run[r], y, ybytes, x, xbytes, nullptr, 0);
     if (rc != QGEMV_OK) return rc;

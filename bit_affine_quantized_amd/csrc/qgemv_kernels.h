@@ -563,11 +563,11 @@ template <> struct Geo<5> { static constexpr int PPC = 5, CPC = 128; };
 template <> struct Geo<6> { static constexpr int PPC = 3, CPC = 64; };
 template <> struct Geo<8> { static constexpr int PPC = 1, CPC = 16; };
 
-#ifndef QG_ODD_ROWS_M1
-#define QG_ODD_ROWS_M1 2
-#endif
+// Output columns per lane of the dot form: 4 at one row for the widths of
+// one-piece chunks, 2 for 3, 5 and 6 bits (their chunks hold 3 or 5 pieces;
+// measured on MI355X, 2 beat 1 and 4 at one row), fewer for wide windows.
 template <int B, int MB> struct FastRows {
-  static constexpr int v = (MB == 1) ? ((B == 2 || B == 4 || B == 8) ? 4 : QG_ODD_ROWS_M1) : (MB <= 4 ? 2 : 1);
+  static constexpr int v = (MB == 1) ? ((B == 2 || B == 4 || B == 8) ? 4 : 2) : (MB <= 4 ? 2 : 1);
 };
 
 // Sum over a column group of LPR = 16, 32 or 64 lanes: rotate 8, rotate 4,
@@ -588,10 +588,16 @@ __device__ __forceinline__ float gsum(float v) {
   return v;
 }
 
-// Buffer resource over [base, base + bytes): loads past the end read 0 and
-// stores past it are dropped (bytes is clamped to the 32-bit field).
+// Lanes with nothing to load or store aim at buffer offset kNoOffset, and
+// every buffer resource spans at most kNoOffset bytes, so that offset is
+// always past the end: such loads read 0 and such stores are dropped.  The
+// host refuses outputs whose extent exceeds kNoOffset bytes, so a real
+// output offset is never clamped away.
+constexpr int kNoOffset = 0x7ffffff0;
+
+// Buffer resource over [base, base + bytes), bytes clamped to kNoOffset.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int nr = bytes > 0x7fffffff ? 0x7fffffff : static_cast<int>(bytes < 0 ? 0 : bytes);
+  const int nr = bytes > kNoOffset ? kNoOffset : static_cast<int>(bytes < 0 ? 0 : bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, nr, 0x00020000);
 }
 
@@ -865,7 +871,7 @@ __device__ __forceinline__ void fast_body(PT& p, const int bx, const int gx, uns
           const int r = e / MB, mi = e - (e / MB) * MB;
           const int row = wrow0 + r * slots_per_wave + slot;
           const bool ok = e < R * MB && li < 16 && mi < mcount && row < n;
-          const int off = ok ? static_cast<int>((s_yoff[ok ? mi : 0] + mapped_column(p, row)) * 4) : 0x7ffffff0;
+          const int off = ok ? static_cast<int>((s_yoff[ok ? mi : 0] + mapped_column(p, row)) * 4) : kNoOffset;
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(apply_epi(v, p.epi)), yres, off, 0, 0);
         }
       }
@@ -1192,7 +1198,7 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
     // its gate columns and its up columns separately (a lane outside a
     // load's range reads zeros), and merges them.
     const int ssoff = MG::SB < 4 ? ((c.gr * MG::SB) & ~3) : c.gr * MG::SB;
-    const int sv = s_live && !(gu && s_col >= 8) ? s_voff : 0x7ffffff0;
+    const int sv = s_live && !(gu && s_col >= 8) ? s_voff : kNoOffset;
     if constexpr (SSZ == 16) {
       u32x4 a4 = __builtin_amdgcn_raw_buffer_load_b128(sr, sv, ssoff, 0);
       u32x4 b4 = __builtin_amdgcn_raw_buffer_load_b128(br, sv, ssoff, 0);
@@ -1201,7 +1207,7 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
                                                      static_cast<int64_t>(ncols) * gpr2);
         const __amdgpu_buffer_rsrc_t br2 = make_rsrc(bexp2 + static_cast<int64_t>(c0) * gpr2,
                                                      static_cast<int64_t>(ncols) * gpr2);
-        const int sv2 = s_live && s_col >= 8 ? s_voff : 0x7ffffff0;
+        const int sv2 = s_live && s_col >= 8 ? s_voff : kNoOffset;
         a4 |= __builtin_amdgcn_raw_buffer_load_b128(sr2, sv2, ssoff, 0);
         b4 |= __builtin_amdgcn_raw_buffer_load_b128(br2, sv2, ssoff, 0);
       }
@@ -1215,7 +1221,7 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
                                                      static_cast<int64_t>(ncols) * gpr2);
         const __amdgpu_buffer_rsrc_t br2 = make_rsrc(bexp2 + static_cast<int64_t>(c0) * gpr2,
                                                      static_cast<int64_t>(ncols) * gpr2);
-        const int sv2 = s_live && s_col >= 8 ? s_voff : 0x7ffffff0;
+        const int sv2 = s_live && s_col >= 8 ? s_voff : kNoOffset;
         sg.s[0] |= __builtin_amdgcn_raw_buffer_load_b32(sr2, sv2, ssoff, 0);
         sg.b[0] |= __builtin_amdgcn_raw_buffer_load_b32(br2, sv2, ssoff, 0);
       }
@@ -1429,7 +1435,7 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
         for (int mb = 0; mb < NACC; ++mb) {
           const int em = WIDE ? 4 * qd + mb : 4 * mb + qd;
           const bool ok = em < mcount && col < n && j < cw;
-          const int off = ok ? static_cast<int>((s_yoff[ok ? em : 0] + mapped_column(p, col)) * 4) : 0x7ffffff0;
+          const int off = ok ? static_cast<int>((s_yoff[ok ? em : 0] + mapped_column(p, col)) * 4) : kNoOffset;
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(gu ? out[mb] : apply_epi(out[mb], p.epi)), yres,
                                                 off, 0, 0);
         }

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libqgemv.so")
 QGEMV_OK = 0
 QGEMV_E_ARG, QGEMV_E_BITS, QGEMV_E_GROUP, QGEMV_E_SHAPE, QGEMV_E_STRIDE = -1, -2, -3, -4, -5
 QGEMV_E_ALIGN, QGEMV_E_WINDOW, QGEMV_E_ALIAS, QGEMV_E_NOKERNEL, QGEMV_E_HIP = -6, -7, -8, -9, -10
+QGEMV_E_INDEX = -11
 QGEMV_EPI_NONE, QGEMV_EPI_RELU2 = 0, 1
 QGEMV_ARITH_AUTO, QGEMV_ARITH_DOT, QGEMV_ARITH_MFMA, QGEMV_ARITH_WIDE = 0, 1, 2, 3
 QGEMV_MAX_WINDOW = 16
@@ -75,6 +76,8 @@ def load(path: str | None = None):
             lib.qgemv_run_strided.restype = ctypes.c_int
             lib.qgemv_run_indexed.argtypes = [p, p, i32, p, i32, p, i32, p]
             lib.qgemv_run_indexed.restype = ctypes.c_int
+            lib.qgemv_check_indices.argtypes = [p, p, i32, i32, p]
+            lib.qgemv_check_indices.restype = ctypes.c_int
             lib.qgemv_run_gateup.argtypes = [p, p, p, i32, p, i64, p]
             lib.qgemv_run_gateup.restype = ctypes.c_int
             lib.qgemv_run_gateup_indexed.argtypes = [p, p, p, i32, p, i32, p, p]
@@ -160,6 +163,10 @@ def qgemv_run_strided(h, x, m, y, ldy, epi=QGEMV_EPI_NONE, stream=None) -> int:
 
 def qgemv_run_indexed(h, x, m, idx, slots, y, epi=QGEMV_EPI_NONE, stream=None) -> int:
     return load().qgemv_run_indexed(h, _addr(x), m, _addr(idx), slots, _addr(y), epi, _stream(stream))
+
+
+def qgemv_check_indices(h, idx, m, slots, stream=None) -> int:
+    return load().qgemv_check_indices(h, _addr(idx), m, slots, _stream(stream))
 
 
 def qgemv_run_gateup(gate, up, x, m, y, ldy, stream=None) -> int:

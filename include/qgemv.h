@@ -27,7 +27,8 @@
  *
  * Memory and ownership.  Every array argument is a DEVICE pointer (HIP
  * device memory, e.g. a torch tensor's data_ptr()).  The library never
- * allocates, frees or synchronises device memory: a handle BORROWS the
+ * allocates or frees device memory and never synchronises (the test-only
+ * qgemv_check_indices excepted): a handle BORROWS the
  * weight pointers given at create, which must stay valid until
  * qgemv_destroy.  A handle is immutable after create, so runs on different
  * streams may share it.
@@ -62,6 +63,8 @@ extern "C" {
 #define QGEMV_E_ALIAS (-8)    /* output overlaps an input                   */
 #define QGEMV_E_NOKERNEL (-9) /* no compiled kernel for this shape          */
 #define QGEMV_E_HIP (-10)     /* a HIP runtime call failed                  */
+#define QGEMV_E_INDEX (-11)   /* an expert index outside [0, n_experts)
+                                 (qgemv_check_indices only)                 */
 
 /* ---- epilogues ------------------------------------------------------- */
 #define QGEMV_EPI_NONE 0
@@ -197,6 +200,16 @@ int qgemv_run_strided(qgemv_t h, const uint16_t* x, int32_t m, float* y, int64_t
  * equal qgemv_run on that expert's single-expert handle with row i. */
 int qgemv_run_indexed(qgemv_t h, const uint16_t* x, int32_t m, const int32_t* idx,
                       int32_t slots, float* y, int32_t epi, void* stream);
+
+/* Checked mode of the indexed calls, for tests and debugging, never for the
+ * decode path: the pages read routing tables on the host and refuse a bad
+ * one by name ("fail closed", P774 "What this changes", item 3).  Copies
+ * idx [m][slots] (device) to the host, which waits for `stream` (this is
+ * the one call that synchronises), and returns QGEMV_E_INDEX if any value
+ * lies outside [0, n_experts) of h, else QGEMV_OK.  m in 0..16 and slots in
+ * 0..64 as for qgemv_run_indexed (QGEMV_E_WINDOW / QGEMV_E_ARG otherwise);
+ * QGEMV_E_HIP if the copy fails.  Launches nothing. */
+int qgemv_check_indices(qgemv_t h, const int32_t* idx, int32_t m, int32_t slots, void* stream);
 
 /* ---- gate/up pairs ------------------------------------------------------
  * The fused gate/up of a gated MLP or expert ("experts gate/up (through

@@ -36,7 +36,7 @@ def test_status_names():
     for code, name in [(0, "QGEMV_OK"), (-1, "QGEMV_E_ARG"), (-2, "QGEMV_E_BITS"), (-3, "QGEMV_E_GROUP"),
                        (-4, "QGEMV_E_SHAPE"), (-5, "QGEMV_E_STRIDE"), (-6, "QGEMV_E_ALIGN"),
                        (-7, "QGEMV_E_WINDOW"), (-8, "QGEMV_E_ALIAS"), (-9, "QGEMV_E_NOKERNEL"),
-                       (-10, "QGEMV_E_HIP")]:
+                       (-10, "QGEMV_E_HIP"), (-11, "QGEMV_E_INDEX")]:
         assert qgemv.qgemv_strerror(code) == name
     assert qgemv.qgemv_strerror(12345) == "QGEMV_E_UNKNOWN"
 
@@ -125,6 +125,40 @@ def test_indexed_refusals():
     assert qgemv.qgemv_run_indexed(h, X, 2, IDX, 8, IDX, 0, 0) == qgemv.QGEMV_E_ALIAS
     assert qgemv.qgemv_debug_unpack(h, 4, Y, 0) == qgemv.QGEMV_E_ARG
     qgemv.qgemv_destroy(h)
+
+
+def test_check_indices_refusals():
+    """The checked mode of indexed calls refuses bad arguments before any HIP
+    call; a valid request needs the device (its copy)."""
+    rc, h = qgemv.qgemv_create(4, 64, 256, 2048, W, S, B, n_experts=4)
+    assert rc == 0
+    chk = qgemv.qgemv_check_indices
+    assert chk(None, IDX, 2, 8, 0) == qgemv.QGEMV_E_ARG
+    assert chk(h, IDX, 17, 8, 0) == qgemv.QGEMV_E_WINDOW
+    assert chk(h, IDX, -1, 8, 0) == qgemv.QGEMV_E_WINDOW
+    assert chk(h, IDX, 2, 65, 0) == qgemv.QGEMV_E_ARG
+    assert chk(h, 0, 2, 8, 0) == qgemv.QGEMV_E_ARG
+    assert chk(h, IDX + 2, 2, 8, 0) == qgemv.QGEMV_E_ALIGN
+    assert chk(h, IDX, 0, 8, 0) == qgemv.QGEMV_OK
+    assert chk(h, IDX, 2, 0, 0) == qgemv.QGEMV_OK
+    qgemv.qgemv_destroy(h)
+
+
+def test_output_extent_limit():
+    """Outputs whose extent passes the kernels' out-of-range store offset
+    (0x7ffffff0 bytes) are refused, so no real store is ever dropped."""
+    rc, h = qgemv.qgemv_create(4, 64, 256, 2048, W, S, B)
+    assert rc == 0
+    # two rows: extent ((2 - 1) * ldy + 256) * 4 bytes.  Only refusals are
+    # called here: the addresses are fake, so nothing may be launched.
+    ldy = 0x7ffffff4 // 4 - 256                 # extent 0x7ffffff4, just past the limit
+    assert qgemv.qgemv_run_strided(h, X, 2, 0x100000000, ldy, 0, 0) == qgemv.QGEMV_E_STRIDE
+    rc, he = qgemv.qgemv_create(4, 64, 1 << 20, 256, W, S, B, n_experts=2)
+    assert rc == 0
+    # 16 rows x 64 slots x 2^20 columns x 4 bytes is far past the limit
+    assert qgemv.qgemv_run_indexed(he, X, 16, IDX, 64, 0x100000000, 0, 0) == qgemv.QGEMV_E_SHAPE
+    qgemv.qgemv_destroy(h)
+    qgemv.qgemv_destroy(he)
 
 
 def test_valid_run_without_a_device_reports_hip(handle):
@@ -287,8 +321,10 @@ def test_kernel_resources_recorded_without_spills():
     needs no scratch), and the matrix-core kernels keep at least 2 waves per
     SIMD."""
     from bit_affine_quantized_amd import build as hip_build
-    if not os.path.exists(hip_build.RESOURCES):
+    if not os.path.exists(hip_build.LIB):
         pytest.skip("library not built here")
+    assert os.path.exists(hip_build.RESOURCES), \
+        f"{hip_build.LIB} is built but {hip_build.RESOURCES} is missing: rebuild with build.build()"
     rows = [line.split() for line in open(hip_build.RESOURCES) if not line.startswith("#")]
     assert len(rows) > 300
     for name, vgprs, agprs, scratch, spill, lds, occ in rows:

@@ -51,7 +51,7 @@ def test_traffic_applies_only_to_its_machine_code(tmp_path, monkeypatch):
     monkeypatch.delenv("QGEMV_LIB", raising=False)
     sha = bench.kernel_hash()
     assert len(sha) == 16 and int(sha, 16) >= 0
-    # the hash covers the kernels' machine code, the library's .hip_fatbin section
+    # the hash covers the kernels' machine code, in the library's .hip_fatbin section
     with open(bench.LIB_DEFAULT, "rb") as f:
         assert bench._elf_section(f.read(), ".hip_fatbin") is not None
     monkeypatch.setattr(bench, "PROFILE_DIR", str(tmp_path))
@@ -63,3 +63,39 @@ def test_traffic_applies_only_to_its_machine_code(tmp_path, monkeypatch):
     (tmp_path / "counters_lmhead_m1.txt").write_text(
         f"kernel_sha: {other}\nhbm_bytes_per_launch: 447000000\n")
     assert bench.read_traffic("lmhead_m1") is None
+
+
+def _patched(tmp_path, name, section, data, fb_off, obj_index, needle=None):
+    """A copy of the library with one byte changed inside one section of one
+    GPU code object (at `needle` if given, else in the section's middle)."""
+    objs = bench.code_objects(data[fb_off[0]:fb_off[0] + fb_off[1]])
+    obj = objs[obj_index]
+    obj_at = data.index(obj, fb_off[0])
+    off, size = bench._elf_section_range(obj, section)
+    at = obj.index(needle, off) if needle else off + size // 2
+    assert off <= at < off + size
+    out = bytearray(data)
+    out[obj_at + at] ^= 0x01
+    path = tmp_path / name
+    path.write_bytes(bytes(out))
+    return str(path)
+
+
+def test_kernel_hash_ignores_path_derived_names(tmp_path):
+    """The hash covers each GPU code object's .text only: changing a byte of a
+    compiler-made, path-derived symbol name (a code object's .strtab, where
+    the __hip_cuid_ names live) keeps it, changing a byte of machine code
+    does not."""
+    if not os.path.exists(bench.LIB_DEFAULT):
+        pytest.skip("library not built here")
+    with open(bench.LIB_DEFAULT, "rb") as f:
+        data = f.read()
+    fb = bench._elf_section_range(data, ".hip_fatbin")
+    objs = bench.code_objects(data[fb[0]:fb[0] + fb[1]])
+    assert len(objs) >= 17                         # one per translation unit
+    base = bench.kernel_hash(bench.LIB_DEFAULT)
+    i = next(j for j, o in enumerate(objs) if b"__hip_cuid_" in o)
+    name_changed = _patched(tmp_path, "names.so", ".strtab", data, fb, i, needle=b"__hip_cuid_")
+    assert bench.kernel_hash(name_changed) == base
+    code_changed = _patched(tmp_path, "code.so", ".text", data, fb, i)
+    assert bench.kernel_hash(code_changed) != base

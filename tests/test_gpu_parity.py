@@ -136,7 +136,9 @@ def test_sweep_within_bound(bits, group, arith):
 @pytest.mark.parametrize("bits,group", PAIRS)
 def test_window_invariance(bits, group, arith):
     """Every row of a 64-row pool alone equals itself at every position of
-    every 2-, 3-, 8- and 16-row window, bit for bit."""
+    every window of 2 to 16 rows, bit for bit (the pages check windows of 1,
+    2, 3, 4, 5, 8, 9, 16, 17 and 33 rows against one call; 17 and 33 are
+    prompt windows, tested separately)."""
     print_case("windows", bits, group, arith)
     d = synth.sweep(bits, group, m=0)
     rng = np.random.default_rng(synth.sweep_seed(bits, group) + 7)
@@ -145,11 +147,14 @@ def test_window_invariance(bits, group, arith):
     alone = torch.empty((64, d["n"]), dtype=torch.float32, device=DEV)
     for r in range(64):
         mat.run(pool[r:r + 1], alone[r:r + 1], m=1)
-    for m in (2, 3, 8, 16):
-        y = torch.empty((m, d["n"]), dtype=torch.float32, device=DEV)
+    for m in range(2, 17):
+        y = torch.empty((64 - m + 1, m, d["n"]), dtype=torch.float32, device=DEV)
         for s0 in range(0, 64 - m + 1):
-            mat.run(pool[s0:s0 + m], y, m=m)
-            assert bits_equal(y, alone[s0:s0 + m]), f"window {m} at {s0}"
+            mat.run(pool[s0:s0 + m], y[s0], m=m)
+        want = torch.stack([alone[s0:s0 + m] for s0 in range(0, 64 - m + 1)])
+        if not bits_equal(y, want):
+            bad = [s0 for s0 in range(0, 64 - m + 1) if not bits_equal(y[s0], want[s0])]
+            raise AssertionError(f"window {m} differs at positions {bad[:8]}")
 
 
 @mc_param
@@ -558,6 +563,45 @@ def lmhead():
 
 
 @arith_param
+def test_lmhead_every_column_one_row(lmhead, arith):
+    """The 1-row LM head (the workload the benchmark times) against the
+    threaded oracle at every one of its 248,320 columns."""
+    d = lmhead
+    n, k, bits, group = d["n"], d["k"], d["bits"], d["group"]
+    y = run(d["mats"][arith], d["xt"], 1).cpu().numpy()
+    if "y64_m1" not in d:
+        d["y64_m1"] = oracle.gemv(d["words"], d["scales"], d["biases"], d["x"][:1], bits, group, n, k,
+                                  threads=THREADS)
+    y64, a64, _ = d["y64_m1"]
+    frac = check_bound(y, y64, a64, k, f"lmhead every column arith={arith}")
+    print_case(f"  lmhead, all {n} columns: worst err/bound {frac:.4f}")
+
+
+# about 2,200 tiles of 64 columns: more than the resident blocks of the
+# whole chip (at most a few per CU), so each block walks several
+MULTI_TILE = [(6, 32, 140000, 512), (4, 64, 141000, 256), (5, 128, 140100, 1024), (3, 32, 139900, 1024),
+              (2, 128, 140007, 512), (8, 64, 140033, 256)]
+
+
+@arith_param
+@pytest.mark.parametrize("bits,group,n,k", MULTI_TILE)
+def test_blocks_walking_several_tiles(bits, group, n, k, arith):
+    """Shapes with more column tiles than the resident grid holds, so that
+    every block walks several tiles and reuses its staged window: every
+    column against the oracle at 1 and 4 rows, and the 4-row window's rows
+    equal to their 1-row calls bit for bit."""
+    print_case("multi-tile", bits, group, n, k, arith)
+    d = synth.matrix(8800 + bits * 10 + group, bits, group, n, k, 4)
+    mat = matrix_of(d, arith=arith)
+    xt = dev(d["x"])
+    y4 = run(mat, xt)
+    y64, a64, _ = oracle.gemv(d["words"], d["scales"], d["biases"], d["x"], bits, group, n, k, threads=THREADS)
+    check_bound(y4.cpu().numpy(), y64, a64, k, f"multi-tile {bits}/{group} {n}x{k}")
+    for r in range(4):
+        assert bits_equal(run(mat, xt[r:r + 1])[0], y4[r]), f"row {r}"
+
+
+@arith_param
 @pytest.mark.parametrize("m", [1, 8, 16])
 def test_lmhead_sampled(lmhead, m, arith):
     d = lmhead
@@ -614,6 +658,56 @@ def test_indexed_experts_config(experts, epi, arith):
         tol = oracle.tol_relu2(y64, tol)
         y64 = oracle.relu2(y64)
     assert np.all(np.abs(got - y64) <= tol)
+
+
+@arith_param
+def test_indexed_out_of_range_slots_write_nothing(arith):
+    """idx values outside [0, n_experts) (-1, n_experts, large) are a caller
+    precondition: the kernels only match valid expert ids, so such slots keep
+    their bytes and every other slot equals the plain call on its expert's
+    own handle; the checked mode names the table QGEMV_E_INDEX.  Indexed
+    gate/up pairs likewise (matrix-core forms)."""
+    bits, group, n, k, e = 4, 64, 200, 1024, 5
+    d = synth.matrix(4300, bits, group, n, k, 6, n_experts=e)
+    idx = np.array([[0, -1, 4], [e, 2, 2], [1, 3, 1 << 20], [-7, -1, e], [4, 0, 3], [2, e + 1, 1]],
+                   dtype=np.int32)
+    tw, ts, tb = dev(d["words"]), dev(d["scales"]), dev(d["biases"])
+    mat = qgemv.Matrix(bits, group, n, k, tw, ts, tb, n_experts=e, arith=arith)
+    xt = dev(d["x"])
+    ti = dev(idx)
+    sentinel = torch.full((6, 3, n), 0x7FC0BEEF, dtype=torch.int32, device=DEV)
+    y = sentinel.clone().view(torch.float32)
+    mat.run_indexed(xt, ti, y.view(-1), epi=qgemv.QGEMV_EPI_RELU2)
+    views = {}
+    for i in range(6):
+        for s_ in range(3):
+            ex = int(idx[i, s_])
+            if not 0 <= ex < e:
+                assert torch.equal(y[i, s_].view(torch.int32), sentinel[i, s_]), (i, s_, ex)
+                continue
+            if ex not in views:
+                views[ex] = qgemv.Matrix(bits, group, n, k, tw[ex], ts[ex], tb[ex], arith=arith)
+            assert bits_equal(run(views[ex], xt[i:i + 1], epi=qgemv.QGEMV_EPI_RELU2)[0], y[i, s_]), (i, s_)
+    assert qgemv.qgemv_check_indices(mat.h, ti, 6, 3) == qgemv.QGEMV_E_INDEX
+    good = dev(np.clip(idx, 0, e - 1).astype(np.int32))
+    assert qgemv.qgemv_check_indices(mat.h, good, 6, 3) == qgemv.QGEMV_OK
+    if arith == qgemv.QGEMV_ARITH_DOT:
+        return
+    du = synth.matrix(4301, bits, group, n, k, n_experts=e)
+    tu = [dev(du[key]) for key in ("words", "scales", "biases")]
+    up = qgemv.Matrix(bits, group, n, k, *tu, n_experts=e, arith=arith)
+    yp = sentinel.clone().view(torch.float32)
+    assert qgemv.qgemv_run_gateup_indexed(mat.h, up.h, xt, 6, ti, 3, yp.view(-1)) == qgemv.QGEMV_OK
+    y1 = torch.empty((1, n), dtype=torch.float32, device=DEV)
+    for i in range(6):
+        for s_ in range(3):
+            ex = int(idx[i, s_])
+            if not 0 <= ex < e:
+                assert torch.equal(yp[i, s_].view(torch.int32), sentinel[i, s_]), (i, s_, ex)
+                continue
+            vu = qgemv.Matrix(bits, group, n, k, tu[0][ex], tu[1][ex], tu[2][ex], arith=arith)
+            assert qgemv.qgemv_run_gateup(views[ex].h, vu.h, xt[i:i + 1], 1, y1, n) == qgemv.QGEMV_OK
+            assert bits_equal(y1[0], yp[i, s_]), (i, s_)
 
 
 @arith_param
