@@ -360,12 +360,12 @@ def time_workload(wl: Workload, steps: int, warmup: int, torch):
     return ms, batches
 
 
-def time_workload_graph(wl: Workload, steps: int, warmup: int, torch, replays: int = 5) -> float:
+def time_workload_graph(wl: Workload, steps: int, warmup: int, torch, min_ms: float = 100.0) -> float:
     """The same K steps captured once in a HIP graph and replayed: the device
     time per step without the host's issue cost, which is what a caller that
     captures its launch-bound calls sees.  Warmup steps run eagerly first,
-    then three untimed replays; returns ms per step over `replays` timed
-    replays issued back to back."""
+    then three untimed replays; returns ms per step over the timed replays
+    issued back to back: at least 5, and at least min_ms of them."""
     stream = torch.cuda.current_stream()
     for i in range(warmup):
         wl.step(i, stream.cuda_stream)
@@ -382,10 +382,13 @@ def time_workload_graph(wl: Workload, steps: int, warmup: int, torch, replays: i
         sid = torch.cuda.current_stream().cuda_stream
         for i in range(steps):
             wl.step(warmup + i, sid)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
     for _ in range(3):
         g.replay()
+    e1.record()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    replays = max(5, int(min_ms / max(e0.elapsed_time(e1) / 3, 1e-3)) + 1)
     e0.record()
     for _ in range(replays):
         g.replay()
@@ -505,9 +508,15 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     arith = {"auto": 0, "dot": 1, "mfma": 2, "wide": 3}[args.arith]
     wl = Workload(args.workload, args.m, torch, qgemv, synth, arith)
-    ms, batches = time_workload(wl, args.steps, args.warmup, torch)
-    # the same steps as one captured graph: no host issue cost
+    # The same K steps as one captured graph first (no host issue cost; 100
+    # eager steps, 3 untimed replays of K steps, then timed replays: at least
+    # 5 and at least 100 ms of them), then the W untimed warmup steps and the
+    # K timed eager steps.  The graph leg also keeps the GPU busy for over
+    # 100 ms before the eager measurement: the clocks climb (the shader clock
+    # from about 1.2 to 2.3 GHz) over the first tens of milliseconds of load,
+    # which a short warmup does not cover.
     ms_graph = time_workload_graph(wl, args.steps, 100, torch)
+    ms, batches = time_workload(wl, args.steps, args.warmup, torch)
     if args.graph:
         ms, batches = ms_graph, [ms_graph]
     gbs = wl.bytes / (ms * 1e-3) / 1e9
@@ -522,7 +531,8 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms, 6),
         "ms_per_step_graph": round(ms_graph, 6),
-        "timing": "HIP graph replay" if args.graph else "eager launches on one stream",
+        "timing": ("HIP graph replay" if args.graph else
+                   "eager launches on one stream, after the graph-replay measurement of the same steps"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -554,8 +564,8 @@ def main():
             if key in extra or (name == args.workload and m == wl.m and w2.arith_used == wl.arith_used):
                 del w2
                 continue
+            msg = time_workload_graph(w2, max(50, args.steps // 2), 100, torch, min_ms=20.0)
             ms2, _ = time_workload(w2, max(50, args.steps // 2), args.warmup, torch)
-            msg = time_workload_graph(w2, max(50, args.steps // 2), 100, torch)
             g2 = w2.bytes / (ms2 * 1e-3) / 1e9
             rc2, mac2 = w2.counts()
             extra[key] = {"us_per_call": round(ms2 * 1e3, 3), "GB/s": round(g2, 1),
@@ -572,8 +582,8 @@ def main():
         for name, m, pair in [("single", 1, None)] + [("sweep", mm, pr) for pr in synth.PAIRS
                                                       for mm in (1, 2, 3, 8, 16)]:
             w2 = Workload(name, m, torch, qgemv, synth, 0, pair)
+            msg = time_workload_graph(w2, max(50, args.steps // 2), 100, torch, min_ms=20.0)
             ms2, _ = time_workload(w2, max(50, args.steps // 2), args.warmup, torch)
-            msg = time_workload_graph(w2, max(50, args.steps // 2), 100, torch)
             g2 = w2.bytes / (ms2 * 1e-3) / 1e9
             key = f"{name}_m{m}" + (f"_b{pair[0]}g{pair[1]}" if pair else "") + f"_{w2.arith_used}"
             extra[key] = {"us_per_call": round(ms2 * 1e3, 3), "GB/s": round(g2, 1),

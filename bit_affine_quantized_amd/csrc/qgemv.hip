@@ -922,7 +922,7 @@ int qgemv_query(qgemv_t h, int64_t out[6]) {
     out[1] = 16;
     out[2] = 32;
     out[3] = h->entry->mfma_waves[0] * qg::kWave;
-    out[4] = static_cast<int64_t>(h->entry->mfma_waves[0]) * 16;
+    out[4] = static_cast<int64_t>(h->entry->mfma_waves[0] / h->ksplit) * 16;
   } else {
     const int R = h->fast ? h->entry->fast_rows[0] : h->entry->generic_rows[0];
     out[0] = h->lpr;

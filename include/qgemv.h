@@ -311,8 +311,10 @@ void qgemv_stack_destroy(qgemv_stack_t s);
 
 /* Launch geometry fixed at create (for tests and reports):
  *   out[0] lanes per output column, out[1] output columns per wave,
- *   out[2] codes per lane chunk, out[3] threads per block,
- *   out[4] output columns per block tile, out[5] compute units seen.   */
+ *   out[2] codes per lane chunk, out[3] threads per block of a 1-row
+ *   window, out[4] output columns per block tile of a 1-row window (the
+ *   K split of a matrix-core handle spreads each column over that many
+ *   waves), out[5] compute units seen.   */
 int qgemv_query(qgemv_t h, int64_t out[6]);
 
 #ifdef __cplusplus

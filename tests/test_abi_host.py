@@ -218,7 +218,9 @@ def test_arith_choice_fixed_at_create():
                 rc, geo = qgemv.qgemv_query(h)
                 assert rc == 0
                 if arith != qgemv.QGEMV_ARITH_DOT:
-                    assert geo[:5] == [4, 16, 32, 256, 64]
+                    # 48 columns: a 4-wave block splits K of one 16-column
+                    # tile in 4 parts (k = 4 load groups)
+                    assert geo[:5] == [4, 16, 32, 256, 16], geo
                 qgemv.qgemv_destroy(h)
             rc, h = qgemv.qgemv_create(bits, group, 48, k, W, S, B)
             assert rc == 0 and qgemv.qgemv_arith(h) in (qgemv.QGEMV_ARITH_DOT, qgemv.QGEMV_ARITH_MFMA)

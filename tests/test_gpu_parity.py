@@ -601,6 +601,43 @@ def test_blocks_walking_several_tiles(bits, group, n, k, arith):
         assert bits_equal(run(mat, xt[r:r + 1])[0], y4[r]), f"row {r}"
 
 
+@mc_param
+def test_many_tiles_consecutive_calls(arith):
+    """Matrix-core plain and strided calls with more column tiles than the
+    resident blocks hold: their rows equal those of a 17-row prompt window
+    (two passes over the tiles) bit for bit; consecutive calls on a large and
+    then a smaller matrix, and a strided call, write every column, and the
+    strided call leaves its gaps untouched."""
+    print_case("many tiles, consecutive calls", arith)
+    big = synth.matrix(8900, 6, 32, 100000, 512, 17)
+    small = synth.matrix(8901, 4, 64, 70001, 256, 3)
+    mb, ms = matrix_of(big, arith=arith), matrix_of(small, arith=arith)
+    xb, xs = dev(big["x"]), dev(small["x"])
+    y17 = run(mb, xb, 17)                           # two passes of window rows
+    sent = 0x7FC0BEEF
+    for rep in range(3):
+        yb = torch.full((2, 100000), sent, dtype=torch.int32, device=DEV).view(torch.float32)
+        mb.run(xb[:2], yb, m=2)
+        ys = torch.full((3, 70001), sent, dtype=torch.int32, device=DEV).view(torch.float32)
+        ms.run(xs, ys, m=3)
+        y1 = run(mb, xb[5:6], 1)
+        assert bits_equal(yb, y17[:2]), rep
+        assert bits_equal(y1[0], y17[5]), rep
+        assert not torch.any(ys.view(torch.int32) == sent), rep
+    y64, a64, _ = oracle.gemv(small["words"], small["scales"], small["biases"], small["x"], 4, 64, 70001, 256,
+                              threads=THREADS)
+    check_bound(ys.cpu().numpy(), y64, a64, 256, "many tiles, smaller matrix")
+    # strided: gaps untouched, columns equal the plain call's
+    ldy = 100003
+    wide = torch.full((2, ldy), sent, dtype=torch.int32, device=DEV)
+    yw = wide.clone().view(torch.float32)
+    mb.run_strided(xb[:2], yw.view(-1)[2:], ldy, m=2)
+    assert bits_equal(yw[:, 2:2 + 100000], y17[:2])
+    gap = torch.ones((2, ldy), dtype=torch.bool, device=DEV)
+    gap[:, 2:2 + 100000] = False
+    assert torch.equal(yw.view(torch.int32)[gap], wide[gap])
+
+
 @arith_param
 @pytest.mark.parametrize("m", [1, 8, 16])
 def test_lmhead_sampled(lmhead, m, arith):
@@ -734,16 +771,28 @@ def test_indexed_small_stack_repeats_and_duplicates(arith):
 # fused stacks: one dispatch, each member equal to its run's strided call
 # ---------------------------------------------------------------------------
 
+def _offset_by_one(a: np.ndarray):
+    """A device copy of a bf16 array that starts 2 bytes into its buffer (so
+    it is 2-byte but not 4-byte aligned)."""
+    buf = torch.zeros(a.size + 1, dtype=torch.int16, device=DEV)
+    buf[1:] = dev(a.reshape(-1))
+    return buf[1:]
+
+
 def _stack_runs(specs, k, seed):
-    """specs: [(bits, group, [(rows, col), ...])]; returns runs for qgemv.Stack
-    plus the host copies."""
+    """specs: [(bits, group, [(rows, col), ...])] or (..., misaligned): with
+    misaligned true the run's scales and biases are only 2-byte aligned.
+    Returns runs for qgemv.Stack plus the host copies."""
     runs, host = [], []
-    for i, (bits, group, members) in enumerate(specs):
+    for i, spec in enumerate(specs):
+        bits, group, members = spec[:3]
+        mis = len(spec) > 3 and spec[3]
         n = sum(r for r, _ in members)
         d = synth.matrix(seed + i, bits, group, n, k)
         host.append(d)
-        runs.append(dict(bits=bits, group=group, n=n, k=k, w=dev(d["words"]), scales=dev(d["scales"]),
-                         biases=dev(d["biases"]), members=members))
+        put = _offset_by_one if mis else dev
+        runs.append(dict(bits=bits, group=group, n=n, k=k, w=dev(d["words"]), scales=put(d["scales"]),
+                         biases=put(d["biases"]), members=members))
     return runs, host
 
 
@@ -815,6 +864,22 @@ def test_fused_stack_both_forms():
     _check_stack(specs, k, 520, 1, 3400)
 
 
+def test_fused_stack_dot_runs_by_alignment():
+    """At K = 2048 a stack's runs whose scales and biases are only 2-byte
+    aligned (which the matrix-core form does not take) run in the dot form,
+    the others on the matrix cores: two dispatches, each member equal to its
+    run's own call, gaps untouched."""
+    k = 2048
+    specs = [(4, 64, [(200, 0)]), (6, 64, [(72, 300), (24, 200)], True), (3, 64, [(96, 400)], True),
+             (5, 128, [(600, 520)])]
+    runs, _ = _stack_runs(specs, k, 3450)
+    forms = [qgemv.Matrix(r["bits"], r["group"], r["n"], k, r["w"], r["scales"], r["biases"]).arith for r in runs]
+    assert forms == [qgemv.QGEMV_ARITH_MFMA, qgemv.QGEMV_ARITH_DOT, qgemv.QGEMV_ARITH_DOT,
+                     qgemv.QGEMV_ARITH_MFMA], forms
+    print_case("fused stack, runs of both forms by alignment", k)
+    _check_stack(specs, k, 1200, 3, 3450)
+
+
 # ---------------------------------------------------------------------------
 # seeded random shapes across widths, groups, forms and windows
 # ---------------------------------------------------------------------------
@@ -877,7 +942,8 @@ def test_random_shapes(bits, group, n, k, m, arith, seed):
 # ---------------------------------------------------------------------------
 
 def test_graph_replay_equals_eager():
-    """Plain, strided, fused-stack and indexed (relu2) calls captured in one
+    """Plain, strided, fused-stack, indexed (relu2) and many-tile plain calls
+    captured in one
     HIP graph and replayed three times, with eager calls and output resets
     between the replays: every replay's outputs equal the eager calls' bit for
     bit, and the strided call's gaps keep their bytes (the library records no
@@ -903,20 +969,26 @@ def test_graph_replay_equals_eager():
     sentinel = torch.full((3, ldy), 0x7FC0BEEF, dtype=torch.int32, device=DEV)
     gap = torch.ones((3, ldy), dtype=torch.bool, device=DEV)
     gap[:, 10:10 + 256] = False
+    # a matrix of more column tiles than the resident blocks hold
+    d4 = synth.matrix(8104, 6, 32, 90000, 512, 3)
+    many = matrix_of(d4)
+    x4 = dev(d4["x"])
 
     def outputs():
         return (torch.empty((3, 1000), dtype=torch.float32, device=DEV),
                 sentinel.clone().view(torch.float32),
                 torch.zeros((3, 512), dtype=torch.float32, device=DEV),
-                torch.empty((9, 3, n), dtype=torch.float32, device=DEV))
+                torch.empty((9, 3, n), dtype=torch.float32, device=DEV),
+                torch.empty((3, 90000), dtype=torch.float32, device=DEV))
 
     def launch(outs, s):
-        yp, ys, yk, yi = outs
+        yp, ys, yk, yi, yd = outs
         assert qgemv.qgemv_run(plain.h, x1, 3, yp, 0, s) == qgemv.QGEMV_OK
         assert qgemv.qgemv_run_strided(strided.h, x1, 3, ys.view(-1)[10:], ldy, 0, s) == qgemv.QGEMV_OK
         assert qgemv.qgemv_stack_run(stack.h, x1, 3, yk, 0, s) == qgemv.QGEMV_OK
         assert qgemv.qgemv_run_indexed(experts.h, x3, 9, idx, 3, yi.view(-1), qgemv.QGEMV_EPI_RELU2, s) \
             == qgemv.QGEMV_OK
+        assert qgemv.qgemv_run(many.h, x4, 3, yd, 0, s) == qgemv.QGEMV_OK
 
     eager = outputs()
     launch(eager, torch.cuda.current_stream().cuda_stream)
@@ -939,6 +1011,7 @@ def test_graph_replay_equals_eager():
         graphed[1].view(torch.int32).copy_(sentinel)
         graphed[2].zero_()
         graphed[3].view(torch.int32).fill_(0x7FC0BEEF)
+        graphed[4].view(torch.int32).fill_(0x7FC0BEEF)
         launch(other, torch.cuda.current_stream().cuda_stream)   # eager work between replays
         g.replay()
         torch.cuda.synchronize()
