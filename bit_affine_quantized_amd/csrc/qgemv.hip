@@ -258,6 +258,17 @@ int check_y_alias(const qgemv_handle* h, const void* y, size_t ybytes, const voi
   return QGEMV_OK;
 }
 
+// The matrix-core form's K split as the kernels take it: its log2, the load
+// groups of each part, and the rounded reciprocal of the 32-code units per
+// row (the kernels split a staging index into row and unit with it).
+void set_split(qg::Params& p, const qgemv_handle* h) {
+  p.ksplit = h->ksplit;
+  p.ks_shift = h->ksplit == 4 ? 2 : (h->ksplit == 2 ? 1 : 0);
+  const int64_t units = h->d.k / 32;
+  p.gpp = static_cast<int32_t>(units / (4 * static_cast<int64_t>(h->entry->mfma_group)) / h->ksplit);
+  p.inv_units = 1.0f / static_cast<float>(units);
+}
+
 // up: the up matrix of a gate/up pair (matrix-core form), else nullptr.
 int launch(const qgemv_handle* h, const uint16_t* x, int32_t m, float* y, int64_t ldy,
            const int32_t* idx, int32_t slots, int32_t epi, void* stream, size_t ybytes,
@@ -332,7 +343,7 @@ int launch(const qgemv_handle* h, const uint16_t* x, int32_t m, float* y, int64_
   p.tiles = static_cast<int32_t>(tiles);
   p.indexed = indexed;
   p.vec_groups = h->vec_groups;
-  p.ksplit = h->ksplit;
+  set_split(p, h);
   p.gateup = up ? 1 : 0;
   p.w2 = up ? up->d.w : nullptr;
   p.scales2 = up ? up->d.scales : nullptr;
@@ -810,7 +821,7 @@ int launch_stack(const qgemv_stack* s, bool mfma, const uint16_t* x, int32_t m, 
     if (mfma) {
       threads = h->entry->mfma_waves[var] * qg::kWave;
       tile_rows = static_cast<int64_t>(h->entry->mfma_waves[var] / h->ksplit) * 16;
-      sp.kind[q] = bi * 3 + gi;
+      sp.sel[q].kind = bi * 3 + gi;
     } else {
       int stage = h->ppc > 1 ? 1 : 0;
       if (stage && lds_bytes(h, var, 1) > qg::kMaxDynamicLds) stage = 0;
@@ -819,7 +830,7 @@ int launch_stack(const qgemv_stack* s, bool mfma, const uint16_t* x, int32_t m, 
       if (l > lds) lds = l;
       const int R = h->entry->fast_rows[var];
       tile_rows = static_cast<int64_t>(qg::kWaves) * (qg::kWave / h->lpr) * R;
-      sp.kind[q] = (bi * 3 + gi) * 2 + stage;
+      sp.sel[q].kind = (bi * 3 + gi) * 2 + stage;
     }
     tiles[q] = (h->d.n + tile_rows - 1) / tile_rows;
     total_tiles += tiles[q];
@@ -845,7 +856,7 @@ int launch_stack(const qgemv_stack* s, bool mfma, const uint16_t* x, int32_t m, 
     p.tiles = static_cast<int32_t>(tiles[q]);
     p.indexed = 0;
     p.vec_groups = h->vec_groups;
-    p.ksplit = h->ksplit;
+    set_split(p, h);
     p.y_bytes = static_cast<int64_t>(ybytes);
     p.nseg = s->n_members[r];
     int64_t row0 = 0;
@@ -879,7 +890,7 @@ int launch_stack(const qgemv_stack* s, bool mfma, const uint16_t* x, int32_t m, 
       if (nb < 1) nb = 1;
       if (nb > tiles[q]) nb = tiles[q];
     }
-    sp.nblocks[q] = static_cast<int32_t>(nb);
+    sp.sel[q].nblocks = static_cast<int32_t>(nb);
     if (nb > widest) widest = nb;
   }
   return enqueue(reinterpret_cast<const void*>(fn), dim3(static_cast<unsigned>(widest), static_cast<unsigned>(nr)),

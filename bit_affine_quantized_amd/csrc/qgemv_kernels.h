@@ -206,25 +206,32 @@ __device__ __forceinline__ void load_chunk(const uint32_t* __restrict__ p, uint3
 }
 
 struct Params {
+  // What a block needs before its first loads comes first, in the first 104
+  // bytes of the argument segment, so that the kernels read it in one round
+  // of scalar loads.
   const uint32_t* w;        // [E][N][WPR]
   const uint16_t* scales;   // [E][N][GPR]
   const uint16_t* biases;
   const uint16_t* x;        // [M][K] bf16
-  float* y;
-  const int32_t* idx;       // indexed: [M][slots]
   int64_t n;                // output columns
   int64_t k;
   int64_t wpr;              // words per row
   int64_t gpr;              // groups per row
-  int64_t ldy;              // plain/strided row stride of y
   int32_t m;                // window rows
+  int32_t tiles;            // column tiles per expert
+  int32_t ks_shift;         // matrix-core form: log2(ksplit)
+  int32_t gpp;              // matrix-core form: load groups per K-part
+  float inv_units;          // matrix-core form: 1 / (k / 32), rounded (see split_units)
   int32_t slots;            // indexed only
+  const int32_t* idx;       // indexed: [M][slots]
+  // the rest
+  float* y;
+  int64_t ldy;              // plain/strided row stride of y
   int32_t n_experts;
   int32_t epi;
   int32_t lpr;              // lanes per output column (power of two <= 64)
   int32_t cpl;              // chunks per lane
   int32_t nchunks;          // chunks per row = lpr * cpl
-  int32_t tiles;            // column tiles per expert
   int32_t indexed;          // 0: plain/strided, 1: indexed
   int32_t vec_groups;       // scales/biases aligned for packed loads
   int32_t ksplit;           // matrix-core form: K-parts per column (1, 2 or 4)
@@ -242,6 +249,7 @@ struct Params {
   int32_t seg_row0[kMaxSeg];
   int64_t seg_delta[kMaxSeg];
 };
+static_assert(offsetof(Params, idx) + sizeof(void*) <= 104, "the first-loads block of Params");
 
 // silu(g) = g / (1 + exp(-g)), fp32, with the device library's expf
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
@@ -1050,6 +1058,18 @@ __device__ __forceinline__ void transpose_rows(uint32_t* q) {
   }
 }
 
+// t = mi * units + un for 0 <= t < 2^22: the quotient from one fp32 product
+// with the rounded reciprocal is off by at most one (relative error below
+// 2^-22 on a quotient below 2^22), and one correction step fixes it.
+// (Selects, not branches: it sits ahead of a kernel's first loads.)
+__device__ __forceinline__ void split_units(int t, int units, float inv_units, int& mi, int& un) {
+  const int q = static_cast<int>(static_cast<float>(t) * inv_units);
+  const int r = t - q * units;
+  const int fix = r < 0 ? -1 : (r >= units ? 1 : 0);
+  mi = q + fix;
+  un = r - fix * units;
+}
+
 // WIDE selects the wide-window form: after the unpack, the four lanes of a
 // column trade quarters of their units (transpose_rows), so that lane (j, q)
 // holds k-quarter q of all four units of the round; each unit is then one
@@ -1067,10 +1087,16 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
   constexpr int NACC = WIDE ? (MB < 4 ? MB : 4) : NMB;
   constexpr int ZB = R * 256;               // zero area: one group's activations
 
-  const int units = static_cast<int>(p.k / 32);
-  const int S = p.ksplit;                   // K-parts per column
-  const int gpp = units / (4 * R) / S;      // groups per K-part
-  const int ncg = NW / S;                   // column groups (of 16 columns) per block
+  // the call's shape as the host derived it: no division on the device
+  // before the first loads (each instruction of a lone wave costs about 4
+  // cycles, and a small call's waves run alone on their SIMDs)
+  const int units = static_cast<int>(p.k) >> 5;
+  const int ksh = p.ks_shift;
+  const int S = 1 << ksh;                   // K-parts per column
+  const int gpp = p.gpp;                    // groups per K-part
+  const int ncg = NW >> ksh;                // column groups (of 16 columns) per block
+  const float inv_units = p.inv_units;
+  const int tiles = p.tiles;
   const int mrows = IDX ? MB : min(p.m, MB);       // window rows staged
   const int xstride = units * 64 + 16;                     // bytes per staged row
   const int sstride = units + 4;                           // floats per row of unit sums
@@ -1093,7 +1119,7 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
   const int lane = tid % kWave;
   const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int j = lane % 16, qd = lane / 16;
-  const int cg = wv / S, ks = wv - (wv / S) * S;   // column group, K-part
+  const int cg = wv >> ksh, ks = wv & (S - 1);    // column group, K-part
   unsigned char* slot = slots + static_cast<size_t>(wv) * MG::SLOT;
   static_assert(4 * kWave * 4 <= MG::SLOT, "partial sums fit a slot");
 
@@ -1117,9 +1143,6 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
   const unsigned char* wexp2 = gu ? reinterpret_cast<const unsigned char*>(p.w2) + static_cast<int64_t>(expert) * p.n * row_bytes : wexp;
   const unsigned char* sexp2 = gu ? reinterpret_cast<const unsigned char*>(p.scales2) + static_cast<int64_t>(expert) * p.n * gpr2 : sexp;
   const unsigned char* bexp2 = gu ? reinterpret_cast<const unsigned char*>(p.biases2) + static_cast<int64_t>(expert) * p.n * gpr2 : bexp;
-  const int my_tiles = bx < p.tiles ? (p.tiles - 1 - bx) / gx + 1 : 0;
-  const int steps = my_tiles * gpp;
-  const __amdgpu_buffer_rsrc_t yres = make_rsrc(p.y, p.y_bytes);
 
   // ---- per-lane constants of the loads and reads (the same for every group) ----
   // weight load t: lanes 8a..8a+7 fetch line lam = 8t + a of the slot, which
@@ -1146,27 +1169,23 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
   // (qd*NP + t) % 8 of the slot (rotated by j / 2).
   constexpr int NP = R * B / 4;
   static_assert((R * B) % 4 == 0, "a lane's units are whole pieces");
+  // (set once the window is staged: only the hand-off reads need them)
   int p_off[NP];
-#pragma unroll
-  for (int t = 0; t < NP; ++t) {
-    const int pc = qd * NP + t, ln = pc / 8, pp = pc % 8;
-    p_off[t] = ((ln * 16 + j) * 8 + ((pp + j / 2) & 7)) * 16;
-  }
   const int s_off = MG::WBYTES + j * MG::SSTR;
   const int b_off = s_off + 16 * MG::SSTR;
   constexpr int UPG = G / 32;                 // units per group
 
   // A step is one group of this wave's K-part of one tile; cursors walk the
-  // steps in order (gr counts groups from the start of the row)
+  // steps in order: tiles bx, bx + gx, ... below the tile count, and in each
+  // the K-part's groups (gr counts groups from the start of the row)
   struct Cursor {
-    int st, i, gr;
+    int tile, gr;
   };
   const int gr0 = ks * gpp;
   auto advance = [&](Cursor& c) {
-    ++c.st;
     if (++c.gr == gr0 + gpp) {
       c.gr = gr0;
-      ++c.i;
+      c.tile += gx;
     }
   };
   struct Stage {
@@ -1176,8 +1195,8 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
   };
   // a step's loads into registers (past the last step: loads that read nothing)
   auto load_stage = [&](Stage& sg, const Cursor& c) {
-    const bool real = c.st < steps;
-    const int c0 = ((bx + c.i * gx) * ncg + cg) * cw;
+    const bool real = c.tile < tiles;
+    const int c0 = (c.tile * ncg + cg) * cw;
     const int ncols = real ? n - c0 : 0;
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(wexp + static_cast<int64_t>(c0) * row_bytes,
                                                 static_cast<int64_t>(ncols) * row_bytes);
@@ -1399,7 +1418,7 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
         for (int q2 = 0; q2 < 4; ++q2) acc[mb] = __builtin_fmaf(sv[q2], d[mb][q2], acc[mb]);
     }
     if (c.gr == gr0 + gpp - 1) {
-      const int col = ((bx + c.i * gx) * ncg + cg) * cw + j;
+      const int col = (c.tile * ncg + cg) * cw + j;
       float out[NACC];
       bool store = true;
       if (S == 1) {
@@ -1431,6 +1450,9 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
         }
       }
       if (store) {
+        // (the output's descriptor is built where it is used: its arguments
+        // are not needed before the first loads)
+        const __amdgpu_buffer_rsrc_t yres = make_rsrc(p.y, p.y_bytes);
 #pragma unroll
         for (int mb = 0; mb < NACC; ++mb) {
           const int em = WIDE ? 4 * qd + mb : 4 * mb + qd;
@@ -1444,33 +1466,51 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
     }
   };
 
-  for (int c0 = 0; c0 < total; c0 += MB) {
-    mcount = min(MB, total - c0);
-    // A thread's first staging item is loaded before the first group's
-    // weights, then the first group's loads are in flight while the window is
-    // staged.  A wave's loads complete in issue order, so the staging waits
-    // for its activations only, not for the weights behind them.
-    const int nstage = mcount * units;
-    uint32_t xfirst[16];
-    if (tid < nstage) {
-      const int mi = tid / units, un = tid - (tid / units) * units;
-      const int e = c0 + mi;
-      const int row = IDX ? s_list[e] / p.slots : e;
-      const u32x4* src = reinterpret_cast<const u32x4*>(p.x + static_cast<int64_t>(row) * p.k +
-                                                        static_cast<int64_t>(un) * 32);
+  // A pass's first loads: each thread's first staging item, then the first
+  // group's weights.  A wave's loads complete in issue order, so the staging
+  // waits for its activations only, not for the weights behind them.  Every
+  // thread loads (one past the pass's staging items reads the pass's first
+  // unit, which always exists, and never uses it): with no branch ahead of
+  // them, only address arithmetic precedes a block's first loads.
+  uint32_t xfirst[16];
+  Stage sa, sb;
+  Cursor cl, cc;
+  auto issue_pass = [&](int c0) {
+    const int nst = min(MB, total - c0) * units;
+    int mi, un;
+    split_units(tid < nst ? tid : 0, units, inv_units, mi, un);
+    const int e = c0 + mi;
+    const int row = IDX ? s_list[e] / p.slots : e;
+    const u32x4* src = reinterpret_cast<const u32x4*>(p.x + static_cast<int64_t>(row) * p.k +
+                                                      static_cast<int64_t>(un) * 32);
 #pragma unroll
-      for (int pc = 0; pc < 4; ++pc) {
-        const u32x4 v = src[pc];
-        xfirst[4 * pc] = v.x;
-        xfirst[4 * pc + 1] = v.y;
-        xfirst[4 * pc + 2] = v.z;
-        xfirst[4 * pc + 3] = v.w;
-      }
+    for (int pc = 0; pc < 4; ++pc) {
+      const u32x4 v = src[pc];
+      xfirst[4 * pc] = v.x;
+      xfirst[4 * pc + 1] = v.y;
+      xfirst[4 * pc + 2] = v.z;
+      xfirst[4 * pc + 3] = v.w;
     }
-    Cursor cl = {0, 0, gr0}, cc = {0, 0, gr0};
-    Stage sa, sb;
+    // (keeps the activations' loads ahead of the weights' in issue order)
+    asm volatile("" ::: "memory");
+    cl = Cursor{bx, gr0};
     load_stage(sa, cl);
+    // (and the weights' loads ahead of the pass's LDS work)
+    asm volatile("" ::: "memory");
     advance(cl);
+  };
+  auto set_p_off = [&]() {
+#pragma unroll
+    for (int t = 0; t < NP; ++t) {
+      const int pc = qd * NP + t, ln = pc / 8, pp = pc % 8;
+      p_off[t] = ((ln * 16 + j) * 8 + ((pp + j / 2) & 7)) * 16;
+    }
+  };
+  for (int c0 = 0; c0 < total; c0 += MB) {
+    issue_pass(c0);
+    mcount = min(MB, total - c0);
+    const int nstage = mcount * units;
+    cc = Cursor{bx, gr0};
     if (tid < mcount) {
       const int e = c0 + tid;
       if (IDX) {
@@ -1488,7 +1528,8 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
     __syncthreads();
     // ---- stage the window: each unit's activations in slot order, and its sum ----
     for (int t = tid; t < nstage; t += NT) {
-      const int mi = t / units, un = t - (t / units) * units;
+      int mi, un;
+      split_units(t, units, inv_units, mi, un);
       uint32_t xin[16];
       if (t == tid) {
 #pragma unroll
@@ -1524,14 +1565,15 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
       xsum[mi * sstride + un] = X;
     }
     __syncthreads();
+    set_p_off();
     // double-buffered: a group's loads are in flight while the previous one
     // is computed
-    while (cc.st < steps) {
+    while (cc.tile < tiles) {
       load_stage(sb, cl);
       advance(cl);
       compute(sa, cc);
       advance(cc);
-      if (cc.st >= steps) break;
+      if (cc.tile >= tiles) break;
       load_stage(sa, cl);
       advance(cl);
       compute(sb, cc);
@@ -1571,10 +1613,16 @@ QG_MFMA_KERNEL(qrow_mfma_wide_gateup_indexed, true, true, true)
 // own strided call, so every member's bits equal that call's.
 // ---------------------------------------------------------------------------
 
+// A run's body and block count side by side: one 8-byte argument read
+// gives a block both.
+struct RunSel {
+  int32_t kind;       // which body: see the two kernels below
+  int32_t nblocks;    // blocks of the run
+};
+
 struct StackParams {
   Params run[kMaxRuns];
-  int32_t kind[kMaxRuns];         // (bits index * 3 + group index) * 2 + staging
-  int32_t nblocks[kMaxRuns];      // blocks of each run
+  RunSel sel[kMaxRuns];
   int32_t nruns;
 };
 
@@ -1586,7 +1634,7 @@ struct StackParams {
 // registers from the start of the body; indexing the by-value StackParams
 // at run time copies all of it to scratch.)
 typedef const __attribute__((address_space(4))) Params KParams;
-typedef const __attribute__((address_space(4))) int32_t KInt;
+typedef const __attribute__((address_space(4))) uint64_t KSel;
 
 // The block's run is blockIdx.y (one grid row per run), its place among
 // that run's blocks blockIdx.x; a row's blocks past its run's block count
@@ -1597,10 +1645,15 @@ typedef const __attribute__((address_space(4))) int32_t KInt;
       (const char __attribute__((address_space(4)))*)(__builtin_amdgcn_kernarg_segment_ptr());  \
   const int r_ = static_cast<int>(blockIdx.y);                                                  \
   KParams& p = reinterpret_cast<KParams*>(args_ + offsetof(StackParams, run))[r_];              \
-  const int gx = reinterpret_cast<KInt*>(args_ + offsetof(StackParams, nblocks))[r_];           \
-  const int kind = reinterpret_cast<KInt*>(args_ + offsetof(StackParams, kind))[r_];            \
+  const uint64_t sel_ = reinterpret_cast<KSel*>(args_ + offsetof(StackParams, sel))[r_];        \
+  const int gx = static_cast<int>(sel_ >> 32);         /* RunSel::nblocks */                    \
+  const int kind = static_cast<int>(sel_ & 0xffffffffu); /* RunSel::kind */                     \
   const int bx = static_cast<int>(blockIdx.x);                                                  \
   if (bx >= gx) return
+
+static_assert(offsetof(StackParams, sel) % 8 == 0 && offsetof(RunSel, kind) == 0 &&
+                  offsetof(RunSel, nblocks) == 4 && sizeof(RunSel) == 8,
+              "one 8-byte read per run, kind in its low half");
 
 // Dot-form runs: kind = (bits index * 3 + group index) * 2 + staging.
 template <int MB>
