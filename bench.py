@@ -424,6 +424,51 @@ def launch_floor(torch, kernels: int = 200, replays: int = 20) -> float:
     return e0.elapsed_time(e1) * 1e3 / (kernels * replays)
 
 
+_COPY_FLOOR = {}
+
+
+def copy_floor(torch, nbytes: int, steps: int = 200) -> float:
+    """Device time, in microseconds, of one library copy whose HBM traffic
+    equals `nbytes` (nbytes / 2 read, nbytes / 2 written), the sources
+    rotating over at least 1 GiB like the weights: a captured graph of
+    `steps` copies replayed for at least 20 ms.  A dispatch that only
+    streams that many bytes takes this long on the same device, so it is
+    the floor for a call of that size in one dispatch."""
+    half = max(4096, (nbytes // 2 + 4095) // 4096 * 4096)
+    if half in _COPY_FLOOR:
+        return _COPY_FLOOR[half]
+    copies = max(2, -(-ROTATE_BYTES // half))
+    src = torch.empty((copies, half), dtype=torch.uint8, device="cuda")
+    dst = torch.empty((copies, half), dtype=torch.uint8, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(3):
+            dst[i % copies].copy_(src[i % copies])
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            dst[i % copies].copy_(src[(i * 7) % copies])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    replays = max(5, int(20.0 / max(e0.elapsed_time(e1) / 3, 1e-3)) + 1)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (steps * replays)
+    del g, src, dst
+    torch.cuda.empty_cache()
+    _COPY_FLOOR[half] = round(us, 3)
+    return _COPY_FLOOR[half]
+
+
 def cpu_baseline(budget_s: float = 12.0):
     """The oracle, as it stands, on a bounded sample of LM-head columns at a
     1-row window, threads = host cores (capped at 16)."""
@@ -593,6 +638,11 @@ def main():
             print(f"# {key}: {ms2 * 1e3:.3f} us, {g2:.1f} GB/s; graph {msg * 1e3:.3f} us", file=sys.stderr, flush=True)
             del w2
             torch.cuda.empty_cache()
+        # the same traffic streamed by a library copy, for the calls small
+        # enough that a dispatch's fixed costs matter
+        for v in extra.values():
+            if v["bytes"] <= (32 << 20):
+                v["copy_floor_us"] = copy_floor(torch, v["bytes"])
         out["workloads"] = extra
         floor = launch_floor(torch)
         out["launch_floor_us"] = round(floor, 3)
