@@ -1587,9 +1587,21 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
 // gate/up pairs, plain/strided or indexed calls.  Pairing and routing are
 // compiled in or out, so no kernel holds the registers of a path it never
 // takes.  Indexed calls stage at most kIndexedWindow routed rows a pass.
+// Waves per SIMD the register allocation must leave room for.  The
+// block-diagonal indexed kernels of the routed window (4 rows) with 8-bit
+// codes, or 4-bit codes in groups of 64 or 128, fit 96 VGPRs with no spill,
+// so a CU holds 5 of their blocks instead of 4: the 4/64 experts (128 x 1024
+// x 2048, 16 rows x 8 slots, 1,360 routed blocks) measured 23.9 against
+// 24.7 us and the gate/up pair 43.3 against 45.6 us on one box.  (Other
+// widths and groups spill at 96.)  Elsewhere the allocator's choice stands.
+template <int B, int G, int MB, bool WIDE, bool IDX> struct MinWaves {
+  static constexpr int v = (IDX && !WIDE && MB == 4 && (B == 8 || (B == 4 && G >= 64))) ? 5 : 1;
+};
+
 #define QG_MFMA_KERNEL(NAME, WIDE, GU, IDX)                                                  \
   template <int B, int G, int MB>                                                            \
-  __global__ __launch_bounds__(MWaves<MB>::v * kWave) void NAME(const Params p) {            \
+  __global__ __launch_bounds__(MWaves<MB>::v * kWave)                                        \
+  __attribute__((amdgpu_waves_per_eu(MinWaves<B, G, MB, WIDE, IDX>::v))) void NAME(const Params p) { \
     extern __shared__ __align__(16) unsigned char smem[];                                    \
     __shared__ int s_wave_cnt[MWaves<MB>::v];                                                \
     __shared__ int s_xrow[QGEMV_MAX_WINDOW];                                                 \
