@@ -170,7 +170,7 @@ void init_device(DeviceInfo* info) {
                                         static_cast<int>(qg::kMaxDynamicLds)) != hipSuccess)
             return;
         const qg::WideEntry& we = qg::wide_entry(bi, gi);
-        for (qg::KernelFn fn : {e.mfma[v], e.mfma_gateup[v], we.k[v], we.gateup[v],
+        for (qg::KernelFn fn : {e.mfma[v], e.mfma_gateup[v], we.k[v], we.gateup[v], v == 0 ? e.mfma_dyn : nullptr,
                                 v < 3 ? e.mfma_indexed[v] : nullptr, v < 3 ? e.mfma_gateup_indexed[v] : nullptr,
                                 v < 3 ? we.indexed[v] : nullptr, v < 3 ? we.gateup_indexed[v] : nullptr})
           if (fn && hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -236,10 +236,10 @@ size_t lds_bytes(const qgemv_handle* h, int var, int stage) {
 // the routed list of an indexed call, and one load-group slot per wave (which
 // also holds the wave's K-split partial sums at a tile's end).  Returns false
 // when it exceeds one block's LDS.
-bool mfma_plan(const qgemv_handle* h, int var, bool indexed, size_t* lds) {
+bool mfma_plan(const qgemv_handle* h, int var, bool indexed, size_t* lds, int waves_override = 0) {
   const size_t mb = static_cast<size_t>(qg::kWindows[var]);
   const size_t units = static_cast<size_t>(h->d.k) / 32;
-  const size_t waves = static_cast<size_t>(h->entry->mfma_waves[var]);
+  const size_t waves = static_cast<size_t>(waves_override ? waves_override : h->entry->mfma_waves[var]);
   const size_t b = mb * (units * 64 + 16) + 256 * static_cast<size_t>(h->entry->mfma_group) + mb * (units + 4) * 4 +
                    (indexed ? qg::kMaxList * 4 : 0) + waves * h->entry->mfma_slot;
   if (b > qg::kMaxMfmaLds) return false;
@@ -359,6 +359,19 @@ int launch(const qgemv_handle* h, const uint16_t* x, int32_t m, float* y, int64_
   // (the matrix-core kernels always take staging 0: their slot 1 holds the
   // gate/up kernel's occupancy; indexed calls size their grid per expert)
   dim3 grid(1u, 1u);
+  // A 1-row plain call on a matrix of many 16-column units with no K split:
+  // one block of kDynWaves waves per CU, each CU's share of units handed out
+  // among its waves (so that the CU's waves end together), when its LDS fits.
+  const int64_t units16 = (h->d.n + 15) / 16;
+  size_t dyn_lds = 0;
+  if (mfma && !indexed && !up && h->arith != QGEMV_ARITH_WIDE && var == 0 && h->ksplit == 1 &&
+      h->entry->mfma_dyn && units16 >= 2LL * qg::kDynWaves * dev->cus &&
+      mfma_plan(h, var, false, &dyn_lds, qg::kDynWaves)) {
+    p.tiles = static_cast<int32_t>(units16);
+    grid.x = static_cast<unsigned>(dev->cus);
+    return enqueue(reinterpret_cast<const void*>(h->entry->mfma_dyn), grid, dim3(qg::kDynWaves * qg::kWave),
+                   dyn_lds, stream, p);
+  }
   if (!indexed) {
     const int oslot = mfma ? (up ? 1 : 0) : stage;
     int occ = h->occupancy[var][oslot].load(std::memory_order_relaxed);

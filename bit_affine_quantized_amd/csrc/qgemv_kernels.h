@@ -1026,6 +1026,10 @@ template <int B, int G> struct MGroup {
   static_assert(R * B % 8 == 0 && SLANES <= 64, "group geometry");
 };
 
+// Waves per block of the 1-row kernel that hands out units in the block:
+// 3 a SIMD, the whole CU's share of a large matrix in one block.
+constexpr int kDynWaves = 12;
+
 // Waves per block: a wide window's activations are staged once for 8 waves.
 template <int MB> struct MWaves {
   static constexpr int v = MB >= 8 ? 8 : 4;
@@ -1075,12 +1079,14 @@ __device__ __forceinline__ void split_units(int t, int units, float inv_units, i
 // holds k-quarter q of all four units of the round; each unit is then one
 // 16x16x32 product over every window row at once (A row i = window row i),
 // and lane (j, q) folds window rows 4q .. 4q+3 of column j.
-template <int B, int G, int MB, bool WIDE = false, bool GU = false, bool IDX = false, class PT = const Params>
+template <int B, int G, int MB, bool WIDE = false, bool GU = false, bool IDX = false, bool DYN = false,
+          class PT = const Params>
 __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, unsigned char* smem,
-                                          int* s_wave_cnt, int* s_xrow, int64_t* s_yoff) {
+                                          int* s_wave_cnt, int* s_xrow, int64_t* s_yoff, int* s_next = nullptr) {
+  static_assert(!DYN || (MB == 1 && !GU && !IDX), "units handed out in a block: 1-row plain calls");
   using MG = MGroup<B, G>;
   constexpr int R = MG::R, SSZ = MG::SSZ;
-  constexpr int NW = MWaves<MB>::v, NT = NW * kWave;
+  constexpr int NW = DYN ? kDynWaves : MWaves<MB>::v, NT = NW * kWave;
   constexpr int NMB = (MB + 3) / 4;         // 4-row blocks of the window
   // outputs each lane folds: one per 4-row block, or (wide form) window rows
   // 4q .. 4q+3 of its column, as many as the window can hold
@@ -1179,24 +1185,49 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
   // steps in order: tiles bx, bx + gx, ... below the tile count, and in each
   // the K-part's groups (gr counts groups from the start of the row)
   struct Cursor {
-    int tile, gr;
+    int tile, gr, k;   // k: units taken so far (units handed out in the block)
   };
   const int gr0 = ks * gpp;
+  // Units handed out in the block (DYN, 1-row calls with no K split): the
+  // block owns 16-column units [u0, u1); each wave takes its first two
+  // statically (u0 + wave, u0 + NW + wave) and then the next free one from
+  // an LDS counter, so faster waves take more and the block's waves end
+  // together.  A column's arithmetic does not depend on its wave.
+  int u0 = 0, u1 = 0;
+  if constexpr (DYN) {
+    u0 = static_cast<int>(static_cast<int64_t>(bx) * tiles / gx);
+    u1 = static_cast<int>(static_cast<int64_t>(bx + 1) * tiles / gx);
+  }
+  const int tend = DYN ? u1 : tiles;   // a cursor is past the end at tile >= tend
+  auto next_unit = [&](Cursor& c) -> int {
+    ++c.k;
+    if (c.k == 1) return u0 + NW + wv;
+    if (c.tile >= u1) return u1;
+    int u = 0;
+    if (lane == 0) u = atomicAdd(s_next, 1);
+    return __builtin_amdgcn_readfirstlane(u);
+  };
   auto advance = [&](Cursor& c) {
     if (++c.gr == gr0 + gpp) {
       c.gr = gr0;
-      c.tile += gx;
+      if constexpr (DYN) {
+        c.tile = next_unit(c);
+      } else {
+        c.tile += gx;
+      }
     }
   };
   struct Stage {
     u32x4 w[MG::WLD];
     uint32_t s[SSZ / 4];
     uint32_t b[SSZ / 4];
+    Cursor cur;   // the step these loads belong to
   };
   // a step's loads into registers (past the last step: loads that read nothing)
   auto load_stage = [&](Stage& sg, const Cursor& c) {
-    const bool real = c.tile < tiles;
-    const int c0 = (c.tile * ncg + cg) * cw;
+    sg.cur = c;
+    const bool real = c.tile < tend;
+    const int c0 = DYN ? c.tile * 16 : (c.tile * ncg + cg) * cw;
     const int ncols = real ? n - c0 : 0;
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(wexp + static_cast<int64_t>(c0) * row_bytes,
                                                 static_cast<int64_t>(ncols) * row_bytes);
@@ -1418,7 +1449,7 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
         for (int q2 = 0; q2 < 4; ++q2) acc[mb] = __builtin_fmaf(sv[q2], d[mb][q2], acc[mb]);
     }
     if (c.gr == gr0 + gpp - 1) {
-      const int col = (c.tile * ncg + cg) * cw + j;
+      const int col = (DYN ? c.tile * 16 : (c.tile * ncg + cg) * cw) + j;
       float out[NACC];
       bool store = true;
       if (S == 1) {
@@ -1493,7 +1524,7 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
     }
     // (keeps the activations' loads ahead of the weights' in issue order)
     asm volatile("" ::: "memory");
-    cl = Cursor{bx, gr0};
+    cl = Cursor{DYN ? u0 + wv : bx, gr0, 0};
     load_stage(sa, cl);
     // (and the weights' loads ahead of the pass's LDS work)
     asm volatile("" ::: "memory");
@@ -1510,7 +1541,7 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
     issue_pass(c0);
     mcount = min(MB, total - c0);
     const int nstage = mcount * units;
-    cc = Cursor{bx, gr0};
+    cc = Cursor{bx, gr0, 0};
     if (tid < mcount) {
       const int e = c0 + tid;
       if (IDX) {
@@ -1523,6 +1554,7 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
         s_yoff[tid] = static_cast<int64_t>(e) * p.ldy;
       }
     }
+    if (DYN && tid == 0) *s_next = u0 + 2 * NW;   // read after the barrier below
     for (int t = tid; t < ZB / 4; t += NT) reinterpret_cast<uint32_t*>(zero_area)[t] = 0u;
     set_bases();
     __syncthreads();
@@ -1568,16 +1600,30 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
     set_p_off();
     // double-buffered: a group's loads are in flight while the previous one
     // is computed
-    while (cc.tile < tiles) {
-      load_stage(sb, cl);
-      advance(cl);
-      compute(sa, cc);
-      advance(cc);
-      if (cc.tile >= tiles) break;
-      load_stage(sa, cl);
-      advance(cl);
-      compute(sb, cc);
-      advance(cc);
+    if constexpr (DYN) {
+      // the compute side follows the stages' own cursors (the units the
+      // load side was handed)
+      while (sa.cur.tile < tend) {
+        load_stage(sb, cl);
+        advance(cl);
+        compute(sa, sa.cur);
+        if (sb.cur.tile >= tend) break;
+        load_stage(sa, cl);
+        advance(cl);
+        compute(sb, sb.cur);
+      }
+    } else {
+      while (cc.tile < tiles) {
+        load_stage(sb, cl);
+        advance(cl);
+        compute(sa, cc);
+        advance(cc);
+        if (cc.tile >= tiles) break;
+        load_stage(sa, cl);
+        advance(cl);
+        compute(sb, cc);
+        advance(cc);
+      }
     }
     __syncthreads();    // LDS window reused by the next pass of routed rows
   }
@@ -1617,6 +1663,19 @@ QG_MFMA_KERNEL(qrow_mfma_wide_indexed, true, false, true)
 QG_MFMA_KERNEL(qrow_mfma_gateup_indexed, false, true, true)
 QG_MFMA_KERNEL(qrow_mfma_wide_gateup_indexed, true, true, true)
 #undef QG_MFMA_KERNEL
+
+// The 1-row block-diagonal kernel for matrices of many columns: one block of
+// kDynWaves waves per CU, its 16-column units handed out in the block.
+template <int B, int G>
+__global__ __launch_bounds__(kDynWaves * kWave) void qrow_mfma_dyn(const Params p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int s_wave_cnt[kDynWaves];
+  __shared__ int s_xrow[QGEMV_MAX_WINDOW];
+  __shared__ int64_t s_yoff[QGEMV_MAX_WINDOW];
+  __shared__ int s_next;
+  mfma_body<B, G, 1, false, false, false, true>(p, blockIdx.x, gridDim.x, smem, s_wave_cnt, s_xrow, s_yoff,
+                                                &s_next);
+}
 
 // ---------------------------------------------------------------------------
 // Fused stack: the runs of a fused projection (each a matrix of one width and
@@ -1784,6 +1843,7 @@ struct Entry {
   KernelFn mfma_gateup[5];  // the same for gate/up pairs
   KernelFn mfma_indexed[3];         // indexed calls (windows of 1, 2 and 4 routed rows)
   KernelFn mfma_gateup_indexed[3];  // indexed gate/up pairs
+  KernelFn mfma_dyn;    // 1-row kernel with units handed out in the block
   int mfma_slot;        // bytes of one wave's LDS slot (one load group)
   int mfma_waves[5];    // waves per block of the matrix-core kernels by window variant
   int mfma_group;       // 128-code rounds per load group (k is a multiple of 128 * this)
@@ -1820,6 +1880,9 @@ Entry make_entry() {
   e.generic_rows[2] = RowsPerLane<B, 4>::v;
   e.generic_rows[3] = RowsPerLane<B, 8>::v;
   e.generic_rows[4] = RowsPerLane<B, 16>::v;
+  // (its 12-wave block holds 3 waves a SIMD, 168 VGPRs: the 5-bit group-32
+  // body needs more, so that pair keeps the tile walk)
+  if constexpr (!(B == 5 && G == 32)) e.mfma_dyn = qrow_mfma_dyn<B, G>;
   e.mfma[0] = qrow_mfma<B, G, 1>;
   e.mfma[1] = qrow_mfma<B, G, 2>;
   e.mfma[2] = qrow_mfma<B, G, 4>;
