@@ -170,7 +170,7 @@ void init_device(DeviceInfo* info) {
                                         static_cast<int>(qg::kMaxDynamicLds)) != hipSuccess)
             return;
         const qg::WideEntry& we = qg::wide_entry(bi, gi);
-        for (qg::KernelFn fn : {e.mfma[v], e.mfma_gateup[v], we.k[v], we.gateup[v], v == 0 ? e.mfma_dyn : nullptr,
+        for (qg::KernelFn fn : {e.mfma[v], e.mfma_gateup[v], we.k[v], we.gateup[v], e.mfma_dyn[v],
                                 v < 3 ? e.mfma_indexed[v] : nullptr, v < 3 ? e.mfma_gateup_indexed[v] : nullptr,
                                 v < 3 ? we.indexed[v] : nullptr, v < 3 ? we.gateup_indexed[v] : nullptr})
           if (fn && hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -359,17 +359,17 @@ int launch(const qgemv_handle* h, const uint16_t* x, int32_t m, float* y, int64_
   // (the matrix-core kernels always take staging 0: their slot 1 holds the
   // gate/up kernel's occupancy; indexed calls size their grid per expert)
   dim3 grid(1u, 1u);
-  // A 1-row plain call on a matrix of many 16-column units with no K split:
-  // one block of kDynWaves waves per CU, each CU's share of units handed out
-  // among its waves (so that the CU's waves end together), when its LDS fits.
+  // A plain or strided call on a matrix of many 16-column units with no K
+  // split: one block per CU, each CU's share of units handed out among its
+  // waves (so that the CU's waves end together), when its kernel and LDS fit.
   const int64_t units16 = (h->d.n + 15) / 16;
+  const int dyn_waves = qg::kWindows[var] >= 16 ? qg::DynWaves<16>::v : qg::DynWaves<1>::v;
   size_t dyn_lds = 0;
-  if (mfma && !indexed && !up && h->arith != QGEMV_ARITH_WIDE && var == 0 && h->ksplit == 1 &&
-      h->entry->mfma_dyn && units16 >= 2LL * qg::kDynWaves * dev->cus &&
-      mfma_plan(h, var, false, &dyn_lds, qg::kDynWaves)) {
+  if (mfma && !indexed && !up && h->arith != QGEMV_ARITH_WIDE && h->ksplit == 1 && h->entry->mfma_dyn[var] &&
+      units16 >= 2LL * dyn_waves * dev->cus && mfma_plan(h, var, false, &dyn_lds, dyn_waves)) {
     p.tiles = static_cast<int32_t>(units16);
     grid.x = static_cast<unsigned>(dev->cus);
-    return enqueue(reinterpret_cast<const void*>(h->entry->mfma_dyn), grid, dim3(qg::kDynWaves * qg::kWave),
+    return enqueue(reinterpret_cast<const void*>(h->entry->mfma_dyn[var]), grid, dim3(dyn_waves * qg::kWave),
                    dyn_lds, stream, p);
   }
   if (!indexed) {

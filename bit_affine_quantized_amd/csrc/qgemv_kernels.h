@@ -1026,9 +1026,12 @@ template <int B, int G> struct MGroup {
   static_assert(R * B % 8 == 0 && SLANES <= 64, "group geometry");
 };
 
-// Waves per block of the 1-row kernel that hands out units in the block:
-// 3 a SIMD, the whole CU's share of a large matrix in one block.
-constexpr int kDynWaves = 12;
+// Waves per block of the kernels that hand out units in the block: the
+// whole CU's share of a large matrix in one block, 3 waves a SIMD for
+// windows of up to 8 rows, 2 for 16 (those kernels hold more registers).
+template <int MB> struct DynWaves {
+  static constexpr int v = MB >= 16 ? 8 : 12;
+};
 
 // Waves per block: a wide window's activations are staged once for 8 waves.
 template <int MB> struct MWaves {
@@ -1083,10 +1086,10 @@ template <int B, int G, int MB, bool WIDE = false, bool GU = false, bool IDX = f
           class PT = const Params>
 __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, unsigned char* smem,
                                           int* s_wave_cnt, int* s_xrow, int64_t* s_yoff, int* s_next = nullptr) {
-  static_assert(!DYN || (MB == 1 && !GU && !IDX), "units handed out in a block: 1-row plain calls");
+  static_assert(!DYN || (!GU && !IDX), "units handed out in a block: plain and strided calls");
   using MG = MGroup<B, G>;
   constexpr int R = MG::R, SSZ = MG::SSZ;
-  constexpr int NW = DYN ? kDynWaves : MWaves<MB>::v, NT = NW * kWave;
+  constexpr int NW = DYN ? DynWaves<MB>::v : MWaves<MB>::v, NT = NW * kWave;
   constexpr int NMB = (MB + 3) / 4;         // 4-row blocks of the window
   // outputs each lane folds: one per 4-row block, or (wide form) window rows
   // 4q .. 4q+3 of its column, as many as the window can hold
@@ -1188,7 +1191,7 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
     int tile, gr, k;   // k: units taken so far (units handed out in the block)
   };
   const int gr0 = ks * gpp;
-  // Units handed out in the block (DYN, 1-row calls with no K split): the
+  // Units handed out in the block (DYN, calls with no K split): the
   // block owns 16-column units [u0, u1); each wave takes its first two
   // statically (u0 + wave, u0 + NW + wave) and then the next free one from
   // an LDS counter, so faster waves take more and the block's waves end
@@ -1664,17 +1667,23 @@ QG_MFMA_KERNEL(qrow_mfma_gateup_indexed, false, true, true)
 QG_MFMA_KERNEL(qrow_mfma_wide_gateup_indexed, true, true, true)
 #undef QG_MFMA_KERNEL
 
-// The 1-row block-diagonal kernel for matrices of many columns: one block of
-// kDynWaves waves per CU, its 16-column units handed out in the block.
-template <int B, int G>
-__global__ __launch_bounds__(kDynWaves * kWave) void qrow_mfma_dyn(const Params p) {
+// Which (bits, group, window) bodies fit the block's register share with no
+// spill (from the compiler's resource report at 12 and 8 waves a block).
+template <int B, int G, int MB> struct DynFits {
+  static constexpr bool v = !(B == 5 && (G == 32 || MB == 8));
+};
+
+// The block-diagonal kernels for matrices of many columns: one block of
+// DynWaves waves per CU, its 16-column units handed out in the block.
+template <int B, int G, int MB>
+__global__ __launch_bounds__(DynWaves<MB>::v * kWave) void qrow_mfma_dyn(const Params p) {
   extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ int s_wave_cnt[kDynWaves];
+  __shared__ int s_wave_cnt[DynWaves<MB>::v];
   __shared__ int s_xrow[QGEMV_MAX_WINDOW];
   __shared__ int64_t s_yoff[QGEMV_MAX_WINDOW];
   __shared__ int s_next;
-  mfma_body<B, G, 1, false, false, false, true>(p, blockIdx.x, gridDim.x, smem, s_wave_cnt, s_xrow, s_yoff,
-                                                &s_next);
+  mfma_body<B, G, MB, false, false, false, true>(p, blockIdx.x, gridDim.x, smem, s_wave_cnt, s_xrow, s_yoff,
+                                                 &s_next);
 }
 
 // ---------------------------------------------------------------------------
@@ -1843,7 +1852,7 @@ struct Entry {
   KernelFn mfma_gateup[5];  // the same for gate/up pairs
   KernelFn mfma_indexed[3];         // indexed calls (windows of 1, 2 and 4 routed rows)
   KernelFn mfma_gateup_indexed[3];  // indexed gate/up pairs
-  KernelFn mfma_dyn;    // 1-row kernel with units handed out in the block
+  KernelFn mfma_dyn[5];  // units handed out in the block, by window variant (null: not built)
   int mfma_slot;        // bytes of one wave's LDS slot (one load group)
   int mfma_waves[5];    // waves per block of the matrix-core kernels by window variant
   int mfma_group;       // 128-code rounds per load group (k is a multiple of 128 * this)
@@ -1880,9 +1889,13 @@ Entry make_entry() {
   e.generic_rows[2] = RowsPerLane<B, 4>::v;
   e.generic_rows[3] = RowsPerLane<B, 8>::v;
   e.generic_rows[4] = RowsPerLane<B, 16>::v;
-  // (its 12-wave block holds 3 waves a SIMD, 168 VGPRs: the 5-bit group-32
-  // body needs more, so that pair keeps the tile walk)
-  if constexpr (!(B == 5 && G == 32)) e.mfma_dyn = qrow_mfma_dyn<B, G>;
+  // (a 12-wave block holds 3 waves a SIMD, at most 168 VGPRs, and an 8-wave
+  // one 2: the bodies that need more keep the tile walk)
+  if constexpr (DynFits<B, G, 1>::v) e.mfma_dyn[0] = qrow_mfma_dyn<B, G, 1>;
+  if constexpr (DynFits<B, G, 2>::v) e.mfma_dyn[1] = qrow_mfma_dyn<B, G, 2>;
+  if constexpr (DynFits<B, G, 4>::v) e.mfma_dyn[2] = qrow_mfma_dyn<B, G, 4>;
+  if constexpr (DynFits<B, G, 8>::v) e.mfma_dyn[3] = qrow_mfma_dyn<B, G, 8>;
+  if constexpr (DynFits<B, G, 16>::v) e.mfma_dyn[4] = qrow_mfma_dyn<B, G, 16>;
   e.mfma[0] = qrow_mfma<B, G, 1>;
   e.mfma[1] = qrow_mfma<B, G, 2>;
   e.mfma[2] = qrow_mfma<B, G, 4>;
