@@ -170,7 +170,7 @@ void init_device(DeviceInfo* info) {
                                         static_cast<int>(qg::kMaxDynamicLds)) != hipSuccess)
             return;
         const qg::WideEntry& we = qg::wide_entry(bi, gi);
-        for (qg::KernelFn fn : {e.mfma[v], e.mfma_gateup[v], we.k[v], we.gateup[v], e.mfma_dyn[v],
+        for (qg::KernelFn fn : {e.mfma[v], e.mfma_gateup[v], we.k[v], we.gateup[v], e.mfma_dyn[v], we.dyn[v],
                                 v < 3 ? e.mfma_indexed[v] : nullptr, v < 3 ? e.mfma_gateup_indexed[v] : nullptr,
                                 v < 3 ? we.indexed[v] : nullptr, v < 3 ? we.gateup_indexed[v] : nullptr})
           if (fn && hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -365,12 +365,13 @@ int launch(const qgemv_handle* h, const uint16_t* x, int32_t m, float* y, int64_
   const int64_t units16 = (h->d.n + 15) / 16;
   const int dyn_waves = qg::kWindows[var] >= 16 ? qg::DynWaves<16>::v : qg::DynWaves<1>::v;
   size_t dyn_lds = 0;
-  if (mfma && !indexed && !up && h->arith != QGEMV_ARITH_WIDE && h->ksplit == 1 && h->entry->mfma_dyn[var] &&
-      units16 >= 2LL * dyn_waves * dev->cus && mfma_plan(h, var, false, &dyn_lds, dyn_waves)) {
+  const qg::KernelFn dyn_fn = !mfma ? nullptr
+                              : (h->arith == QGEMV_ARITH_WIDE ? h->wide->dyn[var] : h->entry->mfma_dyn[var]);
+  if (dyn_fn && !indexed && !up && h->ksplit == 1 && units16 >= 2LL * dyn_waves * dev->cus &&
+      mfma_plan(h, var, false, &dyn_lds, dyn_waves)) {
     p.tiles = static_cast<int32_t>(units16);
     grid.x = static_cast<unsigned>(dev->cus);
-    return enqueue(reinterpret_cast<const void*>(h->entry->mfma_dyn[var]), grid, dim3(dyn_waves * qg::kWave),
-                   dyn_lds, stream, p);
+    return enqueue(reinterpret_cast<const void*>(dyn_fn), grid, dim3(dyn_waves * qg::kWave), dyn_lds, stream, p);
   }
   if (!indexed) {
     const int oslot = mfma ? (up ? 1 : 0) : stage;

@@ -1669,22 +1669,27 @@ QG_MFMA_KERNEL(qrow_mfma_wide_gateup_indexed, true, true, true)
 
 // Which (bits, group, window) bodies fit the block's register share with no
 // spill (from the compiler's resource report at 12 and 8 waves a block).
-template <int B, int G, int MB> struct DynFits {
-  static constexpr bool v = !(B == 5 && (G == 32 || MB == 8));
+template <int B, int G, int MB, bool WIDE = false> struct DynFits {
+  static constexpr bool v = WIDE ? !(B == 5 && G <= 64 && MB >= 2 && MB <= 8)
+                                 : !(B == 5 && (G == 32 || MB == 8));
 };
 
 // The block-diagonal kernels for matrices of many columns: one block of
 // DynWaves waves per CU, its 16-column units handed out in the block.
-template <int B, int G, int MB>
-__global__ __launch_bounds__(DynWaves<MB>::v * kWave) void qrow_mfma_dyn(const Params p) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ int s_wave_cnt[DynWaves<MB>::v];
-  __shared__ int s_xrow[QGEMV_MAX_WINDOW];
-  __shared__ int64_t s_yoff[QGEMV_MAX_WINDOW];
-  __shared__ int s_next;
-  mfma_body<B, G, MB, false, false, false, true>(p, blockIdx.x, gridDim.x, smem, s_wave_cnt, s_xrow, s_yoff,
-                                                 &s_next);
-}
+#define QG_DYN_KERNEL(NAME, WIDE)                                                             \
+  template <int B, int G, int MB>                                                            \
+  __global__ __launch_bounds__(DynWaves<MB>::v * kWave) void NAME(const Params p) {          \
+    extern __shared__ __align__(16) unsigned char smem[];                                    \
+    __shared__ int s_wave_cnt[DynWaves<MB>::v];                                              \
+    __shared__ int s_xrow[QGEMV_MAX_WINDOW];                                                 \
+    __shared__ int64_t s_yoff[QGEMV_MAX_WINDOW];                                             \
+    __shared__ int s_next;                                                                   \
+    mfma_body<B, G, MB, WIDE, false, false, true>(p, blockIdx.x, gridDim.x, smem, s_wave_cnt, s_xrow, \
+                                                  s_yoff, &s_next);                          \
+  }
+QG_DYN_KERNEL(qrow_mfma_dyn, false)
+QG_DYN_KERNEL(qrow_mfma_wide_dyn, true)
+#undef QG_DYN_KERNEL
 
 // ---------------------------------------------------------------------------
 // Fused stack: the runs of a fused projection (each a matrix of one width and
@@ -1926,6 +1931,7 @@ Entry make_entry() {
 // The wide-window matrix-core kernels of one (bits, group) by window variant.
 struct WideEntry {
   KernelFn k[5];
+  KernelFn dyn[5];      // units handed out in the block (null: not built)
   KernelFn gateup[5];   // gate/up pairs
   KernelFn indexed[3];  // indexed calls (windows of 1, 2 and 4 routed rows)
   KernelFn gateup_indexed[3];
@@ -1934,6 +1940,11 @@ struct WideEntry {
 template <int B, int G>
 WideEntry make_wide_entry() {
   WideEntry e{};
+  if constexpr (DynFits<B, G, 1, true>::v) e.dyn[0] = qrow_mfma_wide_dyn<B, G, 1>;
+  if constexpr (DynFits<B, G, 2, true>::v) e.dyn[1] = qrow_mfma_wide_dyn<B, G, 2>;
+  if constexpr (DynFits<B, G, 4, true>::v) e.dyn[2] = qrow_mfma_wide_dyn<B, G, 4>;
+  if constexpr (DynFits<B, G, 8, true>::v) e.dyn[3] = qrow_mfma_wide_dyn<B, G, 8>;
+  if constexpr (DynFits<B, G, 16, true>::v) e.dyn[4] = qrow_mfma_wide_dyn<B, G, 16>;
   e.k[0] = qrow_mfma_wide<B, G, 1>;
   e.k[1] = qrow_mfma_wide<B, G, 2>;
   e.k[2] = qrow_mfma_wide<B, G, 4>;
