@@ -363,7 +363,7 @@ int launch(const qgemv_handle* h, const uint16_t* x, int32_t m, float* y, int64_
   // split: one block per CU, each CU's share of units handed out among its
   // waves (so that the CU's waves end together), when its kernel and LDS fit.
   const int64_t units16 = (h->d.n + 15) / 16;
-  const int dyn_waves = qg::kWindows[var] >= 16 ? qg::DynWaves<16>::v : qg::DynWaves<1>::v;
+  const int dyn_waves = qg::dyn_waves(h->d.bits, qg::kWindows[var]);
   size_t dyn_lds = 0;
   const qg::KernelFn dyn_fn = !mfma ? nullptr
                               : (h->arith == QGEMV_ARITH_WIDE ? h->wide->dyn[var] : h->entry->mfma_dyn[var]);

@@ -1028,9 +1028,15 @@ template <int B, int G> struct MGroup {
 
 // Waves per block of the kernels that hand out units in the block: the
 // whole CU's share of a large matrix in one block, 3 waves a SIMD for
-// windows of up to 8 rows, 2 for 16 (those kernels hold more registers).
-template <int MB> struct DynWaves {
-  static constexpr int v = MB >= 16 ? 8 : 12;
+// windows of up to 8 rows.  At 16 rows the staged window takes 64 KiB of LDS
+// at K = 2048, which leaves room for 11 group slots of 2-, 4-, 6- and 8-bit
+// codes (3 waves on three SIMDs, 2 on the fourth) but only 8 of the larger
+// 3- and 5-bit slots.
+__host__ __device__ constexpr int dyn_waves(int b, int mb) {
+  return mb < 16 ? 12 : ((b == 3 || b == 5) ? 8 : 11);
+}
+template <int B, int MB> struct DynWaves {
+  static constexpr int v = dyn_waves(B, MB);
 };
 
 // Waves per block: a wide window's activations are staged once for 8 waves.
@@ -1089,7 +1095,7 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
   static_assert(!DYN || (!GU && !IDX), "units handed out in a block: plain and strided calls");
   using MG = MGroup<B, G>;
   constexpr int R = MG::R, SSZ = MG::SSZ;
-  constexpr int NW = DYN ? DynWaves<MB>::v : MWaves<MB>::v, NT = NW * kWave;
+  constexpr int NW = DYN ? DynWaves<B, MB>::v : MWaves<MB>::v, NT = NW * kWave;
   constexpr int NMB = (MB + 3) / 4;         // 4-row blocks of the window
   // outputs each lane folds: one per 4-row block, or (wide form) window rows
   // 4q .. 4q+3 of its column, as many as the window can hold
@@ -1420,13 +1426,18 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
         continue;
       }
       // A operand and unit sums of every 4-row block (rows past the window
-      // read zeros and are never stored)
+      // read zeros and are never stored); windows of more than 8 rows read
+      // each step's operands just before its products, which keeps 48 fewer
+      // registers live
+      constexpr bool LATE_A = NMB > 2;
       u32x4 av[NMB][4];
+      if constexpr (!LATE_A) {
 #pragma unroll
-      for (int mb = 0; mb < NMB; ++mb)
+        for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-        for (int sidx = 0; sidx < 4; ++sidx)
-          av[mb][sidx] = *reinterpret_cast<const u32x4*>(smem + a_grp[mb] + r * 64 + sidx * 16);
+          for (int sidx = 0; sidx < 4; ++sidx)
+            av[mb][sidx] = *reinterpret_cast<const u32x4*>(smem + a_grp[mb] + r * 64 + sidx * 16);
+      }
       // B operand: this lane's unit as 16 exact bf16 pairs
       uint32_t qp[16];
       unpack_codes<B, 32>(wu, qp);
@@ -1440,6 +1451,11 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
         bq.y = qp[4 * sidx + 1];
         bq.z = qp[4 * sidx + 2];
         bq.w = qp[4 * sidx + 3];
+        if constexpr (LATE_A) {
+#pragma unroll
+          for (int mb = 0; mb < NMB; ++mb)
+            av[mb][sidx] = *reinterpret_cast<const u32x4*>(smem + a_grp[mb] + r * 64 + sidx * 16);
+        }
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb)
           d[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[mb][sidx]),
@@ -1668,7 +1684,7 @@ QG_MFMA_KERNEL(qrow_mfma_wide_gateup_indexed, true, true, true)
 #undef QG_MFMA_KERNEL
 
 // Which (bits, group, window) bodies fit the block's register share with no
-// spill (from the compiler's resource report at 12 and 8 waves a block).
+// spill (from the compiler's resource report at the block sizes dyn_waves gives).
 template <int B, int G, int MB, bool WIDE = false> struct DynFits {
   static constexpr bool v = WIDE ? !(B == 5 && G <= 64 && MB >= 2 && MB <= 8)
                                  : !(B == 5 && (G == 32 || MB == 8));
@@ -1678,9 +1694,9 @@ template <int B, int G, int MB, bool WIDE = false> struct DynFits {
 // DynWaves waves per CU, its 16-column units handed out in the block.
 #define QG_DYN_KERNEL(NAME, WIDE)                                                             \
   template <int B, int G, int MB>                                                            \
-  __global__ __launch_bounds__(DynWaves<MB>::v * kWave) void NAME(const Params p) {          \
+  __global__ __launch_bounds__(dyn_waves(B, MB) * kWave) void NAME(const Params p) {         \
     extern __shared__ __align__(16) unsigned char smem[];                                    \
-    __shared__ int s_wave_cnt[DynWaves<MB>::v];                                              \
+    __shared__ int s_wave_cnt[DynWaves<B, MB>::v];                                           \
     __shared__ int s_xrow[QGEMV_MAX_WINDOW];                                                 \
     __shared__ int64_t s_yoff[QGEMV_MAX_WINDOW];                                             \
     __shared__ int s_next;                                                                   \
