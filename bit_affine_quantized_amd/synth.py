@@ -16,6 +16,9 @@ codes, scales, biases and inputs, packed as MLX affine):
   drawn in fp64 and rounded to bf16 (fp64 -> fp32 -> bf16, round to nearest
   even at each step).
 * activations x ~ N(0, 1), drawn in fp64 and rounded the same way.
+* wide-range activations (one parity case): sign * (1 + j/128) * 2^e with j
+  uniform over 0..127, e uniform over -24..24 and a fair sign, rounded the
+  same way, so that a 32-code unit's fp32 dot rounds.
 * expert routing: for every activation row, 8 distinct expert slots drawn
   without replacement, kept in the order drawn.
 
@@ -115,6 +118,16 @@ def draw_biases(rng, shape) -> np.ndarray:
 
 def draw_x(rng, m: int, k: int) -> np.ndarray:
     return to_bf16_bits(rng.standard_normal(size=(m, k)))
+
+
+def draw_x_wide(rng, m: int, k: int, span: int = 48) -> np.ndarray:
+    """Activations whose magnitudes spread over 2^(+-span/2) with random
+    signs, so that a 32-code unit's fp32 dot rounds (normal draws keep most
+    unit dots exact)."""
+    mant = 1.0 + rng.integers(0, 128, size=(m, k)) / 128.0
+    expo = rng.integers(-(span // 2), span // 2 + 1, size=(m, k))
+    sign = np.where(rng.integers(0, 2, size=(m, k)) == 1, -1.0, 1.0)
+    return to_bf16_bits(sign * np.ldexp(mant, expo))
 
 
 def draw_routes(rng, m: int, slots: int, n_experts: int) -> np.ndarray:
