@@ -1796,7 +1796,8 @@ __global__ __launch_bounds__(kThreads) void qrow_stack(const StackParams sp) {
 #undef QG_BODY
 }
 
-// Matrix-core runs: kind = bits index * 3 + group index.
+// Matrix-core runs: kind = bits index * 3 + group index.  16-row windows
+// take the wide bodies (the same bits as the block-diagonal ones).
 template <int MB>
 __global__ __launch_bounds__(MWaves<MB>::v * kWave) void qrow_stack_mfma(const StackParams sp) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -1808,7 +1809,7 @@ __global__ __launch_bounds__(MWaves<MB>::v * kWave) void qrow_stack_mfma(const S
 #define QG_BODY(B, G)                    \
   do {                                   \
     asm volatile("" ::: "memory");       \
-    mfma_body<B, G, MB>(p, bx, gx, smem, s_wave_cnt, s_xrow, s_yoff); \
+    mfma_body<B, G, MB, (MB >= 16)>(p, bx, gx, smem, s_wave_cnt, s_xrow, s_yoff); \
   } while (0)
 #define QG_PAIR(BI, B, GI, G) \
   case (BI) * 3 + (GI):       \
