@@ -1044,32 +1044,34 @@ template <int MB> struct MWaves {
   static constexpr int v = MB >= 8 ? 8 : 4;
 };
 
-// 4 x 4 transpose of 4-dword items across the four 16-lane rows of a wave.
-// On entry the lanes of row q hold items X_q[0..3] in q[4t..4t+3]; on exit
-// they hold X_0[q], X_1[q], X_2[q], X_3[q].  First the rows two apart swap
+// 4 x 4 transpose of W-dword items across the four 16-lane rows of a wave.
+// On entry the lanes of row q hold items X_q[0..3] in q[W*t .. W*t+W-1]; on
+// exit they hold X_0[q], X_1[q], X_2[q], X_3[q].  First the rows two apart swap
 // (permlane32: the upper 32 lanes of the first operand with the lower 32 of
 // the second), then adjacent rows (permlane16: the odd rows of the first
 // operand with the even rows of the second).
-__device__ __forceinline__ void transpose_rows(uint32_t* q) {
+template <int W>
+__device__ __forceinline__ void transpose_items(uint32_t* q) {
 #pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const auto a = __builtin_amdgcn_permlane32_swap(q[d], q[8 + d], false, false);
+  for (int d = 0; d < W; ++d) {
+    const auto a = __builtin_amdgcn_permlane32_swap(q[d], q[2 * W + d], false, false);
     q[d] = a[0];
-    q[8 + d] = a[1];
-    const auto b = __builtin_amdgcn_permlane32_swap(q[4 + d], q[12 + d], false, false);
-    q[4 + d] = b[0];
-    q[12 + d] = b[1];
+    q[2 * W + d] = a[1];
+    const auto b = __builtin_amdgcn_permlane32_swap(q[W + d], q[3 * W + d], false, false);
+    q[W + d] = b[0];
+    q[3 * W + d] = b[1];
   }
 #pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const auto a = __builtin_amdgcn_permlane16_swap(q[d], q[4 + d], false, false);
+  for (int d = 0; d < W; ++d) {
+    const auto a = __builtin_amdgcn_permlane16_swap(q[d], q[W + d], false, false);
     q[d] = a[0];
-    q[4 + d] = a[1];
-    const auto b = __builtin_amdgcn_permlane16_swap(q[8 + d], q[12 + d], false, false);
-    q[8 + d] = b[0];
-    q[12 + d] = b[1];
+    q[W + d] = a[1];
+    const auto b = __builtin_amdgcn_permlane16_swap(q[2 * W + d], q[3 * W + d], false, false);
+    q[2 * W + d] = b[0];
+    q[3 * W + d] = b[1];
   }
 }
+__device__ __forceinline__ void transpose_rows(uint32_t* q) { transpose_items<4>(q); }
 
 // t = mi * units + un for 0 <= t < 2^22: the quotient from one fp32 product
 // with the rounded reciprocal is off by at most one (relative error below
@@ -1404,8 +1406,15 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
         // B operand: this lane's unit as 16 exact bf16 pairs, then quarter
         // qd of each of the four units
         uint32_t qp[16];
-        unpack_codes<B, 32>(wu, qp);
-        transpose_rows(qp);
+        if constexpr (B == 4 || B == 8) {
+          // a quarter of a unit is whole words (8 codes in 1 or 2 words,
+          // each unpacked on its own): trade the packed words, then unpack
+          transpose_items<B / 4>(wu);
+          unpack_codes<B, 32>(wu, qp);
+        } else {
+          unpack_codes<B, 32>(wu, qp);
+          transpose_rows(qp);
+        }
         f32x4_t d[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
