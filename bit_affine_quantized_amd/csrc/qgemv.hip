@@ -304,7 +304,7 @@ int launch(const qgemv_handle* h, const uint16_t* x, int32_t m, float* y, int64_
     // one wave per 16 output columns
     // gate/up pairs and indexed calls run kernels of their own, with the
     // pairing and the routing compiled in
-    const bool wide = h->arith == QGEMV_ARITH_WIDE || (h->wide_windows && var == 4 && !indexed && !up);
+    const bool wide = h->arith == QGEMV_ARITH_WIDE || (h->wide_windows && qg::kWindows[var] > 8 && !indexed && !up);
     if (indexed) {
       if (var > 2) return QGEMV_E_WINDOW;   // routed windows have at most kIndexedWindow rows
       fn = wide ? (up ? h->wide->gateup_indexed[var] : h->wide->indexed[var])
@@ -366,7 +366,7 @@ int launch(const qgemv_handle* h, const uint16_t* x, int32_t m, float* y, int64_
   const int64_t units16 = (h->d.n + 15) / 16;
   const int dyn_waves = qg::dyn_waves(h->d.bits, qg::kWindows[var]);
   size_t dyn_lds = 0;
-  const bool dyn_wide = h->arith == QGEMV_ARITH_WIDE || (h->wide_windows && var == 4 && !up);
+  const bool dyn_wide = h->arith == QGEMV_ARITH_WIDE || (h->wide_windows && qg::kWindows[var] > 8 && !up);
   const qg::KernelFn dyn_fn = !mfma ? nullptr : (dyn_wide ? h->wide->dyn[var] : h->entry->mfma_dyn[var]);
   if (dyn_fn && !indexed && !up && h->ksplit == 1 && units16 >= 2LL * dyn_waves * dev->cus &&
       mfma_plan(h, var, false, &dyn_lds, dyn_waves)) {
