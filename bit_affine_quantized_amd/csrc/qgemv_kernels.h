@@ -105,9 +105,9 @@ __device__ __forceinline__ uint32_t bytes_to_bf16x2(uint32_t bytes) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(bytes, 512.0f, HI));
 }
 
-template <int B, int P>
+template <int B, int P, int NPAIR = 16>
 __device__ __forceinline__ void unpack_pairs_odd(const uint32_t* w, uint32_t* q) {
-  if constexpr (P < 16) {
+  if constexpr (P < NPAIR) {
     if constexpr (B == 3) {
       // two 3-bit codes -> bytes {c0, c1} -> one conversion
       q[P] = bytes_to_bf16x2<false>(unit_code<B, 2 * P>(w) | (unit_code<B, 2 * P + 1>(w) << 8));
@@ -115,7 +115,7 @@ __device__ __forceinline__ void unpack_pairs_odd(const uint32_t* w, uint32_t* q)
       q[P] = pack_bf16x2(static_cast<float>(unit_code<B, 2 * P>(w)),
                          static_cast<float>(unit_code<B, 2 * P + 1>(w)));
     }
-    unpack_pairs_odd<B, P + 1>(w, q);
+    unpack_pairs_odd<B, P + 1, NPAIR>(w, q);
   }
 }
 
@@ -173,6 +173,8 @@ __device__ __forceinline__ void unpack_codes(const uint32_t* w, uint32_t* q) {
   } else {
 #pragma unroll
     for (int u = 0; u < NC / 32; ++u) unpack_pairs_odd<B, 0>(w + u * B, q + 16 * u);
+    // a half unit (16 codes in whole words: 6 bits)
+    if constexpr (NC % 32 == 16) unpack_pairs_odd<B, 0, 8>(w + (NC / 32) * B, q + 16 * (NC / 32));
   }
 }
 
@@ -1050,16 +1052,18 @@ template <int MB> struct MWaves {
 // (permlane32: the upper 32 lanes of the first operand with the lower 32 of
 // the second), then adjacent rows (permlane16: the odd rows of the first
 // operand with the even rows of the second).
-template <int W>
+template <int W, bool ROWS_TWO_APART = true>
 __device__ __forceinline__ void transpose_items(uint32_t* q) {
+  if constexpr (ROWS_TWO_APART) {
 #pragma unroll
-  for (int d = 0; d < W; ++d) {
-    const auto a = __builtin_amdgcn_permlane32_swap(q[d], q[2 * W + d], false, false);
-    q[d] = a[0];
-    q[2 * W + d] = a[1];
-    const auto b = __builtin_amdgcn_permlane32_swap(q[W + d], q[3 * W + d], false, false);
-    q[W + d] = b[0];
-    q[3 * W + d] = b[1];
+    for (int d = 0; d < W; ++d) {
+      const auto a = __builtin_amdgcn_permlane32_swap(q[d], q[2 * W + d], false, false);
+      q[d] = a[0];
+      q[2 * W + d] = a[1];
+      const auto b = __builtin_amdgcn_permlane32_swap(q[W + d], q[3 * W + d], false, false);
+      q[W + d] = b[0];
+      q[3 * W + d] = b[1];
+    }
   }
 #pragma unroll
   for (int d = 0; d < W; ++d) {
@@ -1411,6 +1415,19 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
           // each unpacked on its own): trade the packed words, then unpack
           transpose_items<B / 4>(wu);
           unpack_codes<B, 32>(wu, qp);
+        } else if constexpr (B == 6) {
+          // a half of a unit is 3 whole words (16 codes): the rows two apart
+          // trade packed halves, each half is unpacked on its own, then the
+          // adjacent rows trade unpacked quarters
+#pragma unroll
+          for (int d = 0; d < 3; ++d) {
+            const auto a = __builtin_amdgcn_permlane32_swap(wu[d], wu[3 + d], false, false);
+            wu[d] = a[0];
+            wu[3 + d] = a[1];
+          }
+          unpack_codes<6, 16>(wu, qp);
+          unpack_codes<6, 16>(wu + 3, qp + 8);
+          transpose_items<4, false>(qp);
         } else {
           unpack_codes<B, 32>(wu, qp);
           transpose_rows(qp);
