@@ -931,14 +931,36 @@ def _random_cases(count=40, seed=20260):
     return cases
 
 
-@pytest.mark.parametrize("bits,group,n,k,m,arith,seed", _random_cases())
-def test_random_shapes(bits, group, n, k, m, arith, seed):
+def _random_auto_cases(count=24, seed=20261):
+    """The library's choice at matrix-core shapes, windows of 1 to 65 rows;
+    every other case with activations whose unit dots round."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < count:
+        bits, group = PAIRS[int(rng.integers(len(PAIRS)))]
+        step = qgemv.qgemv_mfma_codes(bits, group)
+        k = step * int(rng.integers(1, max(2, 4096 // step) + 1))
+        n = int(rng.integers(1, 2600))
+        m = int(rng.integers(1, qgemv.QGEMV_MAX_PROMPT + 1))
+        if n * k * m > 12_000_000 or k > 4096:
+            continue
+        cases.append((bits, group, n, k, m, qgemv.QGEMV_ARITH_AUTO, int(rng.integers(1 << 30)), len(cases) % 2 == 1))
+    return cases
+
+
+@pytest.mark.parametrize("bits,group,n,k,m,arith,seed,wide_x",
+                         [c + (False,) for c in _random_cases()] + _random_auto_cases())
+def test_random_shapes(bits, group, n, k, m, arith, seed, wide_x):
     """Random (seeded) shapes: ragged N, every admissible K of the form up to
-    4096, windows up to the form's limit.  Outputs meet the bound; two rows
-    equal their 1-row calls bit for bit; a strided call equals the plain one
-    and leaves the gaps untouched."""
-    print_case("random", bits, group, n, k, m, arith, seed)
+    4096, windows up to the form's limit (the library's choice too, which
+    mixes the block-diagonal and wide kernels by window, some with
+    activations over 2^+-24).  Outputs meet the bound; two rows equal their
+    1-row calls bit for bit; a strided call equals the plain one and leaves
+    the gaps untouched."""
+    print_case("random", bits, group, n, k, m, arith, seed, "wide-range x" if wide_x else "")
     d = synth.matrix(seed, bits, group, n, k, m)
+    if wide_x:
+        d["x"] = synth.draw_x_wide(np.random.default_rng(seed + 1), m, k)
     try:
         mat = matrix_of(d, arith=arith)
     except qgemv.QgemvError as e:
