@@ -304,7 +304,7 @@ int launch(const qgemv_handle* h, const uint16_t* x, int32_t m, float* y, int64_
     // one wave per 16 output columns
     // gate/up pairs and indexed calls run kernels of their own, with the
     // pairing and the routing compiled in
-    const bool wide = h->arith == QGEMV_ARITH_WIDE || (h->wide_windows && qg::kWindows[var] > 8 && !indexed && !up);
+    const bool wide = h->arith == QGEMV_ARITH_WIDE || (h->wide_windows && qg::kWindows[var] > 8 && !indexed);
     if (indexed) {
       if (var > 2) return QGEMV_E_WINDOW;   // routed windows have at most kIndexedWindow rows
       fn = wide ? (up ? h->wide->gateup_indexed[var] : h->wide->indexed[var])

@@ -143,8 +143,8 @@ int qgemv_create(const qgemv_desc* d, qgemv_t* out);
  *   QGEMV_ARITH_AUTO  the library's choice (what qgemv_create uses): the
  *                     matrix-core arithmetic when the shape and alignment
  *                     allow it, run by the MFMA form's kernels for windows
- *                     of up to 8 rows and by the WIDE form's above (plain
- *                     and strided calls; the same bits either way);
+ *                     of up to 8 rows and by the WIDE form's above (plain,
+ *                     strided and gate/up calls; the same bits either way);
  *                     qgemv_arith reports QGEMV_ARITH_MFMA.  Else the dot
  *                     form.                                               */
 #define QGEMV_ARITH_AUTO 0
