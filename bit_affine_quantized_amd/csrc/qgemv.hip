@@ -283,6 +283,7 @@ int launch(const qgemv_handle* h, const uint16_t* x, int32_t m, float* y, int64_
   int stage = (h->fast && h->ppc > 1) ? 1 : 0;
   if (stage && lds_bytes(h, var, 1) > qg::kMaxDynamicLds) stage = 0;
   const bool mfma = matrix_cores(h);
+  const int own_var = var;   // the window's own variant, before any narrowing
   size_t lds = 0;
   if (mfma) {
     stage = 0;
@@ -362,17 +363,26 @@ int launch(const qgemv_handle* h, const uint16_t* x, int32_t m, float* y, int64_
   dim3 grid(1u, 1u);
   // A plain or strided call on a matrix of many 16-column units with no K
   // split: one block per CU, each CU's share of units handed out among its
-  // waves (so that the CU's waves end together), when its kernel and LDS fit.
+  // waves (so that the CU's waves end together), when its kernel and LDS fit:
+  // at the window's own variant (its block has fewer waves than the tile
+  // walk's blocks together), else at the tile walk's narrower one (passes).
+  // Its stages of one or two load groups need a row of whole stages.
   const int64_t units16 = (h->d.n + 15) / 16;
-  const int dyn_waves = qg::dyn_waves(h->d.bits, qg::kWindows[var]);
-  size_t dyn_lds = 0;
-  const bool dyn_wide = h->arith == QGEMV_ARITH_WIDE || (h->wide_windows && qg::kWindows[var] > 8 && !up);
-  const qg::KernelFn dyn_fn = !mfma ? nullptr : (dyn_wide ? h->wide->dyn[var] : h->entry->mfma_dyn[var]);
-  if (dyn_fn && !indexed && !up && h->ksplit == 1 && units16 >= 2LL * dyn_waves * dev->cus &&
-      mfma_plan(h, var, false, &dyn_lds, dyn_waves)) {
-    p.tiles = static_cast<int32_t>(units16);
-    grid.x = static_cast<unsigned>(dev->cus);
-    return enqueue(reinterpret_cast<const void*>(dyn_fn), grid, dim3(dyn_waves * qg::kWave), dyn_lds, stream, p);
+  if (mfma && !indexed && !up && h->ksplit == 1 &&
+      h->d.k % (128 * static_cast<int64_t>(h->entry->mfma_group) * h->entry->dyn_stage) == 0) {
+    for (int dv = own_var;; dv = var) {
+      size_t dyn_lds = 0;
+      const bool dyn_wide = h->arith == QGEMV_ARITH_WIDE || (h->wide_windows && qg::kWindows[dv] > 8);
+      const int dyn_waves = qg::dyn_waves(h->d.bits, h->d.group, qg::kWindows[dv], dyn_wide);
+      const qg::KernelFn dyn_fn = dyn_wide ? h->wide->dyn[dv] : h->entry->mfma_dyn[dv];
+      if (dyn_fn && units16 >= 2LL * dyn_waves * dev->cus && mfma_plan(h, dv, false, &dyn_lds, dyn_waves)) {
+        p.tiles = static_cast<int32_t>(units16);
+        grid.x = static_cast<unsigned>(dev->cus);
+        return enqueue(reinterpret_cast<const void*>(dyn_fn), grid, dim3(dyn_waves * qg::kWave), dyn_lds, stream,
+                       p);
+      }
+      if (dv == var) break;
+    }
   }
   if (!indexed) {
     const int oslot = mfma ? (up ? 1 : 0) : stage;

@@ -1013,8 +1013,25 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// 128-code rounds per load group: the fewest whose codes end on a byte.
+__host__ __device__ constexpr int group_rounds(int b) {
+  return b == 8 ? 1 : (b == 4 ? 2 : ((b == 2 || b == 6) ? 4 : 8));
+}
+// Load groups per pipeline stage of the kernels that hand out units in the
+// block: 2 for 2-, 4- and 8-bit codes, whose groups are one 128-byte line a
+// column (2 KiB a wave).  A stage's groups are loaded together and computed
+// one after the other in order, so a wave keeps twice the bytes in flight
+// while it computes and the arithmetic is the tile walk's.
+__host__ __device__ constexpr int dyn_stage_groups(int b) { return (b == 2 || b == 4 || b == 8) ? 2 : 1; }
+// LDS bytes of one wave's load-group slot: 16 columns' weights (R*B/8 lines
+// of 128 bytes each) and their scales and biases (rows of 32 bytes padded to 48).
+__host__ __device__ constexpr int group_slot(int b, int g) {
+  const int r = group_rounds(b), sb = 256 * r / g, sbp = sb < 4 ? 4 : sb;
+  return 16 * (r * b / 8) * 128 + 2 * 16 * (sbp % 32 == 0 ? sbp + 16 : sbp);
+}
+
 template <int B, int G> struct MGroup {
-  static constexpr int R = B == 8 ? 1 : (B == 4 ? 2 : ((B == 2 || B == 6) ? 4 : 8));  // rounds per group
+  static constexpr int R = group_rounds(B);        // rounds per group
   static constexpr int L = R * B / 8;              // 128-byte lines per column per group
   static constexpr int WLD = 2 * L;                // 16-byte weight loads per lane per group
   static constexpr int SB = 256 * R / G;           // scale bytes per column per group
@@ -1025,20 +1042,31 @@ template <int B, int G> struct MGroup {
   static constexpr int SSTR = SBP % 32 == 0 ? SBP + 16 : SBP;   // LDS bytes per column of scales
   static constexpr int WBYTES = 16 * L * 128;
   static constexpr int SLOT = WBYTES + 2 * 16 * SSTR;
-  static_assert(R * B % 8 == 0 && SLANES <= 64, "group geometry");
+  static_assert(R * B % 8 == 0 && SLANES <= 64 && SLOT == group_slot(B, G), "group geometry");
 };
 
-// Waves per block of the kernels that hand out units in the block: the
-// whole CU's share of a large matrix in one block, 3 waves a SIMD for
-// windows of up to 8 rows.  At 16 rows the staged window takes 64 KiB of LDS
-// at K = 2048, which leaves room for 11 group slots of 2-, 4-, 6- and 8-bit
-// codes (3 waves on three SIMDs, 2 on the fourth) but only 8 of the larger
-// 3- and 5-bit slots.
-__host__ __device__ constexpr int dyn_waves(int b, int mb) {
-  return mb < 16 ? 12 : ((b == 3 || b == 5) ? 8 : 11);
+// Waves per block of the kernels that hand out units in the block (the
+// whole CU's share of a large matrix in one block): as many as both the
+// register share and the LDS allow.
+// * Registers: 3 waves a SIMD (168 VGPRs) for windows of up to 8 rows, but 2
+//   (8 waves) for the 5-bit bodies that need more; at 16 rows 11 (3 waves on
+//   three SIMDs, 2 on the fourth), or 8 for 3- and 5-bit codes.
+// * LDS at K = 2048: the staged window, the zero area and the unit sums, as
+//   the host plans them, plus one group slot a wave.  At 16 rows the window
+//   takes 64 KiB, which leaves room for 8 slots of 3-bit or 5-bit/128 codes
+//   and only 7 of 5-bit codes in groups of 32 or 64.
+// At larger K the host finds the plan too large and takes the tile walk.
+__host__ __device__ constexpr int dyn_waves(int b, int g, int mb, bool wide) {
+  const bool big = b == 5 && (wide ? (g <= 64 && mb >= 2 && mb <= 8) : (g == 32 || mb == 8));
+  const int regs = mb < 16 ? (big ? 8 : 12) : ((b == 3 || b == 5) ? 8 : 11);
+  const int units = 2048 / 32;
+  const int fixed = mb * (units * 64 + 16) + 256 * group_rounds(b) + mb * (units + 4) * 4;
+  const int lds = (static_cast<int>(kMaxMfmaLds) - fixed) / group_slot(b, g);
+  return regs < lds ? regs : lds;
 }
-template <int B, int MB> struct DynWaves {
-  static constexpr int v = dyn_waves(B, MB);
+template <int B, int G, int MB, bool WIDE> struct DynWaves {
+  static constexpr int v = dyn_waves(B, G, MB, WIDE);
+  static_assert(v >= 4, "a unit-handout block holds at least one wave a SIMD");
 };
 
 // Waves per block: a wide window's activations are staged once for 8 waves.
@@ -1101,7 +1129,8 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
   static_assert(!DYN || (!GU && !IDX), "units handed out in a block: plain and strided calls");
   using MG = MGroup<B, G>;
   constexpr int R = MG::R, SSZ = MG::SSZ;
-  constexpr int NW = DYN ? DynWaves<B, MB>::v : MWaves<MB>::v, NT = NW * kWave;
+  constexpr int NG = DYN ? dyn_stage_groups(B) : 1;   // load groups per stage
+  constexpr int NW = DYN ? DynWaves<B, G, MB, WIDE>::v : MWaves<MB>::v, NT = NW * kWave;
   constexpr int NMB = (MB + 3) / 4;         // 4-row blocks of the window
   // outputs each lane folds: one per 4-row block, or (wide form) window rows
   // 4q .. 4q+3 of its column, as many as the window can hold
@@ -1223,7 +1252,8 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
     return __builtin_amdgcn_readfirstlane(u);
   };
   auto advance = [&](Cursor& c) {
-    if (++c.gr == gr0 + gpp) {
+    c.gr += NG;
+    if (c.gr == gr0 + gpp) {
       c.gr = gr0;
       if constexpr (DYN) {
         c.tile = next_unit(c);
@@ -1233,10 +1263,10 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
     }
   };
   struct Stage {
-    u32x4 w[MG::WLD];
-    uint32_t s[SSZ / 4];
-    uint32_t b[SSZ / 4];
-    Cursor cur;   // the step these loads belong to
+    u32x4 w[NG][MG::WLD];
+    uint32_t s[NG][SSZ / 4];
+    uint32_t b[NG][SSZ / 4];
+    Cursor cur;   // the step these loads belong to (its first group)
   };
   // a step's loads into registers (past the last step: loads that read nothing)
   auto load_stage = [&](Stage& sg, const Cursor& c) {
@@ -1253,42 +1283,47 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
     // the up matrix's rows of the same tile (gate/up pairs only)
     const __amdgpu_buffer_rsrc_t wr2 = make_rsrc(wexp2 + static_cast<int64_t>(c0) * row_bytes,
                                                  static_cast<int64_t>(gu ? ncols : 0) * row_bytes);
-    const int wsoff = c.gr * (MG::L * 128);
+    // the stage's groups: weights, then scales, of each in order
 #pragma unroll
-    for (int t = 0; t < MG::WLD; ++t)
-      sg.w[t] = __builtin_amdgcn_raw_buffer_load_b128((t & 1) && gu ? wr2 : wr, w_voff[t], wsoff, kNt);
-    // this group's scales: SB bytes per column from byte gr*SB of the row
-    // (at SB = 2, the aligned dword that holds them); default cache policy,
-    // since a row's scale line serves several groups.  A gate/up tile loads
-    // its gate columns and its up columns separately (a lane outside a
-    // load's range reads zeros), and merges them.
-    const int ssoff = MG::SB < 4 ? ((c.gr * MG::SB) & ~3) : c.gr * MG::SB;
-    const int sv = s_live && !(gu && s_col >= 8) ? s_voff : kNoOffset;
-    if constexpr (SSZ == 16) {
-      u32x4 a4 = __builtin_amdgcn_raw_buffer_load_b128(sr, sv, ssoff, 0);
-      u32x4 b4 = __builtin_amdgcn_raw_buffer_load_b128(br, sv, ssoff, 0);
-      if (gu) {
-        const __amdgpu_buffer_rsrc_t sr2 = make_rsrc(sexp2 + static_cast<int64_t>(c0) * gpr2,
-                                                     static_cast<int64_t>(ncols) * gpr2);
-        const __amdgpu_buffer_rsrc_t br2 = make_rsrc(bexp2 + static_cast<int64_t>(c0) * gpr2,
-                                                     static_cast<int64_t>(ncols) * gpr2);
-        const int sv2 = s_live && s_col >= 8 ? s_voff : kNoOffset;
-        a4 |= __builtin_amdgcn_raw_buffer_load_b128(sr2, sv2, ssoff, 0);
-        b4 |= __builtin_amdgcn_raw_buffer_load_b128(br2, sv2, ssoff, 0);
-      }
-      sg.s[0] = a4.x; sg.s[1] = a4.y; sg.s[2] = a4.z; sg.s[3] = a4.w;
-      sg.b[0] = b4.x; sg.b[1] = b4.y; sg.b[2] = b4.z; sg.b[3] = b4.w;
-    } else {
-      sg.s[0] = __builtin_amdgcn_raw_buffer_load_b32(sr, sv, ssoff, 0);
-      sg.b[0] = __builtin_amdgcn_raw_buffer_load_b32(br, sv, ssoff, 0);
-      if (gu) {
-        const __amdgpu_buffer_rsrc_t sr2 = make_rsrc(sexp2 + static_cast<int64_t>(c0) * gpr2,
-                                                     static_cast<int64_t>(ncols) * gpr2);
-        const __amdgpu_buffer_rsrc_t br2 = make_rsrc(bexp2 + static_cast<int64_t>(c0) * gpr2,
-                                                     static_cast<int64_t>(ncols) * gpr2);
-        const int sv2 = s_live && s_col >= 8 ? s_voff : kNoOffset;
-        sg.s[0] |= __builtin_amdgcn_raw_buffer_load_b32(sr2, sv2, ssoff, 0);
-        sg.b[0] |= __builtin_amdgcn_raw_buffer_load_b32(br2, sv2, ssoff, 0);
+    for (int g2 = 0; g2 < NG; ++g2) {
+      const int gr = c.gr + g2;
+      const int wsoff = gr * (MG::L * 128);
+#pragma unroll
+      for (int t = 0; t < MG::WLD; ++t)
+        sg.w[g2][t] = __builtin_amdgcn_raw_buffer_load_b128((t & 1) && gu ? wr2 : wr, w_voff[t], wsoff, kNt);
+      // this group's scales: SB bytes per column from byte gr*SB of the row
+      // (at SB = 2, the aligned dword that holds them); default cache policy,
+      // since a row's scale line serves several groups.  A gate/up tile loads
+      // its gate columns and its up columns separately (a lane outside a
+      // load's range reads zeros), and merges them.
+      const int ssoff = MG::SB < 4 ? ((gr * MG::SB) & ~3) : gr * MG::SB;
+      const int sv = s_live && !(gu && s_col >= 8) ? s_voff : kNoOffset;
+      if constexpr (SSZ == 16) {
+        u32x4 a4 = __builtin_amdgcn_raw_buffer_load_b128(sr, sv, ssoff, 0);
+        u32x4 b4 = __builtin_amdgcn_raw_buffer_load_b128(br, sv, ssoff, 0);
+        if (gu) {
+          const __amdgpu_buffer_rsrc_t sr2 = make_rsrc(sexp2 + static_cast<int64_t>(c0) * gpr2,
+                                                       static_cast<int64_t>(ncols) * gpr2);
+          const __amdgpu_buffer_rsrc_t br2 = make_rsrc(bexp2 + static_cast<int64_t>(c0) * gpr2,
+                                                       static_cast<int64_t>(ncols) * gpr2);
+          const int sv2 = s_live && s_col >= 8 ? s_voff : kNoOffset;
+          a4 |= __builtin_amdgcn_raw_buffer_load_b128(sr2, sv2, ssoff, 0);
+          b4 |= __builtin_amdgcn_raw_buffer_load_b128(br2, sv2, ssoff, 0);
+        }
+        sg.s[g2][0] = a4.x; sg.s[g2][1] = a4.y; sg.s[g2][2] = a4.z; sg.s[g2][3] = a4.w;
+        sg.b[g2][0] = b4.x; sg.b[g2][1] = b4.y; sg.b[g2][2] = b4.z; sg.b[g2][3] = b4.w;
+      } else {
+        sg.s[g2][0] = __builtin_amdgcn_raw_buffer_load_b32(sr, sv, ssoff, 0);
+        sg.b[g2][0] = __builtin_amdgcn_raw_buffer_load_b32(br, sv, ssoff, 0);
+        if (gu) {
+          const __amdgpu_buffer_rsrc_t sr2 = make_rsrc(sexp2 + static_cast<int64_t>(c0) * gpr2,
+                                                       static_cast<int64_t>(ncols) * gpr2);
+          const __amdgpu_buffer_rsrc_t br2 = make_rsrc(bexp2 + static_cast<int64_t>(c0) * gpr2,
+                                                       static_cast<int64_t>(ncols) * gpr2);
+          const int sv2 = s_live && s_col >= 8 ? s_voff : kNoOffset;
+          sg.s[g2][0] |= __builtin_amdgcn_raw_buffer_load_b32(sr2, sv2, ssoff, 0);
+          sg.b[g2][0] |= __builtin_amdgcn_raw_buffer_load_b32(br2, sv2, ssoff, 0);
+        }
       }
     }
   };
@@ -1333,27 +1368,28 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
     }
   };
 
-  auto compute = [&](const Stage& sg, const Cursor& c) {
+  auto compute_group = [&](const u32x4 (&gw)[MG::WLD], const uint32_t (&gs)[SSZ / 4], const uint32_t (&gb)[SSZ / 4],
+                           const Cursor& c, const int gr) {
     // hand the group over: lane order in, the slot layout out (the wave's
     // previous reads of the slot precede these writes in its LDS queue)
 #pragma unroll
-    for (int t = 0; t < MG::WLD; ++t) reinterpret_cast<u32x4*>(slot)[t * kWave + lane] = sg.w[t];
+    for (int t = 0; t < MG::WLD; ++t) reinterpret_cast<u32x4*>(slot)[t * kWave + lane] = gw[t];
     if (s_live) {
       if constexpr (SSZ == 16) {
         u32x4 a4, b4;
-        a4.x = sg.s[0]; a4.y = sg.s[1]; a4.z = sg.s[2]; a4.w = sg.s[3];
-        b4.x = sg.b[0]; b4.y = sg.b[1]; b4.z = sg.b[2]; b4.w = sg.b[3];
+        a4.x = gs[0]; a4.y = gs[1]; a4.z = gs[2]; a4.w = gs[3];
+        b4.x = gb[0]; b4.y = gb[1]; b4.z = gb[2]; b4.w = gb[3];
         *reinterpret_cast<u32x4*>(slot + MG::WBYTES + s_woff) = a4;
         *reinterpret_cast<u32x4*>(slot + MG::WBYTES + 16 * MG::SSTR + s_woff) = b4;
       } else {
-        *reinterpret_cast<uint32_t*>(slot + MG::WBYTES + s_woff) = sg.s[0];
-        *reinterpret_cast<uint32_t*>(slot + MG::WBYTES + 16 * MG::SSTR + s_woff) = sg.b[0];
+        *reinterpret_cast<uint32_t*>(slot + MG::WBYTES + s_woff) = gs[0];
+        *reinterpret_cast<uint32_t*>(slot + MG::WBYTES + 16 * MG::SSTR + s_woff) = gb[0];
       }
     }
     int a_grp[NMB];
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) a_grp[mb] = a_base[mb] + a_live[mb] * (c.gr * R * 256);
-    const int xa_grp = xa_base + c.gr * R * 16;
+    for (int mb = 0; mb < NMB; ++mb) a_grp[mb] = a_base[mb] + a_live[mb] * (gr * R * 256);
+    const int xa_grp = xa_base + gr * R * 16;
     // the group's scale bytes of column j (the kept bytes), read once
     constexpr int NSW = MG::SBP / 4;
     uint32_t sw[NSW];
@@ -1390,12 +1426,12 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
       float sv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int si = MG::SB < 4 ? ((c.gr * R + r) & 1) : (i * R + r) / UPG;
+        const int si = MG::SB < 4 ? ((gr * R + r) & 1) : (i * R + r) / UPG;
         const uint32_t w = sw[MG::SB < 4 ? 0 : si / 2];
         sv[i] = (si & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
       }
       // the bias of this lane's unit qd*R + r
-      const int bofs = MG::SB < 4 ? ((c.gr * R + r) & 1) * 2 : (UPG <= R ? (r / UPG) * 2 : 0);
+      const int bofs = MG::SB < 4 ? ((gr * R + r) & 1) * 2 : (UPG <= R ? (r / UPG) * 2 : 0);
       {
         const float xa = *reinterpret_cast<const float*>(smem + xa_grp + r * 4);
         const uint32_t braw = *reinterpret_cast<const uint16_t*>(slot + b_off + b_lane + bofs);
@@ -1493,7 +1529,7 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
 #pragma unroll
         for (int q2 = 0; q2 < 4; ++q2) acc[mb] = __builtin_fmaf(sv[q2], d[mb][q2], acc[mb]);
     }
-    if (c.gr == gr0 + gpp - 1) {
+    if (gr == gr0 + gpp - 1) {
       const int col = (DYN ? c.tile * 16 : (c.tile * ncg + cg) * cw) + j;
       float out[NACC];
       bool store = true;
@@ -1540,6 +1576,11 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
       }
       acc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
+  };
+  // a stage's groups one after the other, in order
+  auto compute = [&](const Stage& sg, const Cursor& c) {
+#pragma unroll
+    for (int g2 = 0; g2 < NG; ++g2) compute_group(sg.w[g2], sg.s[g2], sg.b[g2], c, c.gr + g2);
   };
 
   // A pass's first loads: each thread's first staging item, then the first
@@ -1709,20 +1750,13 @@ QG_MFMA_KERNEL(qrow_mfma_gateup_indexed, false, true, true)
 QG_MFMA_KERNEL(qrow_mfma_wide_gateup_indexed, true, true, true)
 #undef QG_MFMA_KERNEL
 
-// Which (bits, group, window) bodies fit the block's register share with no
-// spill (from the compiler's resource report at the block sizes dyn_waves gives).
-template <int B, int G, int MB, bool WIDE = false> struct DynFits {
-  static constexpr bool v = WIDE ? !(B == 5 && G <= 64 && MB >= 2 && MB <= 8)
-                                 : !(B == 5 && (G == 32 || MB == 8));
-};
-
 // The block-diagonal kernels for matrices of many columns: one block of
 // DynWaves waves per CU, its 16-column units handed out in the block.
 #define QG_DYN_KERNEL(NAME, WIDE)                                                             \
   template <int B, int G, int MB>                                                            \
-  __global__ __launch_bounds__(dyn_waves(B, MB) * kWave) void NAME(const Params p) {         \
+  __global__ __launch_bounds__(dyn_waves(B, G, MB, WIDE) * kWave) void NAME(const Params p) { \
     extern __shared__ __align__(16) unsigned char smem[];                                    \
-    __shared__ int s_wave_cnt[DynWaves<B, MB>::v];                                           \
+    __shared__ int s_wave_cnt[DynWaves<B, G, MB, WIDE>::v];                                  \
     __shared__ int s_xrow[QGEMV_MAX_WINDOW];                                                 \
     __shared__ int64_t s_yoff[QGEMV_MAX_WINDOW];                                             \
     __shared__ int s_next;                                                                   \
@@ -1905,6 +1939,7 @@ struct Entry {
   int mfma_waves[5];    // waves per block of the matrix-core kernels by window variant
   int mfma_group;       // 128-code rounds per load group (k is a multiple of 128 * this)
   int mfma_salign;      // alignment the scale and bias arrays need (bytes)
+  int dyn_stage;        // load groups per stage of the kernels that hand out units (k: 128 * group * this)
 };
 
 template <int B, int G>
@@ -1937,13 +1972,11 @@ Entry make_entry() {
   e.generic_rows[2] = RowsPerLane<B, 4>::v;
   e.generic_rows[3] = RowsPerLane<B, 8>::v;
   e.generic_rows[4] = RowsPerLane<B, 16>::v;
-  // (a 12-wave block holds 3 waves a SIMD, at most 168 VGPRs, and an 8-wave
-  // one 2: the bodies that need more keep the tile walk)
-  if constexpr (DynFits<B, G, 1>::v) e.mfma_dyn[0] = qrow_mfma_dyn<B, G, 1>;
-  if constexpr (DynFits<B, G, 2>::v) e.mfma_dyn[1] = qrow_mfma_dyn<B, G, 2>;
-  if constexpr (DynFits<B, G, 4>::v) e.mfma_dyn[2] = qrow_mfma_dyn<B, G, 4>;
-  if constexpr (DynFits<B, G, 8>::v) e.mfma_dyn[3] = qrow_mfma_dyn<B, G, 8>;
-  if constexpr (DynFits<B, G, 16>::v) e.mfma_dyn[4] = qrow_mfma_dyn<B, G, 16>;
+  e.mfma_dyn[0] = qrow_mfma_dyn<B, G, 1>;
+  e.mfma_dyn[1] = qrow_mfma_dyn<B, G, 2>;
+  e.mfma_dyn[2] = qrow_mfma_dyn<B, G, 4>;
+  e.mfma_dyn[3] = qrow_mfma_dyn<B, G, 8>;
+  e.mfma_dyn[4] = qrow_mfma_dyn<B, G, 16>;
   e.mfma[0] = qrow_mfma<B, G, 1>;
   e.mfma[1] = qrow_mfma<B, G, 2>;
   e.mfma[2] = qrow_mfma<B, G, 4>;
@@ -1968,6 +2001,7 @@ Entry make_entry() {
   e.mfma_waves[3] = MWaves<8>::v;
   e.mfma_waves[4] = MWaves<16>::v;
   e.mfma_salign = MGroup<B, G>::S16 ? 16 : 4;
+  e.dyn_stage = dyn_stage_groups(B);
   return e;
 }
 
@@ -1983,11 +2017,11 @@ struct WideEntry {
 template <int B, int G>
 WideEntry make_wide_entry() {
   WideEntry e{};
-  if constexpr (DynFits<B, G, 1, true>::v) e.dyn[0] = qrow_mfma_wide_dyn<B, G, 1>;
-  if constexpr (DynFits<B, G, 2, true>::v) e.dyn[1] = qrow_mfma_wide_dyn<B, G, 2>;
-  if constexpr (DynFits<B, G, 4, true>::v) e.dyn[2] = qrow_mfma_wide_dyn<B, G, 4>;
-  if constexpr (DynFits<B, G, 8, true>::v) e.dyn[3] = qrow_mfma_wide_dyn<B, G, 8>;
-  if constexpr (DynFits<B, G, 16, true>::v) e.dyn[4] = qrow_mfma_wide_dyn<B, G, 16>;
+  e.dyn[0] = qrow_mfma_wide_dyn<B, G, 1>;
+  e.dyn[1] = qrow_mfma_wide_dyn<B, G, 2>;
+  e.dyn[2] = qrow_mfma_wide_dyn<B, G, 4>;
+  e.dyn[3] = qrow_mfma_wide_dyn<B, G, 8>;
+  e.dyn[4] = qrow_mfma_wide_dyn<B, G, 16>;
   e.k[0] = qrow_mfma_wide<B, G, 1>;
   e.k[1] = qrow_mfma_wide<B, G, 2>;
   e.k[2] = qrow_mfma_wide<B, G, 4>;

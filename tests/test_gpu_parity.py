@@ -668,6 +668,40 @@ def test_many_tiles_consecutive_calls(arith):
     assert torch.equal(yw.view(torch.int32)[gap], wide[gap])
 
 
+# (bits, group): every width, the scale layouts of the wider load groups
+# (16-byte pieces and dwords), and the 5-bit blocks of 7 and 8 waves
+HANDOUT = [(2, 32), (3, 64), (4, 64), (4, 128), (5, 32), (5, 128), (6, 32), (8, 64), (8, 128)]
+
+
+@mc_param
+@pytest.mark.parametrize("bits,group", HANDOUT)
+def test_unit_handout_equals_tile_walk(bits, group, arith):
+    """A matrix of 100,000 columns at K = 2048 runs the kernels that hand out
+    16-column units inside one block per CU (with their own load-group size);
+    its first 40,000 columns, as a matrix of their own, run the tile walk
+    with no K split.  The shared columns agree bit for bit at 1, 4 and 16
+    rows, with activations whose unit dots round; sampled columns are held
+    to the oracle's bound."""
+    print_case("unit handout vs tile walk", bits, group, arith)
+    n, k, n_small = 100000, 2048, 40000
+    rng = np.random.default_rng(9100 + 10 * bits + group)
+    words = synth.draw_words(rng, (n,), k, bits)
+    scales = synth.draw_scales(rng, (n, k // group))
+    biases = synth.draw_biases(rng, (n, k // group))
+    x = synth.draw_x_wide(rng, 16, k)
+    tw, ts, tb = dev(words), dev(scales), dev(biases)
+    big = qgemv.Matrix(bits, group, n, k, tw, ts, tb, arith=arith)
+    small = qgemv.Matrix(bits, group, n_small, k, tw[:n_small], ts[:n_small], tb[:n_small], arith=arith)
+    xt = dev(x)
+    cols = np.unique(np.concatenate([np.arange(0, n, 997), [n_small - 1, n_small, n - 1]]))
+    y64, a64, _ = oracle.gemv(words[cols], scales[cols], biases[cols], x, bits, group, len(cols), k,
+                              threads=THREADS)
+    for m in (1, 4, 16):
+        yb, ys = run(big, xt, m), run(small, xt, m)
+        assert bits_equal(yb[:, :n_small], ys), f"m={m}"
+        check_bound(yb.cpu().numpy()[:, cols], y64[:m], a64[:m], k, f"unit handout {bits}/{group} m={m}")
+
+
 @pytest.mark.parametrize("arith", ARITHS + [qgemv.QGEMV_ARITH_AUTO], ids=ARITH_IDS + ["auto"])
 @pytest.mark.parametrize("m", [1, 8, 16])
 def test_lmhead_sampled(lmhead, m, arith):
