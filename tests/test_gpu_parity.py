@@ -681,7 +681,8 @@ def test_unit_handout_equals_tile_walk(bits, group, arith):
     its first 40,000 columns, as a matrix of their own, run the tile walk
     with no K split.  The shared columns agree bit for bit at 1, 4 and 16
     rows, with activations whose unit dots round; sampled columns are held
-    to the oracle's bound."""
+    to the oracle's bound; the relu2 epilogue and a strided output of the
+    large matrix hold the plain call's bits, and the gaps keep their bytes."""
     print_case("unit handout vs tile walk", bits, group, arith)
     n, k, n_small = 100000, 2048, 40000
     rng = np.random.default_rng(9100 + 10 * bits + group)
@@ -700,6 +701,18 @@ def test_unit_handout_equals_tile_walk(bits, group, arith):
         yb, ys = run(big, xt, m), run(small, xt, m)
         assert bits_equal(yb[:, :n_small], ys), f"m={m}"
         check_bound(yb.cpu().numpy()[:, cols], y64[:m], a64[:m], k, f"unit handout {bits}/{group} m={m}")
+    # the same kernels with the relu2 epilogue and through an output row
+    # stride: relu2 of the plain call's bits, gaps untouched
+    r = run(big, xt, 4, epi=qgemv.QGEMV_EPI_RELU2)
+    assert bits_equal(r, torch.where(yb[:4] > 0, yb[:4] * yb[:4], torch.zeros_like(yb[:4])))
+    ldy, col = n + 19, 3
+    sentinel = torch.full((4, ldy), 0x7FC0BEEF, dtype=torch.int32, device=DEV)
+    yw = sentinel.clone().view(torch.float32)
+    big.run_strided(xt[:4], yw.view(-1)[col:], ldy, m=4)
+    assert bits_equal(yw[:, col:col + n], yb[:4])
+    gap = torch.ones((4, ldy), dtype=torch.bool, device=DEV)
+    gap[:, col:col + n] = False
+    assert torch.equal(yw.view(torch.int32)[gap], sentinel[gap])
 
 
 @pytest.mark.parametrize("arith", ARITHS + [qgemv.QGEMV_ARITH_AUTO], ids=ARITH_IDS + ["auto"])
