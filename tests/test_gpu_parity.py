@@ -668,24 +668,26 @@ def test_many_tiles_consecutive_calls(arith):
     assert torch.equal(yw.view(torch.int32)[gap], wide[gap])
 
 
-# (bits, group): every width, the scale layouts of the wider load groups
-# (16-byte pieces and dwords), and the 5-bit blocks of 7 and 8 waves
-HANDOUT = [(2, 32), (3, 64), (4, 64), (4, 128), (5, 32), (5, 128), (6, 32), (8, 64), (8, 128)]
+# (bits, group, K): every width and both scale layouts at K = 2048, the 5-bit
+# blocks of 7 and 8 waves, and rows of 3, 6 and 8 two-group stages
+HANDOUT = [(2, 32, 2048), (3, 64, 2048), (4, 64, 2048), (4, 128, 2048), (5, 32, 2048), (5, 128, 2048),
+           (6, 32, 2048), (8, 64, 2048), (8, 128, 2048), (4, 64, 1536), (8, 32, 1536), (2, 128, 3072),
+           (4, 64, 4096)]
 
 
 @mc_param
-@pytest.mark.parametrize("bits,group", HANDOUT)
-def test_unit_handout_equals_tile_walk(bits, group, arith):
-    """A matrix of 100,000 columns at K = 2048 runs the kernels that hand out
-    16-column units inside one block per CU (with their own load-group size);
-    its first 40,000 columns, as a matrix of their own, run the tile walk
-    with no K split.  The shared columns agree bit for bit at 1, 4 and 16
+@pytest.mark.parametrize("bits,group,k", HANDOUT)
+def test_unit_handout_equals_tile_walk(bits, group, k, arith):
+    """A matrix of 100,000 columns runs the kernels that hand out 16-column
+    units inside one block per CU (2-, 4- and 8-bit codes two load groups a
+    stage); its first 40,000 columns, as a matrix of their own, run the tile
+    walk with no K split.  The shared columns agree bit for bit at 1, 4 and 16
     rows, with activations whose unit dots round; sampled columns are held
     to the oracle's bound; the relu2 epilogue and a strided output of the
     large matrix hold the plain call's bits, and the gaps keep their bytes."""
-    print_case("unit handout vs tile walk", bits, group, arith)
-    n, k, n_small = 100000, 2048, 40000
-    rng = np.random.default_rng(9100 + 10 * bits + group)
+    print_case("unit handout vs tile walk", bits, group, k, arith)
+    n, n_small = 100000, 40000
+    rng = np.random.default_rng(9100 + 10 * bits + group + k)
     words = synth.draw_words(rng, (n,), k, bits)
     scales = synth.draw_scales(rng, (n, k // group))
     biases = synth.draw_biases(rng, (n, k // group))
