@@ -173,6 +173,21 @@ def read_traffic(workload: str):
 ARITH_NAMES = {1: "dot", 2: "mfma", 3: "wide"}
 
 
+def parse_shape(text):
+    """'BITS,GROUP,N,K' of --workload matrix -> (bits, group, n, k); raises
+    ValueError for a shape the library refuses on its face (an unknown width
+    or group, K not a multiple of the group)."""
+    try:
+        bits, group, n, k = (int(v) for v in text.split(","))
+    except (AttributeError, ValueError):
+        raise ValueError(f"--shape wants BITS,GROUP,N,K, got {text!r}") from None
+    if bits not in (2, 3, 4, 5, 6, 8) or group not in (32, 64, 128):
+        raise ValueError(f"no MLX affine width/group {bits}/{group}")
+    if n < 1 or k < group or k % group:
+        raise ValueError(f"shape N={n} K={k} does not fit {bits}-bit codes in groups of {group}")
+    return bits, group, n, k
+
+
 class Workload:
     """Device inputs of one workload plus rotating weight copies."""
 
@@ -188,10 +203,15 @@ class Workload:
                     np.dtype(np.int32): np.int32}[a.dtype]
             return torch.from_numpy(a.view(view)).to(dev)
 
-        if name in ("single", "sweep"):
-            # the single 2048 x 2048 4/64 matrix, or one width/group pair of
-            # the 4096 x 4096 sweep
-            d = synth.single(m=m) if name == "single" else synth.sweep(pair[0], pair[1], m=m)
+        if name in ("single", "sweep", "matrix"):
+            # the single 2048 x 2048 4/64 matrix, one width/group pair of the
+            # 4096 x 4096 sweep, or any one matrix (bits, group, N, K)
+            if name == "single":
+                d = synth.single(m=m)
+            elif name == "sweep":
+                d = synth.sweep(pair[0], pair[1], m=m)
+            else:
+                d = synth.matrix(7000 + pair[0] * 10 + pair[1], pair[0], pair[1], pair[2], pair[3], m)
             self.k = d["k"]
             self.runs = [(d["bits"], d["group"], d["n"])]
             self.n_out = d["n"]
@@ -518,7 +538,10 @@ def main():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=1000,
                     help="untimed steps; the GPU clock needs tens of ms of load to settle")
-    ap.add_argument("--workload", default="lmhead", choices=["lmhead", "stack", "stack3", "experts", "gateup"])
+    ap.add_argument("--workload", default="lmhead",
+                    choices=["lmhead", "stack", "stack3", "experts", "gateup", "matrix"])
+    ap.add_argument("--shape", default=None, metavar="BITS,GROUP,N,K",
+                    help="the matrix of --workload matrix, e.g. 5,64,131072,2048")
     ap.add_argument("--m", type=int, default=1, help="window rows")
     ap.add_argument("--all", action="store_true", help="also time the other workloads and windows")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -533,6 +556,17 @@ def main():
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the row product shards along output columns with no "
               "exchange, so a multi-GPU figure is one GPU's share; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    shape = None
+    if args.workload == "matrix":
+        try:
+            shape = parse_shape(args.shape)
+        except ValueError as e:
+            print(f"bench.py: {e}", file=sys.stderr)
+            sys.exit(2)
+    elif args.shape is not None:
+        print("bench.py: --shape belongs to --workload matrix", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -552,7 +586,7 @@ def main():
     qgemv.load()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     arith = {"auto": 0, "dot": 1, "mfma": 2, "wide": 3}[args.arith]
-    wl = Workload(args.workload, args.m, torch, qgemv, synth, arith)
+    wl = Workload(args.workload, args.m, torch, qgemv, synth, arith, shape)
     # The same K steps as one captured graph first (no host issue cost; 100
     # eager steps, 3 untimed replays of K steps, then timed replays: at least
     # 5 and at least 100 ms of them), then the W untimed warmup steps and the
@@ -566,7 +600,8 @@ def main():
         ms, batches = ms_graph, [ms_graph]
     gbs = wl.bytes / (ms * 1e-3) / 1e9
     rows_cols, macs = wl.counts()
-    traffic = read_traffic(f"{args.workload}_m{wl.m}")
+    traffic = read_traffic((f"matrix_b{shape[0]}g{shape[1]}n{shape[2]}k{shape[3]}" if shape else args.workload)
+                           + f"_m{wl.m}")
     out = {
         "metric": "effective HBM GB/s (% of MI355X peak) for affine-quant GEMV, 1-16 row windows",
         "value": round(gbs, 2),

@@ -28,6 +28,20 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2 and "one GPU" in r.stderr
 
 
+def test_matrix_workload_shape():
+    assert bench.parse_shape("5,64,131072,2048") == (5, 64, 131072, 2048)
+    for bad in (None, "5,64,131072", "7,64,1024,2048", "4,48,1024,2048", "4,64,0,2048", "4,64,1024,96"):
+        with pytest.raises(ValueError):
+            bench.parse_shape(bad)
+    # refused before any GPU work, with the reason on stderr
+    r = _run_bench("--workload", "matrix", "--shape", "4,48,1024,2048")
+    assert r.returncode == 2 and "4/48" in r.stderr
+    r = _run_bench("--workload", "matrix")
+    assert r.returncode == 2 and "--shape" in r.stderr
+    r = _run_bench("--shape", "4,64,1024,2048")
+    assert r.returncode == 2 and "--workload matrix" in r.stderr
+
+
 def test_algorithmic_bytes_match_the_stated_sizes():
     # the 1-row LM head: 381,419,520 B of codes, 63,569,920 B of bf16 scales
     # and biases, 4,096 B of activations, 993,280 B of fp32 outputs
