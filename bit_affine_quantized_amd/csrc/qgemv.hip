@@ -366,10 +366,13 @@ int launch(const qgemv_handle* h, const uint16_t* x, int32_t m, float* y, int64_
   // waves (so that the CU's waves end together), when its kernel and LDS fit:
   // at the window's own variant (its block has fewer waves than the tile
   // walk's blocks together), else at the tile walk's narrower one (passes).
-  // Its stages of one or two load groups need a row of whole stages.
+  // Its stages of one or two load groups need a row of whole stages, and its
+  // loads of two groups' scales at once an 8- or 16-byte aligned scale array.
   const int64_t units16 = (h->d.n + 15) / 16;
+  const uintptr_t sb_addr = reinterpret_cast<uintptr_t>(h->d.scales) | reinterpret_cast<uintptr_t>(h->d.biases);
   if (mfma && !indexed && !up && h->ksplit == 1 &&
-      h->d.k % (128 * static_cast<int64_t>(h->entry->mfma_group) * h->entry->dyn_stage) == 0) {
+      h->d.k % (128 * static_cast<int64_t>(h->entry->mfma_group) * h->entry->dyn_stage) == 0 &&
+      sb_addr % static_cast<uintptr_t>(h->entry->dyn_salign) == 0) {
     for (int dv = own_var;; dv = var) {
       size_t dyn_lds = 0;
       const bool dyn_wide = h->arith == QGEMV_ARITH_WIDE || (h->wide_windows && qg::kWindows[dv] > 8);

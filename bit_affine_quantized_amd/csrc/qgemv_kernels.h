@@ -1130,6 +1130,12 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
   using MG = MGroup<B, G>;
   constexpr int R = MG::R, SSZ = MG::SSZ;
   constexpr int NG = DYN ? dyn_stage_groups(B) : 1;   // load groups per stage
+  // a two-group stage whose groups' scales are dwords (4 or 8 bytes a column)
+  // loads both groups' scales (and biases) of a column at once: 8 or 16
+  // bytes from an even group, by lanes 0-15 (lane = column)
+  constexpr bool CS = NG == 2 && MG::SSZ == 4 && MG::SB >= 4;
+  constexpr int CW = CS ? MG::SB / 2 : 1;             // dwords of a column's two groups
+  static_assert(!CS || !GU, "combined scale loads: plain and strided calls");
   constexpr int NW = DYN ? DynWaves<B, G, MB, WIDE>::v : MWaves<MB>::v, NT = NW * kWave;
   constexpr int NMB = (MB + 3) / 4;         // 4-row blocks of the window
   // outputs each lane folds: one per 4-row block, or (wide form) window rows
@@ -1266,6 +1272,7 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
     u32x4 w[NG][MG::WLD];
     uint32_t s[NG][SSZ / 4];
     uint32_t b[NG][SSZ / 4];
+    uint32_t cs[CW], cb[CW];   // both groups' scales and biases of column lane (CS)
     Cursor cur;   // the step these loads belong to (its first group)
   };
   // a step's loads into registers (past the last step: loads that read nothing)
@@ -1298,7 +1305,22 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
       // load's range reads zeros), and merges them.
       const int ssoff = MG::SB < 4 ? ((gr * MG::SB) & ~3) : gr * MG::SB;
       const int sv = s_live && !(gu && s_col >= 8) ? s_voff : kNoOffset;
-      if constexpr (SSZ == 16) {
+      if constexpr (CS) {
+        if (g2 == 0) {
+          const int cv = lane < 16 ? lane * gpr2 : kNoOffset;
+          if constexpr (CW == 4) {
+            const u32x4 a4 = __builtin_amdgcn_raw_buffer_load_b128(sr, cv, ssoff, 0);
+            const u32x4 b4 = __builtin_amdgcn_raw_buffer_load_b128(br, cv, ssoff, 0);
+            sg.cs[0] = a4.x; sg.cs[1] = a4.y; sg.cs[2] = a4.z; sg.cs[3] = a4.w;
+            sg.cb[0] = b4.x; sg.cb[1] = b4.y; sg.cb[2] = b4.z; sg.cb[3] = b4.w;
+          } else {
+            const u32x2 a2 = __builtin_amdgcn_raw_buffer_load_b64(sr, cv, ssoff, 0);
+            const u32x2 b2 = __builtin_amdgcn_raw_buffer_load_b64(br, cv, ssoff, 0);
+            sg.cs[0] = a2.x; sg.cs[1] = a2.y;
+            sg.cb[0] = b2.x; sg.cb[1] = b2.y;
+          }
+        }
+      } else if constexpr (SSZ == 16) {
         u32x4 a4 = __builtin_amdgcn_raw_buffer_load_b128(sr, sv, ssoff, 0);
         u32x4 b4 = __builtin_amdgcn_raw_buffer_load_b128(br, sv, ssoff, 0);
         if (gu) {
@@ -1369,12 +1391,26 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
   };
 
   auto compute_group = [&](const u32x4 (&gw)[MG::WLD], const uint32_t (&gs)[SSZ / 4], const uint32_t (&gb)[SSZ / 4],
-                           const Cursor& c, const int gr) {
+                           const uint32_t* cs, const uint32_t* cb, const Cursor& c, const int gr) {
     // hand the group over: lane order in, the slot layout out (the wave's
     // previous reads of the slot precede these writes in its LDS queue)
 #pragma unroll
     for (int t = 0; t < MG::WLD; ++t) reinterpret_cast<u32x4*>(slot)[t * kWave + lane] = gw[t];
-    if (s_live) {
+    if constexpr (CS) {
+      // this group's half of column lane's scales and biases (SSTR = SB here)
+      if (lane < 16) {
+        if constexpr (CW == 4) {
+          u32x2 a2, b2;
+          a2.x = cs[0]; a2.y = cs[1];
+          b2.x = cb[0]; b2.y = cb[1];
+          *reinterpret_cast<u32x2*>(slot + MG::WBYTES + lane * MG::SSTR) = a2;
+          *reinterpret_cast<u32x2*>(slot + MG::WBYTES + 16 * MG::SSTR + lane * MG::SSTR) = b2;
+        } else {
+          *reinterpret_cast<uint32_t*>(slot + MG::WBYTES + lane * MG::SSTR) = cs[0];
+          *reinterpret_cast<uint32_t*>(slot + MG::WBYTES + 16 * MG::SSTR + lane * MG::SSTR) = cb[0];
+        }
+      }
+    } else if (s_live) {
       if constexpr (SSZ == 16) {
         u32x4 a4, b4;
         a4.x = gs[0]; a4.y = gs[1]; a4.z = gs[2]; a4.w = gs[3];
@@ -1580,7 +1616,8 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
   // a stage's groups one after the other, in order
   auto compute = [&](const Stage& sg, const Cursor& c) {
 #pragma unroll
-    for (int g2 = 0; g2 < NG; ++g2) compute_group(sg.w[g2], sg.s[g2], sg.b[g2], c, c.gr + g2);
+    for (int g2 = 0; g2 < NG; ++g2)
+      compute_group(sg.w[g2], sg.s[g2], sg.b[g2], sg.cs + g2 * (CW / 2), sg.cb + g2 * (CW / 2), c, c.gr + g2);
   };
 
   // A pass's first loads: each thread's first staging item, then the first
@@ -1940,6 +1977,7 @@ struct Entry {
   int mfma_group;       // 128-code rounds per load group (k is a multiple of 128 * this)
   int mfma_salign;      // alignment the scale and bias arrays need (bytes)
   int dyn_stage;        // load groups per stage of the kernels that hand out units (k: 128 * group * this)
+  int dyn_salign;       // the scale and bias alignment those kernels need (their combined scale loads)
 };
 
 template <int B, int G>
@@ -2002,6 +2040,8 @@ Entry make_entry() {
   e.mfma_waves[4] = MWaves<16>::v;
   e.mfma_salign = MGroup<B, G>::S16 ? 16 : 4;
   e.dyn_stage = dyn_stage_groups(B);
+  using MG = MGroup<B, G>;
+  e.dyn_salign = (dyn_stage_groups(B) == 2 && !MG::S16 && MG::SB >= 4) ? 2 * MG::SB : e.mfma_salign;
   return e;
 }
 
