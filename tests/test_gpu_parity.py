@@ -717,6 +717,36 @@ def test_unit_handout_equals_tile_walk(bits, group, k, arith):
     assert torch.equal(yw.view(torch.int32)[gap], sentinel[gap])
 
 
+@pytest.mark.parametrize("bits,group", [(8, 32), (4, 128)])
+def test_unit_handout_scales_only_4_byte_aligned(bits, group):
+    """The unit-handout kernels load a stage's two groups' dword scales of a
+    column at once (16 bytes at 8/32, 8 at 4/128), so they need 16- or
+    8-byte aligned scale and bias arrays; with arrays 4 bytes off that, a
+    large matrix takes the tile walk, and its outputs hold the same bits as
+    with aligned arrays."""
+    print_case("unit handout, scales 4 bytes off", bits, group)
+    n, k = 100000, 2048
+    rng = np.random.default_rng(9300 + bits + group)
+    words = synth.draw_words(rng, (n,), k, bits)
+    scales = synth.draw_scales(rng, (n, k // group))
+    biases = synth.draw_biases(rng, (n, k // group))
+    x = synth.draw_x_wide(rng, 4, k)
+    tw, xt = dev(words), dev(x)
+
+    def shifted(a):
+        # the same values from 4 bytes past a 256-byte aligned allocation
+        t = torch.zeros(a.size + 2, dtype=torch.int16, device=DEV)
+        t[2:] = dev(a).view(-1)
+        return t[2:].view(a.shape)
+
+    aligned = qgemv.Matrix(bits, group, n, k, tw, dev(scales), dev(biases))
+    ss, bb = shifted(scales), shifted(biases)
+    assert ss.data_ptr() % 16 == 4 and bb.data_ptr() % 16 == 4
+    off = qgemv.Matrix(bits, group, n, k, tw, ss, bb)
+    for m in (1, 4):
+        assert bits_equal(run(aligned, xt, m), run(off, xt, m)), f"m={m}"
+
+
 @pytest.mark.parametrize("arith", ARITHS + [qgemv.QGEMV_ARITH_AUTO], ids=ARITH_IDS + ["auto"])
 @pytest.mark.parametrize("m", [1, 8, 16])
 def test_lmhead_sampled(lmhead, m, arith):
