@@ -119,7 +119,7 @@ struct qgemv_handle {
   // resident blocks per CU of each (window variant, staging) kernel, 0 =
   // not yet known (matrix-core forms: [variant][0] plain, [variant][1] gate/up
   // pairs); a benign cache: every thread that fills it writes the same value
-  mutable std::atomic<int> occupancy[5][2];
+  mutable std::atomic<int> occupancy[5][3];   // by window variant and kernel (0 plain, 1 gate/up, 2 4-wave)
 };
 
 namespace {
@@ -297,6 +297,24 @@ int launch(const qgemv_handle* h, const uint16_t* x, int32_t m, float* y, int64_
   } else {
     lds = lds_bytes(h, var, stage);
   }
+  // Small matrices: a plain or strided call's 8- and 16-row windows of the
+  // tile walk in blocks of 4 waves when blocks of 8 would cover at most half
+  // the CUs, at the window's own variant when its 4-wave plan fits (a column's
+  // arithmetic does not depend on its block: the same bits)
+  static_assert(qg::kWindows[3] == 8 && qg::kWindows[4] == 16, "4-wave kernels for windows of 8 and 16 rows");
+  bool four = false;
+  if (mfma && !indexed && !up) {
+    for (int v = own_var; v >= var && qg::kWindows[v] >= 8; --v) {
+      const int64_t rows8 = static_cast<int64_t>(h->entry->mfma_waves[v] / h->ksplit) * 16;
+      size_t l4 = 0;
+      if (2 * ((h->d.n + rows8 - 1) / rows8) <= dev->cus && mfma_plan(h, v, false, &l4, 4)) {
+        four = true;
+        var = v;
+        lds = l4;
+        break;
+      }
+    }
+  }
   if (lds > (mfma ? qg::kMaxMfmaLds : qg::kMaxDynamicLds)) return QGEMV_E_WINDOW;
   qg::KernelFn fn = h->fast ? h->entry->fast[var][stage] : h->entry->generic[var];
   int threads = qg::kThreads;
@@ -311,11 +329,12 @@ int launch(const qgemv_handle* h, const uint16_t* x, int32_t m, float* y, int64_
       fn = wide ? (up ? h->wide->gateup_indexed[var] : h->wide->indexed[var])
                 : (up ? h->entry->mfma_gateup_indexed[var] : h->entry->mfma_indexed[var]);
     } else {
-      fn = wide ? (up ? h->wide->gateup[var] : h->wide->k[var])
-                : (up ? h->entry->mfma_gateup[var] : h->entry->mfma[var]);
+      fn = wide ? (up ? h->wide->gateup[var] : (four ? h->wide->k4[var - 3] : h->wide->k[var]))
+                : (up ? h->entry->mfma_gateup[var] : (four ? h->entry->mfma4[var - 3] : h->entry->mfma[var]));
     }
-    threads = h->entry->mfma_waves[var] * qg::kWave;
-    tile_rows = static_cast<int64_t>(h->entry->mfma_waves[var] / h->ksplit) * (up ? 8 : 16);
+    const int nw = four ? 4 : h->entry->mfma_waves[var];
+    threads = nw * qg::kWave;
+    tile_rows = static_cast<int64_t>(nw / h->ksplit) * (up ? 8 : 16);
   } else {
     const int R = h->fast ? h->entry->fast_rows[var] : h->entry->generic_rows[var];
     const int slots_per_wave = qg::kWave / h->lpr;
@@ -388,7 +407,7 @@ int launch(const qgemv_handle* h, const uint16_t* x, int32_t m, float* y, int64_
     }
   }
   if (!indexed) {
-    const int oslot = mfma ? (up ? 1 : 0) : stage;
+    const int oslot = mfma ? (up ? 1 : (four ? 2 : 0)) : stage;
     int occ = h->occupancy[var][oslot].load(std::memory_order_relaxed);
     if (occ == 0) {
       int nb = 0;

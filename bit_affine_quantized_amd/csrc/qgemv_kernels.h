@@ -1123,7 +1123,7 @@ __device__ __forceinline__ void split_units(int t, int units, float inv_units, i
 // 16x16x32 product over every window row at once (A row i = window row i),
 // and lane (j, q) folds window rows 4q .. 4q+3 of column j.
 template <int B, int G, int MB, bool WIDE = false, bool GU = false, bool IDX = false, bool DYN = false,
-          class PT = const Params>
+          class PT = const Params, int NWO = 0>
 __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, unsigned char* smem,
                                           int* s_wave_cnt, int* s_xrow, int64_t* s_yoff, int* s_next = nullptr) {
   static_assert(!DYN || (!GU && !IDX), "units handed out in a block: plain and strided calls");
@@ -1136,7 +1136,7 @@ __device__ __forceinline__ void mfma_body(PT& p, const int bx, const int gx, uns
   constexpr bool CS = NG == 2 && MG::SSZ == 4 && MG::SB >= 4;
   constexpr int CW = CS ? MG::SB / 2 : 1;             // dwords of a column's two groups
   static_assert(!CS || !GU, "combined scale loads: plain and strided calls");
-  constexpr int NW = DYN ? DynWaves<B, G, MB, WIDE>::v : MWaves<MB>::v, NT = NW * kWave;
+  constexpr int NW = DYN ? DynWaves<B, G, MB, WIDE>::v : (NWO ? NWO : MWaves<MB>::v), NT = NW * kWave;
   constexpr int NMB = (MB + 3) / 4;         // 4-row blocks of the window
   // outputs each lane folds: one per 4-row block, or (wide form) window rows
   // 4q .. 4q+3 of its column, as many as the window can hold
@@ -1787,6 +1787,25 @@ QG_MFMA_KERNEL(qrow_mfma_gateup_indexed, false, true, true)
 QG_MFMA_KERNEL(qrow_mfma_wide_gateup_indexed, true, true, true)
 #undef QG_MFMA_KERNEL
 
+// The tile walk's 8- and 16-row windows in blocks of 4 waves, for plain and
+// strided calls on small matrices, whose 8-wave blocks would leave CUs idle
+// (two waves a SIMD on half the CUs or fewer): one wave a SIMD on twice the
+// CUs, each block staging the window for fewer waves.  A column's arithmetic
+// does not depend on its block, so the bits are those of the 8-wave blocks.
+#define QG_MFMA4_KERNEL(NAME, WIDE)                                                           \
+  template <int B, int G, int MB>                                                            \
+  __global__ __launch_bounds__(4 * kWave) void NAME(const Params p) {                       \
+    extern __shared__ __align__(16) unsigned char smem[];                                    \
+    __shared__ int s_wave_cnt[4];                                                            \
+    __shared__ int s_xrow[QGEMV_MAX_WINDOW];                                                 \
+    __shared__ int64_t s_yoff[QGEMV_MAX_WINDOW];                                             \
+    mfma_body<B, G, MB, WIDE, false, false, false, const Params, 4>(p, blockIdx.x, gridDim.x, smem, \
+                                                                   s_wave_cnt, s_xrow, s_yoff); \
+  }
+QG_MFMA4_KERNEL(qrow_mfma_w4, false)
+QG_MFMA4_KERNEL(qrow_mfma_wide_w4, true)
+#undef QG_MFMA4_KERNEL
+
 // The block-diagonal kernels for matrices of many columns: one block of
 // DynWaves waves per CU, its 16-column units handed out in the block.
 #define QG_DYN_KERNEL(NAME, WIDE)                                                             \
@@ -1972,6 +1991,7 @@ struct Entry {
   KernelFn mfma_indexed[3];         // indexed calls (windows of 1, 2 and 4 routed rows)
   KernelFn mfma_gateup_indexed[3];  // indexed gate/up pairs
   KernelFn mfma_dyn[5];  // units handed out in the block, by window variant (null: not built)
+  KernelFn mfma4[2];     // the 8- and 16-row variants in 4-wave blocks (small matrices)
   int mfma_slot;        // bytes of one wave's LDS slot (one load group)
   int mfma_waves[5];    // waves per block of the matrix-core kernels by window variant
   int mfma_group;       // 128-code rounds per load group (k is a multiple of 128 * this)
@@ -2020,6 +2040,8 @@ Entry make_entry() {
   e.mfma[2] = qrow_mfma<B, G, 4>;
   e.mfma[3] = qrow_mfma<B, G, 8>;
   e.mfma[4] = qrow_mfma<B, G, 16>;
+  e.mfma4[0] = qrow_mfma_w4<B, G, 8>;
+  e.mfma4[1] = qrow_mfma_w4<B, G, 16>;
   e.mfma_gateup[0] = qrow_mfma_gateup<B, G, 1>;
   e.mfma_gateup[1] = qrow_mfma_gateup<B, G, 2>;
   e.mfma_gateup[2] = qrow_mfma_gateup<B, G, 4>;
@@ -2048,6 +2070,7 @@ Entry make_entry() {
 // The wide-window matrix-core kernels of one (bits, group) by window variant.
 struct WideEntry {
   KernelFn k[5];
+  KernelFn k4[2];       // the 8- and 16-row variants in 4-wave blocks (small matrices)
   KernelFn dyn[5];      // units handed out in the block (null: not built)
   KernelFn gateup[5];   // gate/up pairs
   KernelFn indexed[3];  // indexed calls (windows of 1, 2 and 4 routed rows)
@@ -2067,6 +2090,8 @@ WideEntry make_wide_entry() {
   e.k[2] = qrow_mfma_wide<B, G, 4>;
   e.k[3] = qrow_mfma_wide<B, G, 8>;
   e.k[4] = qrow_mfma_wide<B, G, 16>;
+  e.k4[0] = qrow_mfma_wide_w4<B, G, 8>;
+  e.k4[1] = qrow_mfma_wide_w4<B, G, 16>;
   e.gateup[0] = qrow_mfma_wide_gateup<B, G, 1>;
   e.gateup[1] = qrow_mfma_wide_gateup<B, G, 2>;
   e.gateup[2] = qrow_mfma_wide_gateup<B, G, 4>;

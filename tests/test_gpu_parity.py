@@ -717,6 +717,37 @@ def test_unit_handout_equals_tile_walk(bits, group, k, arith):
     assert torch.equal(yw.view(torch.int32)[gap], sentinel[gap])
 
 
+@mc_param
+@pytest.mark.parametrize("bits,group", [(2, 32), (3, 64), (4, 64), (5, 32), (5, 128), (6, 32), (8, 128)])
+def test_four_wave_blocks_equal_eight(bits, group, arith):
+    """Small matrices run 8- and 16-row windows of the tile walk in blocks of
+    4 waves (blocks of 8 would cover at most half the CUs).  At K = 2048 a
+    4096-column matrix and a larger one split K alike (in 4 parts, or in 2
+    for 3- and 5-bit codes, whose rows hold two load groups), and the first
+    takes 4-wave blocks, the second (8192 columns, or 16384 at a split of 2)
+    8-wave ones.  The larger matrix's first 4096 columns are the smaller
+    matrix: they agree bit for bit at 8 and 16 rows (and at a 12-row window),
+    with activations whose unit dots round, and the 4096-column outputs stay
+    within the oracle's bound."""
+    print_case("4-wave blocks", bits, group, arith)
+    n, k, n_small = (16384 if bits in (3, 5) else 8192), 2048, 4096
+    rng = np.random.default_rng(9400 + 10 * bits + group)
+    words = synth.draw_words(rng, (n,), k, bits)
+    scales = synth.draw_scales(rng, (n, k // group))
+    biases = synth.draw_biases(rng, (n, k // group))
+    x = synth.draw_x_wide(rng, 16, k)
+    tw, ts, tb = dev(words), dev(scales), dev(biases)
+    big = qgemv.Matrix(bits, group, n, k, tw, ts, tb, arith=arith)
+    small = qgemv.Matrix(bits, group, n_small, k, tw[:n_small], ts[:n_small], tb[:n_small], arith=arith)
+    xt = dev(x)
+    y64, a64, _ = oracle.gemv(words[:n_small], scales[:n_small], biases[:n_small], x, bits, group, n_small, k,
+                              threads=THREADS)
+    for m in (8, 12, 16):
+        ys = run(small, xt, m)
+        assert bits_equal(run(big, xt, m)[:, :n_small], ys), f"m={m}"
+        check_bound(ys.cpu().numpy(), y64[:m], a64[:m], k, f"4-wave blocks {bits}/{group} m={m}")
+
+
 @pytest.mark.parametrize("bits,group", [(8, 32), (4, 128)])
 def test_unit_handout_scales_only_4_byte_aligned(bits, group):
     """The unit-handout kernels load a stage's two groups' dword scales of a
