@@ -164,7 +164,11 @@ int qgemv_arith(qgemv_t h);
  * bits, 1024 for 3 and 5, 256 for 4, 128 for 8 (256 at group 128); 0 for a
  * bad bits or group.  The MFMA form also needs scales and biases 16-byte
  * aligned where a row's scales of one load group fill whole 16-byte pieces,
- * else 4-byte aligned. */
+ * else 4-byte aligned.
+ * Speed only (the bits do not change): on matrices of about 100,000 columns
+ * or more, 2-, 4- and 8-bit codes run their fastest kernels when k is a
+ * multiple of twice this and, at 8/32, 8/64, 4/64, 4/128 and 2/128, the
+ * scale and bias arrays are 16-byte (8/32, 4/64, 2/128) or 8-byte aligned. */
 int64_t qgemv_mfma_codes(int32_t bits, int32_t group);
 
 /* Free the host-side handle (never touches device memory). NULL is a no-op. */
